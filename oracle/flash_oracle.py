@@ -1,0 +1,330 @@
+"""fp64 CPU oracle for the forward pass of one FLASH layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute this module:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+It shares no code, header, table or helper with the HIP library; it takes plain NumPy arrays and
+computes everything in float64.
+
+What is computed, and where the pages define it
+------------------------------------------------
+Page "FLASH: Possibly the Most Interesting Efficient Transformer Design Recently"
+(kexue.fm/archives/8934, English translation):
+
+* section "Initial Power": the GLU form O = (U ⊙ V) W_o with U = SiLU(X W_u), V = SiLU(X W_v),
+  W_u, W_v of shape [d, e]; Swish/SiLU on both branches.
+* section "Strong Combination", equation (mix): O = (U ⊙ A V) W_o; A = I gives the GLU FFN.
+* section "Weak Attention", equation (relu-att): Z = phi_z(X W_z), W_z of shape [d, s]; Q and K are
+  per-dimension scale-and-offset maps of Z; relu² means relu followed by squaring; the appendix
+  code normalises by 1/n² instead of the blog's 1/(ns).
+* section "Mixed Chunk": split the n tokens into n/c chunks of c tokens; four scale/offset heads
+  of Z_g give Q_quad, K_quad, Q_lin, K_lin; the local term is relu²(Q_quad K_quadᵀ) V inside each
+  chunk (upper triangle masked for a decoder); the global term is Q_lin Σ_h K_linᵀ V_h / n, and for
+  a decoder the sum runs over the earlier chunks h < g only; O_g = [U_g ⊙ (V̂_quad + V̂_lin)] W_o.
+
+Page "大模型训练之加速篇 -attention优化" (blog.csdn.net), section 1.4 (autoregressive generation):
+the RNN form of causal linear attention (a running state S_t = S_{t-1} + k_tᵀ v_t) and the cumsum
+form (all outer products, then a prefix sum over tokens). Both are alternative routes to the same
+global term and serve here as cross-checks.
+
+Readings taken where the pages are silent, garbled or in conflict
+------------------------------------------------------------------
+* Local normalisation: relu²(Q Kᵀ / c), i.e. relu²(Q Kᵀ) / c². This is the appendix convention of
+  "Weak Attention" applied per chunk (chunk = n gives the appendix's 1/n²). The blog's 1/(cs) is
+  kept as the variant ``local_norm="cs"``.
+* Global normalisation: 1/n (the sequence length) for both the causal and the non-causal form. The
+  causal prefactor printed in "Mixed Chunk" is garbled (it is 0/0 for the first chunk); the
+  "Extended Thoughts" section says the appendix divides by n. The variant ``global_norm="count"``
+  divides chunk g's read-out by the number of earlier tokens (g-1)c instead (zero for g = 1).
+* phi_z is SiLU, like phi_u and phi_v.
+* Causal local mask: entries with key index j > query index i (inside the chunk) are zero; the
+  diagonal is kept.
+* Head order in gamma/beta rows: Q_quad, K_quad, Q_lin, K_lin.
+* The layer has no bias, norm, residual, dropout or position encoding.
+
+Parity status: every function below is pinned by tests that do not re-type its formula
+(brute-force n×n matrices, the RNN recurrence, the chunk = n and A = I reductions, causality,
+permutation equivariance, closed-form values and hand-worked fixtures).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "silu",
+    "project",
+    "scale_offset_heads",
+    "local_quad",
+    "chunk_states",
+    "prefix_states",
+    "global_linear",
+    "combine",
+    "flash_forward",
+    "brute_force_forward",
+    "rnn_global_linear",
+    "cumsum_global_linear",
+    "gau_forward",
+    "glu_forward",
+    "quad_gau_attention",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(x):
+    """Swish / SiLU, x · sigmoid(x) ("Initial Power": both U and V use Swish).
+
+    Written as x / (1 + e^{-x}); for large negative x, e^{-x} overflows to inf and the quotient
+    is the correct limit -0.0, so the warning is silenced.
+    """
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def project(X, W_u, W_v, W_z):
+    """U = SiLU(X W_u), V = SiLU(X W_v), Z = SiLU(X W_z).
+
+    "Initial Power" (GLU with Swish on U and V) and "Weak Attention" (Z = phi_z(X W_z), W_z of
+    shape [d, s]; phi_z read as SiLU). X is [..., n, d].
+    """
+    X = _f64(X)
+    return silu(X @ _f64(W_u)), silu(X @ _f64(W_v)), silu(X @ _f64(W_z))
+
+
+def scale_offset_heads(Z, gamma, beta):
+    """The four per-dimension affine heads of Z ("Mixed Chunk"; "Weak Attention" likens them to
+    LayerNorm's gamma and beta). gamma, beta are [4, s] in the order Q_quad, K_quad, Q_lin, K_lin.
+    Returns the tuple (Q_quad, K_quad, Q_lin, K_lin), each shaped like Z."""
+    Z, gamma, beta = _f64(Z), _f64(gamma), _f64(beta)
+    return tuple(Z * gamma[h] + beta[h] for h in range(4))
+
+
+def _chunks(n, chunk):
+    if chunk <= 0 or n % chunk != 0:
+        raise ValueError(f"chunk {chunk} must divide n {n}")
+    return n // chunk
+
+
+def local_quad(Qq, Kq, V, chunk, causal, local_norm="c2", return_weights=False):
+    """Quadratic attention inside each non-overlapping chunk ("Mixed Chunk", first display).
+
+    For chunk g: W_g = relu(Q_g K_gᵀ / c)² (the adopted normalisation) or relu(Q_g K_gᵀ)² / (c s)
+    (``local_norm="cs"``, the blog's own constant); when causal, entries above the diagonal are
+    zeroed. V̂_quad_g = W_g V_g. Inputs are [B, n, ·]; returns V̂_quad [B, n, e] and optionally the
+    weights [B, G, c, c].
+    """
+    Qq, Kq, V = _f64(Qq), _f64(Kq), _f64(V)
+    B, n, s = Qq.shape
+    G = _chunks(n, chunk)
+    out = np.zeros(V.shape, dtype=np.float64)
+    weights = np.zeros((B, G, chunk, chunk), dtype=np.float64)
+    keep = np.tril(np.ones((chunk, chunk), dtype=bool)) if causal else np.ones((chunk, chunk), dtype=bool)
+    for b in range(B):
+        for g in range(G):
+            rows = slice(g * chunk, (g + 1) * chunk)
+            scores = Qq[b, rows] @ Kq[b, rows].T
+            if local_norm == "c2":
+                w = np.maximum(scores / chunk, 0.0) ** 2
+            elif local_norm == "cs":
+                w = np.maximum(scores, 0.0) ** 2 / (chunk * s)
+            else:
+                raise ValueError(local_norm)
+            w = np.where(keep, w, 0.0)
+            weights[b, g] = w
+            out[b, rows] = w @ V[b, rows]
+    return (out, weights) if return_weights else out
+
+
+def chunk_states(Kl, V, chunk):
+    """Per-chunk linear-attention summary T_g = K_lin_gᵀ V_g, an s×e matrix ("Mixed Chunk": the
+    b(n/c)se state memory). Kl is [B, n, s], V is [B, n, e]; returns [B, G, s, e]."""
+    Kl, V = _f64(Kl), _f64(V)
+    B, n, s = Kl.shape
+    G = _chunks(n, chunk)
+    T = np.zeros((B, G, s, V.shape[-1]), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * chunk, (g + 1) * chunk)
+        T[:, g] = np.einsum("bts,bte->bse", Kl[:, rows], V[:, rows])
+    return T
+
+
+def prefix_states(T, causal):
+    """Cross-chunk sum of the summaries ("Mixed Chunk").
+
+    Non-causal: every chunk sees the full sum Σ_{h=1}^{n/c} T_h. Causal: chunk g sees the exclusive
+    prefix Σ_{h=1}^{g-1} T_h, so the first chunk sees zero. T is [B, G, s, e]; returns the same shape.
+    """
+    T = _f64(T)
+    S = np.zeros_like(T)
+    G = T.shape[1]
+    if causal:
+        run = np.zeros_like(T[:, 0])
+        for g in range(G):
+            S[:, g] = run
+            run = run + T[:, g]
+    else:
+        total = T.sum(axis=1)
+        for g in range(G):
+            S[:, g] = total
+    return S
+
+
+def global_linear(Ql, S, chunk, n, global_norm="n"):
+    """Global read-out V̂_lin_g = Q_lin_g S_g / n ("Mixed Chunk", second and third displays, with the
+    1/n reading for both forms). ``global_norm="count"`` divides chunk g by (g-1)c instead (the
+    "divide by t" remark of "Extended Thoughts", at chunk granularity); the first chunk then reads 0.
+    Ql is [B, n, s], S is [B, G, s, e]; returns [B, n, e]."""
+    Ql, S = _f64(Ql), _f64(S)
+    B = Ql.shape[0]
+    G = _chunks(n, chunk)
+    out = np.zeros((B, n, S.shape[-1]), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * chunk, (g + 1) * chunk)
+        if global_norm == "n":
+            scale = 1.0 / n
+        elif global_norm == "count":
+            scale = 0.0 if g == 0 else 1.0 / (g * chunk)
+        else:
+            raise ValueError(global_norm)
+        out[:, rows] = (Ql[:, rows] @ S[:, g]) * scale
+    return out
+
+
+def combine(U, Vq, Vl, W_o):
+    """O = [U ⊙ (V̂_quad + V̂_lin)] W_o ("Mixed Chunk", last display; the gate of equation (mix))."""
+    return (_f64(U) * (_f64(Vq) + _f64(Vl))) @ _f64(W_o)
+
+
+def flash_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal,
+                  local_norm="c2", global_norm="n", return_intermediates=False):
+    """One FLASH layer forward in the chunked form, steps in the order of "Mixed Chunk".
+
+    X is [B, n, d] (a 2-D [n, d] input is treated as B = 1). Returns O [B, n, d] in float64, and
+    with ``return_intermediates`` also a dict of U, V, Z, the four heads, the local weights P
+    [B, G, c, c], the chunk summaries T and the prefix states S [B, G, s, e], V̂_quad, V̂_lin and
+    the gated product Y = U ⊙ (V̂_quad + V̂_lin).
+    """
+    X = _f64(X)
+    squeeze = X.ndim == 2
+    if squeeze:
+        X = X[None]
+    n = X.shape[1]
+    U, V, Z = project(X, W_u, W_v, W_z)
+    Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    Vq, P = local_quad(Qq, Kq, V, chunk, causal, local_norm=local_norm, return_weights=True)
+    T = chunk_states(Kl, V, chunk)
+    S = prefix_states(T, causal)
+    Vl = global_linear(Ql, S, chunk, n, global_norm=global_norm)
+    Y = U * (Vq + Vl)
+    O = combine(U, Vq, Vl, W_o)
+    if squeeze:
+        O = O[0]
+    if not return_intermediates:
+        return O
+    inter = dict(U=U, V=V, Z=Z, Qq=Qq, Kq=Kq, Ql=Ql, Kl=Kl, P=P, T=T, S=S, Vq=Vq, Vl=Vl, Y=Y)
+    return O, inter
+
+
+# ---------------------------------------------------------------------------------------------
+# Independent formulations used to pin the chunked oracle.
+# ---------------------------------------------------------------------------------------------
+
+def brute_force_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal):
+    """The same layer with both attention matrices materialised as full n×n arrays.
+
+    "Mixed Chunk" says the local term is attention restricted to the block diagonal (masked to the
+    lower triangle for a decoder) and that the global term equals linear attention with the full
+    Q_lin, K_lin in R^{n×s}; for a decoder only keys in earlier chunks are visible. Here
+    A_quad[i, j] = relu(q_i·k_j / c)² when i, j share a chunk (and j <= i if causal),
+    A_lin[i, j] = ql_i·kl_j / n when chunk(j) < chunk(i) (causal) or always (non-causal), and
+    O = (U ⊙ (A_quad + A_lin) V) W_o, the form of equation (mix).
+    """
+    X = _f64(X)
+    B, n, _ = X.shape
+    _chunks(n, chunk)
+    U, V, Z = project(X, W_u, W_v, W_z)
+    Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    idx = np.arange(n)
+    cid = idx // chunk
+    same = cid[:, None] == cid[None, :]
+    if causal:
+        quad_mask = same & (idx[None, :] <= idx[:, None])
+        lin_mask = cid[None, :] < cid[:, None]
+    else:
+        quad_mask = same
+        lin_mask = np.ones((n, n), dtype=bool)
+    O = np.zeros((B, n, _f64(W_o).shape[1]))
+    for b in range(B):
+        a_quad = np.where(quad_mask, np.maximum(Qq[b] @ Kq[b].T / chunk, 0.0) ** 2, 0.0)
+        a_lin = np.where(lin_mask, Ql[b] @ Kl[b].T / n, 0.0)
+        O[b] = (U[b] * ((a_quad + a_lin) @ V[b])) @ _f64(W_o)
+    return O
+
+
+def rnn_global_linear(Ql, Kl, V, chunk, n):
+    """Causal global term through the token recurrence of the RNN form (csdn survey §1.4, first
+    form): S_t = S_{t-1} + kl_tᵀ v_t, one token at a time. A query in chunk g reads the state as it
+    stood after the last token of chunk g-1, divided by n. Returns [B, n, e]."""
+    Ql, Kl, V = _f64(Ql), _f64(Kl), _f64(V)
+    B, _, s = Kl.shape
+    e = V.shape[-1]
+    out = np.zeros((B, n, e))
+    for b in range(B):
+        state = np.zeros((s, e))
+        state_at_chunk_start = np.zeros((s, e))
+        for t in range(n):
+            if t % chunk == 0:
+                state_at_chunk_start = state.copy()
+            out[b, t] = Ql[b, t] @ state_at_chunk_start / n
+            state = state + np.outer(Kl[b, t], V[b, t])
+    return out
+
+
+def cumsum_global_linear(Ql, Kl, V, chunk, n):
+    """Causal global term through the cumsum form (csdn survey §1.4, second form): all n outer
+    products kl_tᵀ v_t as an [n, s, e] array, then a prefix sum over tokens. Chunk g reads the
+    inclusive sum up to its own first token minus one. Tiny shapes only (n·s·e memory)."""
+    Ql, Kl, V = _f64(Ql), _f64(Kl), _f64(V)
+    B = Ql.shape[0]
+    out = np.zeros((B, n, V.shape[-1]))
+    for b in range(B):
+        outer = Kl[b][:, :, None] * V[b][:, None, :]
+        csum = np.cumsum(outer, axis=0)
+        for t in range(n):
+            start = (t // chunk) * chunk
+            state = csum[start - 1] if start > 0 else np.zeros_like(csum[0])
+            out[b, t] = Ql[b, t] @ state / n
+    return out
+
+
+def gau_forward(X, A, W_u, W_v, W_o):
+    """Equation (mix) of "Strong Combination" with a given n×n matrix A: O = (U ⊙ A V) W_o,
+    U = SiLU(X W_u), V = SiLU(X W_v). X is [n, d]."""
+    X = _f64(X)
+    U = silu(X @ _f64(W_u))
+    V = silu(X @ _f64(W_v))
+    return (U * (_f64(A) @ V)) @ _f64(W_o)
+
+
+def glu_forward(X, W_u, W_v, W_o):
+    """The GLU FFN of "Initial Power": O = (U ⊙ V) W_o with Swish on both branches. X is [n, d]."""
+    X = _f64(X)
+    return (silu(X @ _f64(W_u)) * silu(X @ _f64(W_v))) @ _f64(W_o)
+
+
+def quad_gau_attention(X, W_z, gamma_q, beta_q, gamma_k, beta_k, causal):
+    """The quadratic GAU's attention matrix with the appendix normalisation of "Weak Attention":
+    A = relu²(Q Kᵀ) / n², Q = gamma_q ⊙ Z + beta_q, K = gamma_k ⊙ Z + beta_k, Z = SiLU(X W_z);
+    the upper triangle is zeroed when causal. X is [n, d]; returns [n, n]."""
+    X = _f64(X)
+    n = X.shape[0]
+    Z = silu(X @ _f64(W_z))
+    Q = Z * _f64(gamma_q) + _f64(beta_q)
+    K = Z * _f64(gamma_k) + _f64(beta_k)
+    A = np.maximum(Q @ K.T, 0.0) ** 2 / float(n) ** 2
+    if causal:
+        A = np.tril(A)
+    return A
