@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of one FLASH layer forward on one MI355X (the HIP library through its C ABI).
+
+Default workload: causal, bf16 storage with fp32 accumulation, B = 8, n = 4096, d = 768,
+e = 1536, s = 128, chunk 256, seeded synthetic inputs (X ~ N(0,1), weights ~ N(0, 1/fan_in),
+gamma ~ N(1, 0.02), beta = 0). A step is one full forward call: all six kernels (pack, proj,
+scores, states, mix, out) over the whole batch, with inputs already resident in HBM.
+
+Prints one JSON line. `value` is tokens/s = B*n / (wall time of one step), timed over exactly
+--steps calls between two device synchronisations. Each call also records a HIP event before
+every kernel on the library's stream, which gives every kernel's average duration; the roofline
+object reports the kernel that takes the longest. The CPU baseline is the fp64 oracle timed on
+the host on one sequence of the same batch; its output also checks the GPU's on that sequence.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec per FLASH layer fwd (n=4096 causal bf16); % bf16 MFMA peak"
+PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core TFLOP/s of MI355X
+HBM_PEAK = 8000.0  # GB/s
+
+
+def alg_flops(B, n, d, e, s, c, causal):
+    """Algorithmic FLOPs of one layer forward, split by kernel (multiply-add = 2)."""
+    N = B * n
+    proj = 2 * N * d * (2 * e + s)
+    if causal:
+        # query i of a chunk sees i+1 keys: scores and P·V over (c+1)/2 keys on average
+        scores = N * (c + 1) * s
+        pv = N * (c + 1) * e
+        n_state = N - B * c  # the last chunk's summary and the first chunk's read-out are unused
+    else:
+        scores = 2 * N * c * s
+        pv = 2 * N * c * e
+        n_state = N
+    states = 2 * n_state * s * e
+    readout = 2 * n_state * s * e
+    out = 2 * N * e * d
+    return {"pack": 0, "proj": proj, "scores": scores, "states": states, "mix": pv + readout,
+            "out": out}
+
+
+def alg_bytes(B, n, d, e, s, c, causal, esz):
+    """Bytes each kernel must move at least once between HBM and the chip."""
+    N = B * n
+    G = n // c
+    nst = (B * G if causal else B) * e * s
+    pc = (c * (c + 1) // 2) if causal else c * c  # P entries the mix reads per chunk
+    return {
+        "pack": 2 * ((2 * e + s) * d + e * d) * esz,
+        "proj": (N * d + (2 * e + s) * d + N * (2 * e + 4 * s)) * esz,
+        "scores": (2 * N * s + B * G * c * c) * esz,
+        "states": (N * (e + s) + nst) * esz,
+        "mix": (N * e * 2 + B * G * pc + N * s + nst + N * e) * esz,
+        "out": (N * e + e * d + N * d) * esz,
+    }
+
+
+BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "mix": "hbm",
+         "out": "mfma"}
+
+
+class HipEvents:
+    def __init__(self, count):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.handles = []
+        for _ in range(count):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.handles.append(h.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
+
+    def close(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def cpu_baseline(inp, seconds):
+    """Times the fp64 oracle on sequence 0 of the batch until `seconds` have passed (at least
+    one run); returns the baseline record and the oracle output for that sequence."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    times = []
+    ref = None
+    t_start = time.perf_counter()
+    while not times or time.perf_counter() - t_start < seconds:
+        t0 = time.perf_counter()
+        ref = oracle.flash_forward(inp.X[:1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta,
+                                   inp.W_o, inp.chunk, inp.causal)
+        times.append(time.perf_counter() - t0)
+    n = inp.X.shape[1]
+    med = statistics.median(times)
+    rec = {"value": n / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"sequence 0 of {inp.X.shape[0]} ({n} tokens) of the same workload, "
+                     f"fp64 NumPy oracle, median of {len(times)} runs ({med:.2f} s each); "
+                     f"host has {os.cpu_count()} logical CPUs"}
+    return rec, ref
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="name in inputs.WORKLOADS")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline (0 disables it)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from efficient_transformer_attention_amd import flashgau as fg
+    from efficient_transformer_attention_amd import inputs as gen
+
+    name = args.workload or gen.HEADLINE
+    B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
+    inp = gen.workload_inputs(name, seed=0)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+    esz = 2 if dtype == "bf16" else 4
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    X, Wu, Wv, Wz, Wo = (up(a) for a in (inp.X, inp.W_u, inp.W_v, inp.W_z, inp.W_o))
+    gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, n, d), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ptrs = (X.data_ptr(), Wu.data_ptr(), Wv.data_ptr(), Wz.data_ptr(), gamma.data_ptr(),
+            beta.data_ptr(), Wo.data_ptr())
+    nst = len(fg.STAGES)
+    events = HipEvents(args.steps * (nst + 1))
+
+    def step(k=None):
+        if k is None:
+            rc = fg.forward_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
+                                nbytes, stream)
+        else:
+            evs = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+            rc = fg.forward_timed_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(),
+                                      ws.data_ptr(), nbytes, stream, evs)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_forward")
+
+    print(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("[bench] timed region done", file=sys.stderr, flush=True)
+
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {st: [] for st in fg.STAGES}
+    gpu_ms = []
+    for k in range(args.steps):
+        h = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+        for i, st in enumerate(fg.STAGES):
+            stage_ms[st].append(events.ms(h[i], h[i + 1]))
+        gpu_ms.append(events.ms(h[0], h[nst]))
+    events.close()
+    stage_avg = {st: statistics.mean(v) for st, v in stage_ms.items()}
+
+    flops = alg_flops(B, n, d, e, s, c, causal)
+    nbytes_alg = alg_bytes(B, n, d, e, s, c, causal, esz)
+    total_flops = sum(flops.values())
+    tokens = B * n
+    value = tokens / (ms_step / 1e3)
+    peak = PEAK[dtype]
+    stages = {}
+    for st in fg.STAGES:
+        t = stage_avg[st] / 1e3
+        stages[st] = {"us": round(stage_avg[st] * 1e3, 2),
+                      "tflops": round(flops[st] / t / 1e12, 2) if flops[st] else 0.0,
+                      "gbs": round(nbytes_alg[st] / t / 1e9, 1)}
+    dom = max(fg.STAGES, key=lambda st: stage_avg[st])
+    t_dom = stage_avg[dom] / 1e3
+    if BOUND[dom] == "mfma":
+        achieved, pk, unit = flops[dom] / t_dom / 1e12, peak, "TFLOP/s"
+    else:
+        achieved, pk, unit = nbytes_alg[dom] / t_dom / 1e9, HBM_PEAK, "GB/s"
+    roofline = {"kernel": dom, "bound": BOUND[dom], "achieved": round(achieved, 2), "peak": pk,
+                "unit": unit, "frac": round(achieved / pk, 4), "traffic": None}
+
+    cpu = None
+    max_rel_err = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu, ref = cpu_baseline(inp, args.cpu_seconds)
+        got = O[:1].float().cpu().numpy().astype(np.float64)
+        max_rel_err = float(np.abs(got - ref).max() / np.abs(ref).max())
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "seq_len": n, "d": d, "e": e, "s": s,
+                   "chunk": c, "causal": causal},
+        "frac_bf16_peak": round(total_flops / (ms_step / 1e3) / 1e12 / PEAK["bf16"], 4)
+        if dtype == "bf16" else None,
+        "alg_gflop": round(total_flops / 1e9, 2),
+        "gpu_ms_per_step": round(statistics.mean(gpu_ms), 4),
+        "roofline": roofline,
+        "stages": stages,
+        "cpu_baseline": cpu,
+        "max_rel_err_seq0": max_rel_err,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,870 @@
+// flashgau.hip — FLASH layer forward for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// The layer (page "FLASH: Possibly the Most Interesting Efficient Transformer Design Recently",
+// kexue.fm/archives/8934, sections "Initial Power", "Weak Attention" and "Mixed Chunk"):
+//   U = SiLU(X W_u), V = SiLU(X W_v), Z = SiLU(X W_z); four scale/offset heads of Z;
+//   local relu²(Q_quad K_quadᵀ / c) V inside each chunk (causal: lower triangle);
+//   global Q_lin S_g / n with S_g = Σ K_lin_hᵀ V_h over all chunks (non-causal) or h < g (causal);
+//   O = [U ⊙ (V̂_quad + V̂_lin)] W_o.
+//
+// Every step is a dense contraction, so every kernel here is one tiled matrix-core GEMM with its
+// own operand sources and epilogue:
+//   pack    W_u|W_v|W_z and W_o transposed so that every GEMM reads K-contiguous rows
+//   proj    H = X [W_u|W_v|W_z]; epilogue SiLU, the four heads, V and K_lin written chunk-transposed
+//   scores  per chunk P = relu(Q_quad K_quadᵀ / c)², zero above the diagonal when causal
+//   states  per (sequence, e-tile): the accumulator runs over the chunks in order, so it IS the
+//           prefix Σ_{h<g} K_lin_hᵀ V_h; it is written (scaled by 1/n) before chunk g is added
+//   mix     per chunk, (V̂_quad + V̂_lin)ᵀ = [V_gᵀ | S_gᵀ] [P_g | Q_lin_g]ᵀ, one GEMM with the local
+//           and the global term concatenated along K; epilogue Y = U ⊙ (·)
+//   out     O = Y W_o (computed as Oᵀ tiles so each lane stores contiguous outputs)
+//
+// Matrix-core mapping (CDNA4): bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses four
+// v_mfma_f32_16x16x4_f32. Operand tiles are staged in LDS as rows of 128 bytes (8 chunks of 16 B);
+// the 16-byte chunk index is XOR-swizzled with the row index so that both the row-wise fills and
+// the fragment reads of 16 consecutive rows are free of bank conflicts. Two LDS stages alternate:
+// global loads of tile t+1 are in flight while tile t is multiplied.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "flashgau.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, each with a private L2
+constexpr int kRowChunks = 8;   // 16-byte chunks per LDS row and K-stage (128 bytes)
+constexpr int kStageBytes = kRowChunks * 16;
+
+// ------------------------------------------------------------------------------ element types
+struct BF16 {
+  using T = uint16_t;  // raw bf16 bits
+  static constexpr int kSize = 2;
+};
+struct F32 {
+  using T = float;
+  static constexpr int kSize = 4;
+};
+
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+// fp32 -> bf16, round to nearest even on the 16 dropped bits.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <class E>
+__device__ __forceinline__ typename E::T from_f32(float f);
+template <>
+__device__ __forceinline__ uint16_t from_f32<BF16>(float f) { return f32_to_bf16(f); }
+template <>
+__device__ __forceinline__ float from_f32<F32>(float f) { return f; }
+
+// Store four consecutive elements (8-byte aligned for bf16, 16-byte aligned for fp32).
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  u32x2 v;
+  v[0] = uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  v[1] = uint32_t(f32_to_bf16(c)) | (uint32_t(f32_to_bf16(d)) << 16);
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float* o) {
+  u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  o[0] = __uint_as_float(v[0] << 16);
+  o[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+  o[2] = __uint_as_float(v[1] << 16);
+  o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v[0];
+  o[1] = v[1];
+  o[2] = v[2];
+  o[3] = v[3];
+}
+
+// SiLU(x) = x · sigmoid(x) ("Initial Power": Swish on U and V; read as phi_z too).
+// e^{-x} is evaluated as 2^{-x·log2 e} on the hardware base-2 exponential (v_exp_f32) and the
+// quotient through the hardware reciprocal (v_rcp_f32). Large negative x gives 2^{+big} = inf,
+// rcp(inf) = 0 and the exact limit -0.
+__device__ __forceinline__ float silu(float x) {
+  const float t = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+// ------------------------------------------------------------------------------ matrix cores
+// One 16-byte chunk per lane and operand: 8 bf16 (one 16x16x32 MFMA) or 4 fp32 (four 16x16x4
+// MFMAs, component j of every lane group forming one k-slice). Lane l supplies row (l % 16) of A
+// and column (l % 16) of B; lane group l / 16 selects the chunk, identically for A and B, so the
+// sum over all chunks is the full contraction.
+__device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, BF16) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, F32) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
+}
+
+// A K-contiguous operand: `rows` valid rows starting at `ptr`, `ld` bytes apart, each holding
+// `kbytes` valid bytes (a multiple of 16). Loads outside either extent return zeros.
+struct Src {
+  const char* ptr;
+  int64_t ld;
+  int rows;
+  int kbytes;
+};
+
+__device__ __forceinline__ Src make_src(const void* base, int64_t row0, int64_t ld_elems, int esz,
+                                        int rows, int k_elems) {
+  Src s;
+  s.ptr = reinterpret_cast<const char*>(base) + row0 * ld_elems * esz;
+  s.ld = ld_elems * esz;
+  s.rows = rows;
+  s.kbytes = k_elems * esz;
+  return s;
+}
+
+// Hardware places consecutive workgroup ids on consecutive XCDs (round robin). Give each XCD a
+// contiguous range of logical tiles, so tiles that share operand rows also share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid % kXcds;
+  const int local = bid / kXcds;
+  const int per = nblocks / kXcds;
+  const int rem = nblocks % kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
+template <class E, int BM, int BN, int WM, int WN>
+struct TileGemm {
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int WTM = BM / WM;
+  static constexpr int WTN = BN / WN;
+  static constexpr int TM = WTM / 16;
+  static constexpr int TN = WTN / 16;
+  static constexpr int ALD = BM * kRowChunks / kThreads;
+  static constexpr int BLD = BN * kRowChunks / kThreads;
+  static constexpr int kStage = (BM + BN) * kRowChunks;  // u32x4 elements per stage
+  static constexpr int kLds = 2 * kStage;
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert((BM * kRowChunks) % kThreads == 0 && (BN * kRowChunks) % kThreads == 0,
+                "tile rows must spread evenly over the threads");
+
+  f32x4 acc[TM][TN];
+  u32x4 ra[ALD];
+  u32x4 rb[BLD];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  template <int N, int R>
+  __device__ __forceinline__ static void gload(u32x4 (&reg)[N], const Src& s, int kb0, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kThreads;
+      const int r = i >> 3;
+      const int kb = kb0 + (i & 7) * 16;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < s.rows && kb < s.kbytes)
+        v = *reinterpret_cast<const u32x4*>(s.ptr + int64_t(r) * s.ld + kb);
+      reg[j] = v;
+    }
+  }
+
+  template <int N>
+  __device__ __forceinline__ static void lstore(u32x4* lds, const u32x4 (&reg)[N], int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kThreads;
+      const int r = i >> 3;
+      lds[r * kRowChunks + ((i & 7) ^ (r & 7))] = reg[j];
+    }
+  }
+
+  __device__ __forceinline__ void load(const Src& a, int ka, const Src& b, int kb, int tid) {
+    gload<ALD, BM>(ra, a, ka, tid);
+    gload<BLD, BN>(rb, b, kb, tid);
+  }
+
+  __device__ __forceinline__ void stage_store(u32x4* stage, int tid) {
+    lstore<ALD>(stage, ra, tid);
+    lstore<BLD>(stage + BM * kRowChunks, rb, tid);
+  }
+
+  __device__ __forceinline__ void compute(const u32x4* stage, int wm, int wn, int lane) {
+    const u32x4* As = stage;
+    const u32x4* Bs = stage + BM * kRowChunks;
+    const int lr = lane & 15;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < kRowChunks / 4; ++ks) {
+      const int ch = (ks * 4 + q) ^ (lr & 7);  // rows below differ from lr by multiples of 16
+      u32x4 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = As[(wm * WTM + i * 16 + lr) * kRowChunks + ch];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = Bs[(wn * WTN + j * 16 + lr) * kRowChunks + ch];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mma(acc[i][j], a[i], b[j], E());
+    }
+  }
+
+  // Runs K-tiles 0..nt-1. tiles(t, a, ka, b, kb) names the operands and byte offsets of tile t;
+  // pre(t) runs right before tile t is multiplied (it may read the accumulators).
+  template <class Tiles, class Pre>
+  __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, int tid,
+                                      int wm, int wn, int lane) {
+    if (nt <= 0) return;
+    Src a, b;
+    int ka, kb;
+    tiles(0, a, ka, b, kb);
+    load(a, ka, b, kb, tid);
+    stage_store(lds, tid);
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      u32x4* cur = lds + (t & 1) * kStage;
+      u32x4* nxt = lds + ((t + 1) & 1) * kStage;
+      const bool more = t + 1 < nt;
+      if (more) {
+        tiles(t + 1, a, ka, b, kb);
+        load(a, ka, b, kb, tid);
+      }
+      pre(t);
+      compute(cur, wm, wn, lane);
+      if (more) stage_store(nxt, tid);
+      __syncthreads();
+    }
+  }
+
+  // Calls f(row, col, acc) for each 16x16 fragment: rows row..row+3 of column col (tile-local).
+  template <class F>
+  __device__ __forceinline__ void epilogue(int wm, int wn, int lane, F&& f) const {
+    const int lr = lane & 15;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) f(wm * WTM + i * 16 + q * 4, wn * WTN + j * 16 + lr, acc[i][j]);
+  }
+};
+
+struct NoPre {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// ------------------------------------------------------------------------------ pack
+template <class E>
+struct TransposeJob {
+  const typename E::T* src;  // [R, C]
+  typename E::T* dst;        // [C, R]
+  int R, C;
+};
+template <class E>
+struct PackArgs {
+  TransposeJob<E> job[4];
+};
+
+template <class E>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs<E> args) {
+  using T = typename E::T;
+  __shared__ T tile[64][65];
+  const TransposeJob<E> jb = args.job[blockIdx.z];
+  const int r0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  if (r0 >= jb.R || c0 >= jb.C) return;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = tid + i * 256;
+    const int rr = idx >> 6, cc = idx & 63;
+    if (r0 + rr < jb.R && c0 + cc < jb.C) tile[rr][cc] = jb.src[int64_t(r0 + rr) * jb.C + c0 + cc];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = tid + i * 256;
+    const int cc = idx >> 6, rr = idx & 63;
+    if (r0 + rr < jb.R && c0 + cc < jb.C) jb.dst[int64_t(c0 + cc) * jb.R + r0 + rr] = tile[rr][cc];
+  }
+}
+
+// ------------------------------------------------------------------------------ proj
+template <class E>
+struct ProjArgs {
+  const typename E::T* X;      // [M, d]
+  const typename E::T* WcatT;  // [2e+s, d]
+  typename E::T* U;            // [M, e]
+  typename E::T* Vt;           // [M/c, e, c]
+  typename E::T* Qq;           // [M, s]
+  typename E::T* Kq;           // [M, s]
+  typename E::T* Ql;           // [M, s]
+  typename E::T* Klt;          // [M/c, s, c]
+  const float* gamma;          // [4, s]
+  const float* beta;           // [4, s]
+  int M, d, e, s, c;
+};
+
+template <class E, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
+  using G = TileGemm<E, BM, BN, WM, WN>;
+  using T = typename E::T;
+  __shared__ u32x4 lds[G::kLds];
+  const int ncols = 2 * p.e + p.s;
+  const int ntn = (ncols + BN - 1) / BN;
+  const int ntm = (p.M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, ntm * ntn);
+  const int mt = lid / ntn, nt = lid % ntn;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  G g;
+  g.zero();
+  const Src a = make_src(p.X, m0, p.d, E::kSize, p.M - m0, p.d);
+  const Src b = make_src(p.WcatT, n0, p.d, E::kSize, ncols - n0, p.d);
+  const int nk = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
+  g.run(lds, nk,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          sa = a;
+          sb = b;
+          ka = kb = t * kStageBytes;
+        },
+        NoPre(), tid, wm, wn, lane);
+
+  const int e = p.e, s = p.s, c = p.c;
+  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+    const int row = m0 + r, col = n0 + cl;
+    if (row >= p.M || col >= ncols) return;
+    float y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = silu(v[k]);
+    const int64_t bg = row / c, t = row % c;  // c % 8 == 0: rows row..row+3 share a chunk
+    if (col < e) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p.U[int64_t(row + k) * e + col] = from_f32<E>(y[k]);
+    } else if (col < 2 * e) {
+      store4(p.Vt + (bg * e + (col - e)) * c + t, y[0], y[1], y[2], y[3]);
+    } else {
+      const int j = col - 2 * e;
+      const float g0 = p.gamma[j], g1 = p.gamma[s + j], g2 = p.gamma[2 * s + j], g3 = p.gamma[3 * s + j];
+      const float b0 = p.beta[j], b1 = p.beta[s + j], b2 = p.beta[2 * s + j], b3 = p.beta[3 * s + j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t o = int64_t(row + k) * s + j;
+        p.Qq[o] = from_f32<E>(fmaf(g0, y[k], b0));
+        p.Kq[o] = from_f32<E>(fmaf(g1, y[k], b1));
+        p.Ql[o] = from_f32<E>(fmaf(g2, y[k], b2));
+      }
+      store4(p.Klt + (bg * s + j) * c + t, fmaf(g3, y[0], b3), fmaf(g3, y[1], b3),
+             fmaf(g3, y[2], b3), fmaf(g3, y[3], b3));
+    }
+  });
+}
+
+// ------------------------------------------------------------------------------ scores
+template <class E>
+struct ScoresArgs {
+  const typename E::T* Qq;  // [nbg*c, s]
+  const typename E::T* Kq;  // [nbg*c, s]
+  typename E::T* P;         // [nbg, c, c]
+  int nbg, c, s, causal;
+  float inv_c;
+};
+
+template <class E, int BT, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
+  using G = TileGemm<E, BT, BT, WM, WN>;
+  __shared__ u32x4 lds[G::kLds];
+  const int ntc = (p.c + BT - 1) / BT;
+  const int lid = xcd_remap(blockIdx.x, p.nbg * ntc * ntc);
+  const int bg = lid / (ntc * ntc);
+  const int rem = lid % (ntc * ntc);
+  const int mt = rem / ntc, nt = rem % ntc;
+  const int m0 = mt * BT, n0 = nt * BT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  G g;
+  g.zero();
+  // A tile entirely above the diagonal (every key after every query) stays zero when causal.
+  const bool live = !(p.causal && n0 > m0 + BT - 1);
+  if (live) {
+    const int64_t base = int64_t(bg) * p.c;
+    const Src a = make_src(p.Qq, base + m0, p.s, E::kSize, p.c - m0, p.s);
+    const Src b = make_src(p.Kq, base + n0, p.s, E::kSize, p.c - n0, p.s);
+    const int nk = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
+    g.run(lds, nk,
+          [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+            sa = a;
+            sb = b;
+            ka = kb = t * kStageBytes;
+          },
+          NoPre(), tid, wm, wn, lane);
+  }
+  typename E::T* P = p.P + int64_t(bg) * p.c * p.c;
+  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+    const int i = m0 + r, j = n0 + cl;
+    if (i >= p.c || j >= p.c) return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x = fmaxf(v[k] * p.inv_c, 0.0f);
+      const float w = (p.causal && j > i + k) ? 0.0f : x * x;
+      P[int64_t(i + k) * p.c + j] = from_f32<E>(w);
+    }
+  });
+}
+
+// ------------------------------------------------------------------------------ states
+template <class E>
+struct StatesArgs {
+  const typename E::T* Klt;  // [B*G, s, c]
+  const typename E::T* Vt;   // [B*G, e, c]
+  typename E::T* St;         // causal [B*G, e, s], non-causal [B, e, s]
+  int B, G, s, e, c, causal;
+  float inv_n;
+};
+
+template <class E, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
+  using G = TileGemm<E, BM, BN, WM, WN>;
+  __shared__ u32x4 lds[G::kLds];
+  const int nts = (p.s + BM - 1) / BM;
+  const int nte = (p.e + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, p.B * nts * nte);
+  const int b = lid / (nts * nte);
+  const int rem = lid % (nts * nte);
+  const int mt = rem / nte, nt = rem % nte;
+  const int m0 = mt * BM, n0 = nt * BN;  // m: state row (s), n: value column (e)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int nk = (p.c * E::kSize + kStageBytes - 1) / kStageBytes;
+  const int64_t seq0 = int64_t(b) * p.G;
+
+  auto write_state = [&](G& gg, int64_t slot) {
+    typename E::T* St = p.St + slot * p.e * p.s;
+    gg.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+      const int i = m0 + r, j = n0 + cl;
+      if (i >= p.s || j >= p.e) return;
+      store4(St + int64_t(j) * p.s + i, v[0] * p.inv_n, v[1] * p.inv_n, v[2] * p.inv_n,
+             v[3] * p.inv_n);
+    });
+  };
+
+  G g;
+  g.zero();
+  g.run(lds, p.G * nk,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          const int64_t chunk = seq0 + t / nk;
+          sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, p.c);
+          sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, p.c);
+          ka = kb = (t % nk) * kStageBytes;
+        },
+        [&](int t) {
+          // exclusive prefix: chunk g reads the sum of chunks before it
+          if (p.causal && t % nk == 0) write_state(g, seq0 + t / nk);
+        },
+        tid, wm, wn, lane);
+  if (!p.causal) write_state(g, b);
+}
+
+// ------------------------------------------------------------------------------ mix
+template <class E>
+struct MixArgs {
+  const typename E::T* Vt;  // [B*G, e, c]
+  const typename E::T* St;  // causal [B*G, e, s], non-causal [B, e, s]
+  const typename E::T* P;   // [B*G, c, c]
+  const typename E::T* Ql;  // [B*G*c, s]
+  const typename E::T* U;   // [B*G*c, e]
+  typename E::T* Y;         // [B*G*c, e]
+  int nbg, G, c, e, s, causal;
+};
+
+template <class E, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
+  using G = TileGemm<E, BM, BN, WM, WN>;
+  __shared__ u32x4 lds[G::kLds];
+  const int nte = (p.e + BM - 1) / BM;
+  const int ntt = (p.c + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, p.nbg * nte * ntt);
+  const int bg = lid / (nte * ntt);
+  const int rem = lid % (nte * ntt);
+  const int nt = rem / nte, mt = rem % nte;
+  const int m0 = mt * BM, n0 = nt * BN;  // m: value column (e), n: token inside the chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Causal: tokens n0..n0+BN-1 attend to keys 0..n0+BN-1 of their chunk only; P is zero above
+  // the diagonal, so stopping the key range there is exact.
+  const int keys = p.causal ? min(p.c, n0 + BN) : p.c;
+  const int nk0 = (keys * E::kSize + kStageBytes - 1) / kStageBytes;
+  const int nk1 = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
+  const int64_t tok0 = int64_t(bg) * p.c;
+  const int64_t slot = p.causal ? bg : bg / p.G;
+  const Src a0 = make_src(p.Vt, int64_t(bg) * p.e + m0, p.c, E::kSize, p.e - m0, p.c);
+  const Src b0 = make_src(p.P, tok0 + n0, p.c, E::kSize, p.c - n0, p.c);
+  const Src a1 = make_src(p.St, slot * p.e + m0, p.s, E::kSize, p.e - m0, p.s);
+  const Src b1 = make_src(p.Ql, tok0 + n0, p.s, E::kSize, p.c - n0, p.s);
+
+  G g;
+  g.zero();
+  g.run(lds, nk0 + nk1,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          if (t < nk0) {
+            sa = a0;
+            sb = b0;
+            ka = kb = t * kStageBytes;
+          } else {
+            sa = a1;
+            sb = b1;
+            ka = kb = (t - nk0) * kStageBytes;
+          }
+        },
+        NoPre(), tid, wm, wn, lane);
+
+  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+    const int j = m0 + r, i = n0 + cl;  // j: value column (4 consecutive), i: token
+    if (j >= p.e || i >= p.c) return;
+    const int64_t o = (tok0 + i) * p.e + j;
+    float u[4];
+    load4(p.U + o, u);
+    store4(p.Y + o, u[0] * v[0], u[1] * v[1], u[2] * v[2], u[3] * v[3]);
+  });
+}
+
+// ------------------------------------------------------------------------------ out
+template <class E>
+struct OutArgs {
+  const typename E::T* WoT;  // [d, e]
+  const typename E::T* Y;    // [M, e]
+  typename E::T* O;          // [M, d]
+  int M, d, e;
+};
+
+template <class E, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
+  using G = TileGemm<E, BM, BN, WM, WN>;
+  __shared__ u32x4 lds[G::kLds];
+  const int ntd = (p.d + BM - 1) / BM;
+  const int ntt = (p.M + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, ntd * ntt);
+  const int nt = lid / ntd, mt = lid % ntd;
+  const int m0 = mt * BM, n0 = nt * BN;  // m: output feature (d), n: token
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  G g;
+  g.zero();
+  const Src a = make_src(p.WoT, m0, p.e, E::kSize, p.d - m0, p.e);
+  const Src b = make_src(p.Y, n0, p.e, E::kSize, p.M - n0, p.e);
+  const int nk = (p.e * E::kSize + kStageBytes - 1) / kStageBytes;
+  g.run(lds, nk,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          sa = a;
+          sb = b;
+          ka = kb = t * kStageBytes;
+        },
+        NoPre(), tid, wm, wn, lane);
+  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+    const int j = m0 + r, i = n0 + cl;  // j: feature (4 consecutive), i: token
+    if (j >= p.d || i >= p.M) return;
+    store4(p.O + int64_t(i) * p.d + j, v[0], v[1], v[2], v[3]);
+  });
+}
+
+// ------------------------------------------------------------------------------ tile shapes
+// (BM, BN, waves along M, waves along N) per kernel and element type.
+template <class E> struct Shapes;
+template <> struct Shapes<BF16> {
+  static constexpr int kProjBM = 256, kProjBN = 128, kProjWM = 2, kProjWN = 2;
+  static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
+  static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kMixBM = 128, kMixBN = 128, kMixWM = 2, kMixWN = 2;
+  static constexpr int kOutBM = 128, kOutBN = 256, kOutWM = 2, kOutWN = 2;
+};
+template <> struct Shapes<F32> {
+  static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2;
+  static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
+  static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2;
+  static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2;
+};
+
+// ------------------------------------------------------------------------------ host side
+struct Plan {
+  int64_t B, n, d, e, s, c, G, M, nbg, ncols;
+  int64_t esz;
+  size_t off[FLASHGAU_WS_COUNT];
+  size_t total;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-bit grid
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
+              flashgau_dtype dtype, Plan* p) {
+  if (dtype != FLASHGAU_F32 && dtype != FLASHGAU_BF16) return FLASHGAU_ERR_UNSUPPORTED;
+  if (B < 0 || n < 0 || d < 1 || e < 1 || s < 1 || chunk < 1) return FLASHGAU_ERR_BAD_SHAPE;
+  if (n % chunk != 0) return FLASHGAU_ERR_BAD_SHAPE;
+  if (d % 8 || e % 8 || s % 8 || chunk % 8) return FLASHGAU_ERR_UNSUPPORTED;
+  memset(p, 0, sizeof(*p));
+  p->B = B; p->n = n; p->d = d; p->e = e; p->s = s; p->c = chunk;
+  p->esz = dtype == FLASHGAU_BF16 ? 2 : 4;
+  int64_t M;
+  if (!mul_ok(B, n, &M) || M > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
+  p->M = M;
+  p->G = chunk > 0 ? n / chunk : 0;
+  p->nbg = B * p->G;
+  p->ncols = 2 * e + s;
+  if (d > kInt32Max || p->ncols > kInt32Max || chunk > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
+  if (M == 0) {
+    p->total = 0;
+    return FLASHGAU_OK;
+  }
+  // Element counts of each buffer; every product is checked.
+  int64_t cnt[FLASHGAU_WS_COUNT];
+  int64_t t0;
+  if (!mul_ok(p->ncols, d, &cnt[FLASHGAU_WS_WCAT_T])) return FLASHGAU_ERR_BAD_SHAPE;
+  if (!mul_ok(d, e, &cnt[FLASHGAU_WS_WO_T])) return FLASHGAU_ERR_BAD_SHAPE;
+  if (!mul_ok(M, e, &cnt[FLASHGAU_WS_U])) return FLASHGAU_ERR_BAD_SHAPE;
+  cnt[FLASHGAU_WS_VT] = cnt[FLASHGAU_WS_U];
+  if (!mul_ok(M, s, &cnt[FLASHGAU_WS_QQ])) return FLASHGAU_ERR_BAD_SHAPE;
+  cnt[FLASHGAU_WS_KQ] = cnt[FLASHGAU_WS_QL] = cnt[FLASHGAU_WS_KLT] = cnt[FLASHGAU_WS_QQ];
+  if (!mul_ok(M, chunk, &cnt[FLASHGAU_WS_P])) return FLASHGAU_ERR_BAD_SHAPE;
+  if (!mul_ok(causal ? p->nbg : B, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_ST]))
+    return FLASHGAU_ERR_BAD_SHAPE;
+  cnt[FLASHGAU_WS_Y] = cnt[FLASHGAU_WS_U];
+  size_t off = 0;
+  for (int i = 0; i < FLASHGAU_WS_COUNT; ++i) {
+    int64_t bytes;
+    if (!mul_ok(cnt[i], p->esz, &bytes)) return FLASHGAU_ERR_BAD_SHAPE;
+    p->off[i] = off;
+    const size_t padded = (size_t(bytes) + 255) & ~size_t(255);
+    if (__builtin_add_overflow(off, padded, &off)) return FLASHGAU_ERR_BAD_SHAPE;
+  }
+  p->total = off;
+  // Grid sizes of every launch (the largest tile counts use the smallest tiles).
+  const int64_t grids[] = {
+      cdiv(M, 128) * cdiv(p->ncols, 128),
+      p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64),
+      B * cdiv(s, 128) * cdiv(e, 64),
+      p->nbg * cdiv(e, 128) * cdiv(chunk, 64),
+      cdiv(d, 128) * cdiv(M, 128),
+  };
+  for (int64_t g : grids)
+    if (g > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
+  if (cdiv(std::max(std::max(d, e), s), 64) > 65535) return FLASHGAU_ERR_BAD_SHAPE;
+  return FLASHGAU_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+template <class E>
+int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
+               const float* gamma, const float* beta, const void* W_o, int causal, void* O,
+               char* ws, hipStream_t stream, hipEvent_t const* events) {
+  using T = typename E::T;
+  using S = Shapes<E>;
+  // events (optional): events[i] is recorded right before stage i is launched, and
+  // events[FLASHGAU_NUM_STAGES] after the last one.
+  int stage = 0;
+  auto mark = [&]() -> bool {
+    if (!events) return true;
+    return hipEventRecord(events[stage++], stream) == hipSuccess;
+  };
+  T* WcatT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WCAT_T]);
+  T* WoT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WO_T]);
+  T* U = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_U]);
+  T* Vt = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_VT]);
+  T* Qq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_QQ]);
+  T* Kq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_KQ]);
+  T* Ql = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_QL]);
+  T* Klt = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_KLT]);
+  T* P = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_P]);
+  T* St = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_ST]);
+  T* Y = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_Y]);
+  const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
+
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  // pack: (W_u | W_v | W_z)ᵀ and W_oᵀ
+  {
+    PackArgs<E> a;
+    a.job[0] = {reinterpret_cast<const T*>(W_u), WcatT, d, e};
+    a.job[1] = {reinterpret_cast<const T*>(W_v), WcatT + int64_t(e) * d, d, e};
+    a.job[2] = {reinterpret_cast<const T*>(W_z), WcatT + int64_t(2 * e) * d, d, s};
+    a.job[3] = {reinterpret_cast<const T*>(W_o), WoT, e, d};
+    const int64_t mx = std::max(std::max(d, e), s);
+    dim3 grid(unsigned(cdiv(mx, 64)), unsigned(cdiv(mx, 64)), 4);
+    hipLaunchKernelGGL(pack_kernel<E>, grid, dim3(256), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  {
+    ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT, U, Vt, Qq, Kq, Ql, Klt, gamma, beta,
+                  M, d, e, s, c};
+    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
+    hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN>),
+                       dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  {
+    ScoresArgs<E> a{Qq, Kq, P, int(pl.nbg), c, s, causal, 1.0f / float(c)};
+    const int64_t nb = pl.nbg * cdiv(c, S::kScoresBT) * cdiv(c, S::kScoresBT);
+    hipLaunchKernelGGL((scores_kernel<E, S::kScoresBT, S::kScoresWM, S::kScoresWN>),
+                       dim3(unsigned(nb)), dim3(64 * S::kScoresWM * S::kScoresWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  {
+    StatesArgs<E> a{Klt, Vt, St, int(pl.B), int(pl.G), s, e, c, causal, float(1.0 / double(pl.n))};
+    const int64_t nb = pl.B * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
+    hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN>),
+                       dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  {
+    MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal};
+    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
+    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN>),
+                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  {
+    OutArgs<E> a{WoT, Y, reinterpret_cast<T*>(O), M, d, e};
+    const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
+    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN>),
+                       dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flashgau_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                            int causal, flashgau_dtype dtype, size_t* out_bytes) {
+  if (!out_bytes) return FLASHGAU_ERR_NULL_PTR;
+  Plan p;
+  const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &p);
+  if (rc != FLASHGAU_OK) return rc;
+  *out_bytes = p.total;
+  return FLASHGAU_OK;
+}
+
+int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                               int64_t chunk, int causal, flashgau_dtype dtype,
+                               size_t* out_offsets) {
+  if (!out_offsets) return FLASHGAU_ERR_NULL_PTR;
+  Plan p;
+  const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &p);
+  if (rc != FLASHGAU_OK) return rc;
+  for (int i = 0; i < FLASHGAU_WS_COUNT; ++i) out_offsets[i] = p.off[i];
+  return FLASHGAU_OK;
+}
+
+static int forward_impl(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                        const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                        int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                        flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
+                        void* hip_stream, hipEvent_t const* events) {
+  Plan pl;
+  const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &pl);
+  if (rc != FLASHGAU_OK) return rc;
+  if (pl.M == 0) return FLASHGAU_OK;
+  if (!X || !W_u || !W_v || !W_z || !gamma || !beta || !W_o || !O || !workspace)
+    return FLASHGAU_ERR_NULL_PTR;
+  if (misaligned(X) || misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o) ||
+      misaligned(O) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return FLASHGAU_ERR_MISALIGNED;
+  if (workspace_bytes < pl.total) return FLASHGAU_ERR_WORKSPACE;
+  const size_t es = size_t(pl.esz);
+  const size_t nX = size_t(pl.M) * pl.d * es, nO = nX;
+  const size_t nWu = size_t(pl.d) * pl.e * es, nWz = size_t(pl.d) * pl.s * es;
+  const size_t nWo = size_t(pl.e) * pl.d * es, nGB = size_t(4) * pl.s * sizeof(float);
+  const void* ins[] = {X, W_u, W_v, W_z, W_o, gamma, beta};
+  const size_t nin[] = {nX, nWu, nWu, nWz, nWo, nGB, nGB};
+  for (int i = 0; i < 7; ++i)
+    if (overlaps(O, nO, ins[i], nin[i]) || overlaps(workspace, pl.total, ins[i], nin[i]))
+      return FLASHGAU_ERR_ALIASING;
+  if (overlaps(O, nO, workspace, pl.total)) return FLASHGAU_ERR_ALIASING;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == FLASHGAU_BF16)
+    return launch_all<BF16>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, O, ws, stream,
+                            events);
+  return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, O, ws, stream,
+                         events);
+}
+
+int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                      const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                      int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                      flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                      workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                            const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                            int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                            flashgau_dtype dtype, void* O, void* workspace,
+                            size_t workspace_bytes, void* hip_stream, void* const* stage_events,
+                            int num_events) {
+  if (!stage_events) return FLASHGAU_ERR_NULL_PTR;
+  if (num_events != FLASHGAU_NUM_STAGES + 1) return FLASHGAU_ERR_BAD_SHAPE;
+  for (int i = 0; i < num_events; ++i)
+    if (!stage_events[i]) return FLASHGAU_ERR_NULL_PTR;
+  return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                      workspace, workspace_bytes, hip_stream,
+                      reinterpret_cast<hipEvent_t const*>(stage_events));
+}
+
+const char* flashgau_strerror(int code) {
+  switch (code) {
+    case FLASHGAU_OK: return "success";
+    case FLASHGAU_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FLASHGAU_ERR_BAD_SHAPE: return "bad shape (size < 1, n % chunk != 0, or a size overflows)";
+    case FLASHGAU_ERR_UNSUPPORTED: return "unsupported (dtype, or d, e, s, chunk not a multiple of 8)";
+    case FLASHGAU_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+    case FLASHGAU_ERR_WORKSPACE: return "workspace smaller than flashgau_workspace_size()";
+    case FLASHGAU_ERR_ALIASING: return "output or workspace overlaps an input or each other";
+    case FLASHGAU_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+"""Python binding of libflashgau.so (include/flashgau.h): argument marshalling only.
+
+Every step of the layer runs in the HIP kernels of the library; this module checks tensor
+metadata, allocates the output and the workspace with torch (caller-owned device memory, the
+library itself never allocates) and passes raw pointers and torch's current stream. There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libflashgau.so")
+
+F32 = 0
+BF16 = 1
+
+OK = 0
+ERR_NULL_PTR = -1
+ERR_BAD_SHAPE = -2
+ERR_UNSUPPORTED = -3
+ERR_MISALIGNED = -4
+ERR_WORKSPACE = -5
+ERR_ALIASING = -6
+ERR_HIP = -7
+
+# Order of the workspace buffers (FLASHGAU_WS_* in include/flashgau.h).
+WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y")
+
+EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flash_gau_forward",
+           "flash_gau_forward_timed", "flashgau_strerror")
+
+# Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
+STAGES = ("pack", "proj", "scores", "states", "mix", "out")
+
+_lib = None
+
+
+class FlashGauError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflashgau.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(python -m efficient_transformer_attention_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, sz = ctypes.c_int64, ctypes.c_size_t
+    L.flashgau_workspace_size.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_workspace_size.restype = ctypes.c_int
+    L.flashgau_workspace_offsets.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_workspace_offsets.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    L.flash_gau_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
+                                    i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
+    L.flash_gau_forward.restype = ctypes.c_int
+    L.flash_gau_forward_timed.argtypes = L.flash_gau_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
+    L.flash_gau_forward_timed.restype = ctypes.c_int
+    L.flashgau_strerror.argtypes = [ctypes.c_int]
+    L.flashgau_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().flashgau_strerror(int(code)).decode()
+
+
+def workspace_size(B, n, d, e, s, chunk, causal, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().flashgau_workspace_size(B, n, d, e, s, chunk, int(bool(causal)), dtype, ctypes.byref(out))
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_workspace_size")
+    return out.value
+
+
+def workspace_offsets(B, n, d, e, s, chunk, causal, dtype) -> dict:
+    arr = (ctypes.c_size_t * len(WS_NAMES))()
+    rc = lib().flashgau_workspace_offsets(B, n, d, e, s, chunk, int(bool(causal)), dtype, arr)
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_workspace_offsets")
+    return dict(zip(WS_NAMES, list(arr)))
+
+
+def forward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                workspace, workspace_bytes, stream) -> int:
+    """Direct call of flash_gau_forward with integer addresses; returns the library's code."""
+    return lib().flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
+                                   B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream)
+
+
+def forward_timed_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                      workspace, workspace_bytes, stream, events) -> int:
+    """flash_gau_forward_timed with integer addresses; ``events`` is a sequence of
+    len(STAGES) + 1 hipEvent_t handles (integers)."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    return lib().flash_gau_forward_timed(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
+                                         B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream,
+                                         arr, len(events))
+
+
+def _dtype_code(t):
+    import torch
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t}; use torch.bfloat16 or torch.float32")
+
+
+def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=None, workspace=None,
+                      stream=None):
+    """One FLASH layer forward on the GPU. X [B, n, d]; W_u, W_v [d, e]; W_z [d, s]; gamma, beta
+    [4, s] float32 (heads Q_quad, K_quad, Q_lin, K_lin); W_o [e, d]. X and the weights share one
+    dtype (bfloat16 or float32). Returns O [B, n, d] of that dtype. ``workspace`` (uint8, on the
+    same device) receives the intermediates; it is allocated when not given."""
+    import torch
+    B, n, d = X.shape
+    e = W_u.shape[1]
+    s = W_z.shape[1]
+    dt = _dtype_code(X.dtype)
+    for name, t, shape in (("W_u", W_u, (d, e)), ("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)),
+                           ("W_o", W_o, (e, d))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if t.dtype != X.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from X dtype {X.dtype}")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if tuple(t.shape) != (4, s) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [4, {s}]")
+    tensors = (X, W_u, W_v, W_z, gamma, beta, W_o)
+    dev = X.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous (row-major)")
+    nbytes = workspace_size(B, n, d, e, s, chunk, causal, dt)
+    if out is None:
+        out = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = forward_raw(X.data_ptr(), W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), gamma.data_ptr(),
+                     beta.data_ptr(), W_o.data_ptr(), chunk, causal, B, n, d, e, s, dt,
+                     out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    if rc != OK:
+        raise FlashGauError(rc, "flash_gau_forward")
+    return out
+
+
+def workspace_views(workspace, B, n, d, e, s, chunk, causal, dtype):
+    """Typed views of the intermediates inside a workspace filled by flash_gau_forward, with the
+    layouts documented in include/flashgau.h (for stage-by-stage checks)."""
+    import torch
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    esz = 2 if dtype == BF16 else 4
+    off = workspace_offsets(B, n, d, e, s, chunk, causal, dtype)
+    G = n // chunk
+    M = B * n
+    shapes = {
+        "WCAT_T": (2 * e + s, d), "WO_T": (d, e), "U": (M, e), "VT": (B * G, e, chunk),
+        "QQ": (M, s), "KQ": (M, s), "QL": (M, s), "KLT": (B * G, s, chunk),
+        "P": (B * G, chunk, chunk), "ST": ((B * G) if causal else B, e, s), "Y": (M, e),
+    }
+    views = {}
+    for name, shape in shapes.items():
+        count = 1
+        for x in shape:
+            count *= x
+        raw = workspace[off[name]: off[name] + count * esz]
+        views[name] = raw.view(tdt).view(shape)
+    return views

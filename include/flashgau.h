@@ -1,0 +1,148 @@
+/*
+ * flashgau.h — C ABI of the FLASH layer forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is one layer of FLASH as defined on the page "FLASH: Possibly the Most Interesting
+ * Efficient Transformer Design Recently" (kexue.fm/archives/8934): a gated attention unit whose
+ * token mixing is mixed-chunk attention.
+ *
+ *   U = SiLU(X W_u), V = SiLU(X W_v), Z = SiLU(X W_z)               ("Initial Power", eq. relu-att)
+ *   Q_quad, K_quad, Q_lin, K_lin = gamma[h] ⊙ Z + beta[h], h = 0..3   ("Mixed Chunk", four heads)
+ *   per chunk g of c tokens:
+ *     V̂_quad_g = relu(Q_quad_g K_quad_gᵀ / c)² V_g   (entries with key j > query i zeroed if causal)
+ *     V̂_lin_g  = Q_lin_g S_g / n, S_g = Σ_h K_lin_hᵀ V_h over all chunks h (non-causal) or over
+ *                the earlier chunks h < g only (causal; the first chunk reads S = 0)
+ *   O = [U ⊙ (V̂_quad + V̂_lin)] W_o                                  ("Mixed Chunk", last display)
+ *
+ * Normalisation readings (the page's constants conflict): the local term uses relu²(q·k / c), the
+ * appendix convention of "Weak Attention" applied per chunk; the global term divides by the
+ * sequence length n in both the causal and the non-causal form ("Extended Thoughts" says the
+ * appendix divides by n). SiLU is used for Z as for U and V.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense row-major; every device pointer is memory owned by the caller.
+ *   - The library never allocates, frees or synchronises and keeps no mutable global state.
+ *   - flash_gau_forward enqueues its kernels on `hip_stream` (NULL = the null stream) and returns
+ *     at once. Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Every argument is validated on the host before the first launch; on any error nothing has
+ *     been launched and nothing has been written.
+ *   - Sizes: B >= 0 and n >= 0 (B*n == 0 is an empty call that succeeds and launches nothing);
+ *     d, e, s, chunk >= 1; n % chunk == 0; d, e, s and chunk must be multiples of 8 so that
+ *     every row starts on a 16-byte boundary; every dimension and product used as a row count
+ *     must fit in int32 (B*n, 2e+s, B*(n/chunk)*max(e, s)).
+ */
+#ifndef FLASHGAU_H
+#define FLASHGAU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage and arithmetic type of X, the weights, O and every intermediate. bf16 runs accumulate
+ * in fp32 (matrix-core accumulators) and store intermediates as bf16 (round to nearest even);
+ * f32 runs are fp32 throughout. gamma and beta are always fp32. */
+typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
+
+/* Return codes. */
+#define FLASHGAU_OK 0
+#define FLASHGAU_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
+#define FLASHGAU_ERR_BAD_SHAPE (-2)   /* negative/zero size, n % chunk != 0, or a size overflows */
+#define FLASHGAU_ERR_UNSUPPORTED (-3) /* unknown dtype, or d, e, s, chunk not a multiple of 8 */
+#define FLASHGAU_ERR_MISALIGNED (-4)  /* a tensor pointer is not 16-byte aligned */
+#define FLASHGAU_ERR_WORKSPACE (-5)   /* workspace_bytes smaller than flashgau_workspace_size() */
+#define FLASHGAU_ERR_ALIASING (-6)    /* O or the workspace overlaps an input or each other */
+#define FLASHGAU_ERR_HIP (-7)         /* a kernel launch was rejected by the HIP runtime */
+
+/* Workspace buffers, in the order of their byte offsets (see flashgau_workspace_offsets). Each
+ * holds an intermediate of the one forward path; tests read them to check each stage. Layouts,
+ * with G = n / chunk and element type = the call's dtype:
+ *   WCAT_T  [2e+s, d]     transposed, concatenated projection weights (W_u | W_v | W_z)ᵀ
+ *   WO_T    [d, e]        transposed output weights W_oᵀ
+ *   U       [B*n, e]      SiLU(X W_u)
+ *   VT      [B*G, e, c]   SiLU(X W_v), transposed inside each chunk (token index fastest)
+ *   QQ, KQ, QL [B*n, s]   the heads Q_quad, K_quad, Q_lin
+ *   KLT     [B*G, s, c]   the head K_lin, transposed inside each chunk
+ *   P       [B*G, c, c]   relu(Q_quad K_quadᵀ / c)² per chunk, zero above the diagonal if causal
+ *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed
+ *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin)                                               */
+enum {
+  FLASHGAU_WS_WCAT_T = 0,
+  FLASHGAU_WS_WO_T,
+  FLASHGAU_WS_U,
+  FLASHGAU_WS_VT,
+  FLASHGAU_WS_QQ,
+  FLASHGAU_WS_KQ,
+  FLASHGAU_WS_QL,
+  FLASHGAU_WS_KLT,
+  FLASHGAU_WS_P,
+  FLASHGAU_WS_ST,
+  FLASHGAU_WS_Y,
+  FLASHGAU_WS_COUNT
+};
+
+/* Bytes of device workspace flash_gau_forward needs for this problem. Host-only; makes no HIP
+ * call. Writes the size to *out_bytes (0 for an empty problem) and returns FLASHGAU_OK, or returns
+ * an error code (same validation as flash_gau_forward) and leaves *out_bytes untouched. */
+int flashgau_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                            int causal, flashgau_dtype dtype, size_t* out_bytes);
+
+/* Byte offsets of the FLASHGAU_WS_* buffers inside the workspace (each 256-byte aligned), written
+ * to out_offsets[0 .. FLASHGAU_WS_COUNT-1]. Host-only. Returns FLASHGAU_OK or an error code. */
+int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                               int64_t chunk, int causal, flashgau_dtype dtype,
+                               size_t* out_offsets);
+
+/* One FLASH layer forward, O = FLASH(X) as defined at the top of this header.
+ *   X        [B, n, d]   dtype, device
+ *   W_u, W_v [d, e]      dtype, device
+ *   W_z      [d, s]      dtype, device
+ *   gamma    [4, s]      fp32, device; rows Q_quad, K_quad, Q_lin, K_lin
+ *   beta     [4, s]      fp32, device; same row order
+ *   W_o      [e, d]      dtype, device
+ *   chunk    c, the chunk length; causal != 0 selects the decoder (causal) form
+ *   O        [B, n, d]   dtype, device; fully overwritten
+ *   workspace, workspace_bytes: device scratch of at least flashgau_workspace_size() bytes;
+ *            may be NULL only when that size is 0. Its contents on return are the intermediates
+ *            listed above (valid once the stream has run the call).
+ *   hip_stream: a hipStream_t (NULL for the null stream).
+ * Every tensor pointer must be 16-byte aligned. O and the workspace must not overlap each other
+ * or any input. Returns FLASHGAU_OK or one of the error codes above. */
+int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                      const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                      int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                      flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/* Stages of flash_gau_forward, in launch order (one kernel each). */
+#define FLASHGAU_NUM_STAGES 6
+/* 0 pack   : transpose W_u|W_v|W_z and W_o into the workspace (WCAT_T, WO_T)
+ * 1 proj   : X W_u|W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
+ * 2 scores : per chunk relu(Q_quad K_quadᵀ / c)², masked when causal ("Mixed Chunk", local term)
+ * 3 states : per sequence the chunk prefix (causal) or total (non-causal) of K_linᵀ V, times 1/n
+ * 4 mix    : per chunk P V + Q_lin S / n, gated by U ("Mixed Chunk", both terms and the gate)
+ * 5 out    : Y W_o                                                                            */
+
+/* flash_gau_forward with per-stage timing: the same validation and the same launches, plus
+ * hipEventRecord(stage_events[i], hip_stream) right before stage i is launched and
+ * hipEventRecord(stage_events[FLASHGAU_NUM_STAGES], hip_stream) after the last stage.
+ * stage_events points to num_events == FLASHGAU_NUM_STAGES + 1 hipEvent_t handles created by the
+ * caller (NULL pointer or entry -> FLASHGAU_ERR_NULL_PTR, wrong count -> FLASHGAU_ERR_BAD_SHAPE).
+ * For an empty problem no event is recorded. Used by benchmarks to time each kernel on the stream
+ * it runs on. */
+int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                            const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                            int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                            flashgau_dtype dtype, void* O, void* workspace,
+                            size_t workspace_bytes, void* hip_stream, void* const* stage_events,
+                            int num_events);
+
+/* Static, human-readable text for a return code ("unknown error" for other values). */
+const char* flashgau_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHGAU_H */

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/flashgau.h declares,
+sizes its workspace as documented, and rejects every invalid call on the host before any launch.
+
+Every flash_gau_forward call here is built to fail one validation rule, so no kernel is ever
+launched (the addresses passed are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_transformer_attention_amd import flashgau as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashgau.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*|size_t)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert _declared_functions() == sorted(fg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(fg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_workspace_enum_matches_binding():
+    text = open(HEADER).read()
+    names = re.findall(r"FLASHGAU_WS_(\w+)\s*(?:=\s*0)?,", text)
+    assert tuple(names) == fg.WS_NAMES
+
+
+def _expected_layout(B, n, d, e, s, c, causal, esz):
+    G = n // c
+    M = B * n
+    counts = [(2 * e + s) * d, d * e, M * e, M * e, M * s, M * s, M * s, M * s, M * c,
+              (B * G if causal else B) * e * s, M * e]
+    off, offs = 0, []
+    for cnt in counts:
+        offs.append(off)
+        off += (cnt * esz + 255) // 256 * 256
+    return offs, off
+
+
+@pytest.mark.parametrize("name,args", [
+    ("c1", (1, 512, 256, 512, 128, 128, False, fg.F32)),
+    ("c3", (8, 4096, 768, 1536, 128, 256, True, fg.BF16)),
+    ("c4nc", (2, 8192, 768, 1536, 128, 512, False, fg.BF16)),
+    ("c5", (1, 32768, 1024, 2048, 128, 512, True, fg.BF16)),
+    ("ragged", (3, 72, 200, 136, 24, 24, True, fg.BF16)),
+])
+def test_workspace_size_and_offsets(name, args):
+    B, n, d, e, s, c, causal, dt = args
+    esz = 2 if dt == fg.BF16 else 4
+    offs, total = _expected_layout(B, n, d, e, s, c, causal, esz)
+    assert fg.workspace_size(*args) == total
+    got = fg.workspace_offsets(*args)
+    assert [got[k] for k in fg.WS_NAMES] == offs
+    assert all(o % 256 == 0 for o in offs)
+
+
+def test_empty_problem_needs_no_workspace_and_succeeds_without_pointers():
+    assert fg.workspace_size(0, 256, 64, 128, 128, 64, True, fg.BF16) == 0
+    assert fg.workspace_size(4, 0, 64, 128, 128, 64, True, fg.BF16) == 0
+    rc = fg.forward_raw(None, None, None, None, None, None, None, 64, 1, 0, 256, 64, 128, 128,
+                        fg.BF16, None, None, 0, None)
+    assert rc == fg.OK
+
+
+@pytest.mark.parametrize("shape,code", [
+    ((2, 100, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),   # n % chunk != 0
+    ((-1, 128, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),  # negative batch
+    ((1, 128, 64, 128, 128, 0), fg.ERR_BAD_SHAPE),    # chunk 0
+    ((1, 128, 0, 128, 128, 64), fg.ERR_BAD_SHAPE),    # d 0
+    ((1, 128, 60, 128, 128, 64), fg.ERR_UNSUPPORTED),  # d not a multiple of 8
+    ((1, 120, 64, 128, 128, 12), fg.ERR_UNSUPPORTED),  # chunk not a multiple of 8
+    ((1, 128, 64, 100, 128, 64), fg.ERR_UNSUPPORTED),  # e not a multiple of 8
+    ((1, 1 << 31, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),  # B*n beyond int32
+])
+def test_shape_validation(shape, code):
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.workspace_size(*shape, True, fg.BF16)
+    assert ei.value.code == code
+
+
+def test_unknown_dtype():
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.workspace_size(1, 128, 64, 128, 128, 64, True, 7)
+    assert ei.value.code == fg.ERR_UNSUPPORTED
+
+
+# Fake, well-separated, 256-aligned addresses: never dereferenced because every call below fails
+# one host-side rule.
+SHAPE = dict(B=1, n=128, d=64, e=128, s=128, chunk=64)
+
+
+def _call(**over):
+    B, n, d, e, s, c = (SHAPE[k] for k in ("B", "n", "d", "e", "s", "chunk"))
+    ws = fg.workspace_size(B, n, d, e, s, c, True, fg.BF16)
+    base = 1 << 40
+    ptrs = dict(X=base, W_u=base + (1 << 30), W_v=base + (2 << 30), W_z=base + (3 << 30),
+                gamma=base + (4 << 30), beta=base + (5 << 30), W_o=base + (6 << 30),
+                O=base + (7 << 30), workspace=base + (8 << 30), workspace_bytes=ws)
+    ptrs.update(over)
+    return fg.forward_raw(ptrs["X"], ptrs["W_u"], ptrs["W_v"], ptrs["W_z"], ptrs["gamma"],
+                          ptrs["beta"], ptrs["W_o"], c, 1, B, n, d, e, s, fg.BF16, ptrs["O"],
+                          ptrs["workspace"], ptrs["workspace_bytes"], None)
+
+
+@pytest.mark.parametrize("which", ["X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "O", "workspace"])
+def test_null_pointer_rejected(which):
+    assert _call(**{which: None}) == fg.ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("which,delta", [("X", 8), ("W_o", 2), ("O", 4), ("workspace", 8), ("gamma", 2)])
+def test_misaligned_pointer_rejected(which, delta):
+    base = {"X": 1 << 40, "W_o": (1 << 40) + (6 << 30), "O": (1 << 40) + (7 << 30),
+            "workspace": (1 << 40) + (8 << 30), "gamma": (1 << 40) + (4 << 30)}[which]
+    assert _call(**{which: base + delta}) == fg.ERR_MISALIGNED
+
+
+def test_small_workspace_rejected():
+    assert _call(workspace_bytes=1024) == fg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("over", [
+    dict(O=1 << 40),                                  # O is X
+    dict(O=(1 << 40) + 256),                           # O starts inside X
+    dict(workspace=(1 << 40) + (6 << 30)),             # workspace is W_o
+    dict(O=(1 << 40) + (8 << 30) + 4096),              # O inside the workspace
+    dict(workspace=(1 << 40) + (4 << 30)),             # workspace over gamma
+])
+def test_aliasing_rejected(over):
+    assert _call(**over) == fg.ERR_ALIASING
+
+
+def test_strerror_covers_every_code():
+    texts = {c: fg.strerror(c) for c in range(-7, 1)}
+    assert len(set(texts.values())) == 8
+    assert fg.strerror(-99) == "unknown error"
