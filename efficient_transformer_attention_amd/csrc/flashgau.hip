@@ -121,21 +121,29 @@ __device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, 
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
 }
 
-// A K-contiguous operand: `rows` valid rows starting at `ptr`, `ld` bytes apart, each holding
-// `kbytes` valid bytes (a multiple of 16). Loads outside either extent return zeros.
+// A K-contiguous operand tile, read through a buffer resource that covers exactly its valid rows:
+// the hardware range check turns every read past the last valid row into zeros, so tile loads
+// need no per-lane branches. `kbytes` (a multiple of 16) is the valid length of each row; chunks
+// past it are zeroed when the tile is written to LDS.
 struct Src {
-  const char* ptr;
-  int64_t ld;
-  int rows;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t ld;  // row pitch, bytes
   int kbytes;
 };
 
+// Raw buffer resource word 3 for gfx9-family (CDNA) parts: 32-bit data format, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
+
+// base: tensor base; row0: first row of the tile; rows: valid rows from row0 (may exceed the
+// tile; only `max_rows` are ever read); k_elems: valid elements per row.
 __device__ __forceinline__ Src make_src(const void* base, int64_t row0, int64_t ld_elems, int esz,
-                                        int rows, int k_elems) {
+                                        int rows, int max_rows, int k_elems) {
   Src s;
-  s.ptr = reinterpret_cast<const char*>(base) + row0 * ld_elems * esz;
-  s.ld = ld_elems * esz;
-  s.rows = rows;
+  const char* p = reinterpret_cast<const char*>(base) + row0 * ld_elems * esz;
+  const int r = rows < 0 ? 0 : (rows > max_rows ? max_rows : rows);
+  s.ld = uint32_t(ld_elems * esz);
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, int(uint32_t(r) * s.ld),
+                                             kBufferFlags);
   s.kbytes = k_elems * esz;
   return s;
 }
@@ -151,7 +159,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 // Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
-template <class E, int BM, int BN, int WM, int WN>
+// WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of 16x16 accumulator fragments.
+// DEPTH = 1: the global loads of tile t+1 are issued before tile t is multiplied. DEPTH > 1: a
+// ring of DEPTH register stages keeps tiles t+2 .. t+DEPTH in flight while tile t is multiplied
+// (for loops whose K-tiles are small and latency-bound). PRIO raises the wave priority while it
+// issues matrix instructions.
+template <class E, int BM, int BN, int WM, int WN, int DEPTH = 1, bool PRIO = false>
 struct TileGemm {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int WTM = BM / WM;
@@ -165,10 +178,16 @@ struct TileGemm {
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert((BM * kRowChunks) % kThreads == 0 && (BN * kRowChunks) % kThreads == 0,
                 "tile rows must spread evenly over the threads");
+  static_assert(DEPTH >= 1, "at least one tile in flight");
+
+  struct Slot {
+    u32x4 a[ALD];
+    u32x4 b[BLD];
+    int ka, kb, akbytes, bkbytes;
+  };
 
   f32x4 acc[TM][TN];
-  u32x4 ra[ALD];
-  u32x4 rb[BLD];
+  Slot slot[DEPTH];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -177,38 +196,43 @@ struct TileGemm {
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  template <int N, int R>
+  template <int N>
   __device__ __forceinline__ static void gload(u32x4 (&reg)[N], const Src& s, int kb0, int tid) {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int i = tid + j * kThreads;
-      const int r = i >> 3;
-      const int kb = kb0 + (i & 7) * 16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < s.rows && kb < s.kbytes)
-        v = *reinterpret_cast<const u32x4*>(s.ptr + int64_t(r) * s.ld + kb);
-      reg[j] = v;
+      const uint32_t off = uint32_t(i >> 3) * s.ld + uint32_t(kb0 + (i & 7) * 16);
+      reg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off, 0, 0));
     }
   }
 
+  // Chunks at or past `kbytes` in a partial K tile are written as zeros (kb0, kbytes are
+  // block-uniform; (tid + j * kThreads) & 7 == tid & 7).
   template <int N>
-  __device__ __forceinline__ static void lstore(u32x4* lds, const u32x4 (&reg)[N], int tid) {
+  __device__ __forceinline__ static void lstore(u32x4* lds, const u32x4 (&reg)[N], int kb0,
+                                                int kbytes, int tid) {
+    const bool keep = kb0 + kStageBytes <= kbytes || kb0 + (tid & 7) * 16 < kbytes;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int i = tid + j * kThreads;
       const int r = i >> 3;
-      lds[r * kRowChunks + ((i & 7) ^ (r & 7))] = reg[j];
+      lds[r * kRowChunks + ((i & 7) ^ (r & 7))] = keep ? reg[j] : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  __device__ __forceinline__ void load(const Src& a, int ka, const Src& b, int kb, int tid) {
-    gload<ALD, BM>(ra, a, ka, tid);
-    gload<BLD, BN>(rb, b, kb, tid);
+  template <class Tiles>
+  __device__ __forceinline__ void load(Slot& sl, Tiles& tiles, int t, int tid) {
+    Src a, b;
+    tiles(t, a, sl.ka, b, sl.kb);
+    sl.akbytes = a.kbytes;
+    sl.bkbytes = b.kbytes;
+    gload<ALD>(sl.a, a, sl.ka, tid);
+    gload<BLD>(sl.b, b, sl.kb, tid);
   }
 
-  __device__ __forceinline__ void stage_store(u32x4* stage, int tid) {
-    lstore<ALD>(stage, ra, tid);
-    lstore<BLD>(stage + BM * kRowChunks, rb, tid);
+  __device__ __forceinline__ static void stage_store(u32x4* stage, const Slot& sl, int tid) {
+    lstore<ALD>(stage, sl.a, sl.ka, sl.akbytes, tid);
+    lstore<BLD>(stage + BM * kRowChunks, sl.b, sl.kb, sl.bkbytes, tid);
   }
 
   __device__ __forceinline__ void compute(const u32x4* stage, int wm, int wn, int lane) {
@@ -216,6 +240,7 @@ struct TileGemm {
     const u32x4* Bs = stage + BM * kRowChunks;
     const int lr = lane & 15;
     const int q = lane >> 4;
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kRowChunks / 4; ++ks) {
       const int ch = (ks * 4 + q) ^ (lr & 7);  // rows below differ from lr by multiples of 16
@@ -229,6 +254,7 @@ struct TileGemm {
 #pragma unroll
         for (int j = 0; j < TN; ++j) mma(acc[i][j], a[i], b[j], E());
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
   }
 
   // Runs K-tiles 0..nt-1. tiles(t, a, ka, b, kb) names the operands and byte offsets of tile t;
@@ -237,24 +263,46 @@ struct TileGemm {
   __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, int tid,
                                       int wm, int wn, int lane) {
     if (nt <= 0) return;
-    Src a, b;
-    int ka, kb;
-    tiles(0, a, ka, b, kb);
-    load(a, ka, b, kb, tid);
-    stage_store(lds, tid);
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-      u32x4* cur = lds + (t & 1) * kStage;
-      u32x4* nxt = lds + ((t + 1) & 1) * kStage;
-      const bool more = t + 1 < nt;
-      if (more) {
-        tiles(t + 1, a, ka, b, kb);
-        load(a, ka, b, kb, tid);
-      }
-      pre(t);
-      compute(cur, wm, wn, lane);
-      if (more) stage_store(nxt, tid);
+    if constexpr (DEPTH == 1) {
+      load(slot[0], tiles, 0, tid);
+      stage_store(lds, slot[0], tid);
       __syncthreads();
+      for (int t = 0; t < nt; ++t) {
+        u32x4* cur = lds + (t & 1) * kStage;
+        u32x4* nxt = lds + ((t + 1) & 1) * kStage;
+        const bool more = t + 1 < nt;
+        if (more) load(slot[0], tiles, t + 1, tid);
+        pre(t);
+        compute(cur, wm, wn, lane);
+        if (more) stage_store(nxt, slot[0], tid);
+        __syncthreads();
+      }
+    } else {
+      // tile k always travels in register slot k % DEPTH. Tile 0 goes to LDS stage 0 before
+      // its slot is reused for tile DEPTH; tiles 1..DEPTH then wait in the ring.
+      load(slot[0], tiles, 0, tid);
+#pragma unroll
+      for (int u = 1; u < DEPTH; ++u)
+        if (u < nt) load(slot[u], tiles, u, tid);
+      stage_store(lds, slot[0], tid);
+      if (DEPTH < nt) load(slot[0], tiles, DEPTH, tid);
+      __syncthreads();
+      for (int t0 = 0; t0 < nt; t0 += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+          const int t = t0 + u;
+          if (t < nt) {
+            pre(t);
+            compute(lds + (t & 1) * kStage, wm, wn, lane);
+            if (t + 1 < nt) {
+              Slot& sl = slot[(u + 1) % DEPTH];  // holds tile t+1
+              stage_store(lds + ((t + 1) & 1) * kStage, sl, tid);
+              if (t + 1 + DEPTH < nt) load(sl, tiles, t + 1 + DEPTH, tid);
+            }
+            __syncthreads();
+          }
+        }
+      }
     }
   }
 
@@ -275,38 +323,56 @@ struct NoPre {
 };
 
 // ------------------------------------------------------------------------------ pack
+// Transposes src [R, C] into dst [C, R] in 64x64 tiles: 16-byte row reads, an LDS tile padded by
+// one element per row, 16-byte row writes. R and C are multiples of 8.
 template <class E>
 struct TransposeJob {
   const typename E::T* src;  // [R, C]
   typename E::T* dst;        // [C, R]
   int R, C;
+  int tiles_c;     // tiles along C
+  int first_tile;  // index of this job's first tile in the launch
 };
 template <class E>
 struct PackArgs {
   TransposeJob<E> job[4];
+  int njobs;
 };
 
 template <class E>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs<E> args) {
   using T = typename E::T;
-  __shared__ T tile[64][65];
-  const TransposeJob<E> jb = args.job[blockIdx.z];
-  const int r0 = blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
-  if (r0 >= jb.R || c0 >= jb.C) return;
-  const int tid = threadIdx.x;
+  constexpr int kPer16 = 16 / E::kSize;  // elements per 16-byte access
+  __shared__ T tile[64][64 + 1];
+  int jb = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int idx = tid + i * 256;
-    const int rr = idx >> 6, cc = idx & 63;
-    if (r0 + rr < jb.R && c0 + cc < jb.C) tile[rr][cc] = jb.src[int64_t(r0 + rr) * jb.C + c0 + cc];
+  for (int i = 1; i < 4; ++i)
+    if (i < args.njobs && int(blockIdx.x) >= args.job[i].first_tile) jb = i;
+  const TransposeJob<E> J = args.job[jb];
+  const int t = blockIdx.x - J.first_tile;
+  const int r0 = (t / J.tiles_c) * 64;
+  const int c0 = (t % J.tiles_c) * 64;
+  const int tid = threadIdx.x;
+  constexpr int kVecPerRow = 64 / kPer16;
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int rr = idx / kVecPerRow, cv = (idx % kVecPerRow) * kPer16;
+    if (r0 + rr < J.R && c0 + cv < J.C) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(J.src + int64_t(r0 + rr) * J.C + c0 + cv);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int k = 0; k < kPer16; ++k) tile[rr][cv + k] = e[k];
+    }
   }
   __syncthreads();
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int cc = idx / kVecPerRow, rv = (idx % kVecPerRow) * kPer16;
+    if (c0 + cc < J.C && r0 + rv < J.R) {
+      u32x4 v;
+      T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int idx = tid + i * 256;
-    const int cc = idx >> 6, rr = idx & 63;
-    if (r0 + rr < jb.R && c0 + cc < jb.C) jb.dst[int64_t(c0 + cc) * jb.R + r0 + rr] = tile[rr][cc];
+      for (int k = 0; k < kPer16; ++k) e[k] = tile[rv + k][cc];
+      *reinterpret_cast<u32x4*>(J.dst + int64_t(c0 + cc) * J.R + r0 + rv) = v;
+    }
   }
 }
 
@@ -329,7 +395,6 @@ struct ProjArgs {
 template <class E, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   using G = TileGemm<E, BM, BN, WM, WN>;
-  using T = typename E::T;
   __shared__ u32x4 lds[G::kLds];
   const int ncols = 2 * p.e + p.s;
   const int ntn = (ncols + BN - 1) / BN;
@@ -342,8 +407,8 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
 
   G g;
   g.zero();
-  const Src a = make_src(p.X, m0, p.d, E::kSize, p.M - m0, p.d);
-  const Src b = make_src(p.WcatT, n0, p.d, E::kSize, ncols - n0, p.d);
+  const Src a = make_src(p.X, m0, p.d, E::kSize, p.M - m0, BM, p.d);
+  const Src b = make_src(p.WcatT, n0, p.d, E::kSize, ncols - n0, BN, p.d);
   const int nk = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
   g.run(lds, nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
@@ -412,8 +477,8 @@ __global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
   const bool live = !(p.causal && n0 > m0 + BT - 1);
   if (live) {
     const int64_t base = int64_t(bg) * p.c;
-    const Src a = make_src(p.Qq, base + m0, p.s, E::kSize, p.c - m0, p.s);
-    const Src b = make_src(p.Kq, base + n0, p.s, E::kSize, p.c - n0, p.s);
+    const Src a = make_src(p.Qq, base + m0, p.s, E::kSize, p.c - m0, BT, p.s);
+    const Src b = make_src(p.Kq, base + n0, p.s, E::kSize, p.c - n0, BT, p.s);
     const int nk = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
     g.run(lds, nk,
           [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
@@ -446,9 +511,9 @@ struct StatesArgs {
   float inv_n;
 };
 
-template <class E, int BM, int BN, int WM, int WN>
+template <class E, int BM, int BN, int WM, int WN, int DEPTH>
 __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN>;
+  using G = TileGemm<E, BM, BN, WM, WN, DEPTH>;
   __shared__ u32x4 lds[G::kLds];
   const int nts = (p.s + BM - 1) / BM;
   const int nte = (p.e + BN - 1) / BN;
@@ -478,8 +543,8 @@ __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
   g.run(lds, p.G * nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
           const int64_t chunk = seq0 + t / nk;
-          sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, p.c);
-          sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, p.c);
+          sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, BM, p.c);
+          sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, BN, p.c);
           ka = kb = (t % nk) * kStageBytes;
         },
         [&](int t) {
@@ -523,10 +588,10 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   const int nk1 = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
   const int64_t tok0 = int64_t(bg) * p.c;
   const int64_t slot = p.causal ? bg : bg / p.G;
-  const Src a0 = make_src(p.Vt, int64_t(bg) * p.e + m0, p.c, E::kSize, p.e - m0, p.c);
-  const Src b0 = make_src(p.P, tok0 + n0, p.c, E::kSize, p.c - n0, p.c);
-  const Src a1 = make_src(p.St, slot * p.e + m0, p.s, E::kSize, p.e - m0, p.s);
-  const Src b1 = make_src(p.Ql, tok0 + n0, p.s, E::kSize, p.c - n0, p.s);
+  const Src a0 = make_src(p.Vt, int64_t(bg) * p.e + m0, p.c, E::kSize, p.e - m0, BM, p.c);
+  const Src b0 = make_src(p.P, tok0 + n0, p.c, E::kSize, p.c - n0, BN, p.c);
+  const Src a1 = make_src(p.St, slot * p.e + m0, p.s, E::kSize, p.e - m0, BM, p.s);
+  const Src b1 = make_src(p.Ql, tok0 + n0, p.s, E::kSize, p.c - n0, BN, p.s);
 
   G g;
   g.zero();
@@ -563,9 +628,9 @@ struct OutArgs {
   int M, d, e;
 };
 
-template <class E, int BM, int BN, int WM, int WN>
+template <class E, int BM, int BN, int WM, int WN, bool PRIO>
 __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN>;
+  using G = TileGemm<E, BM, BN, WM, WN, 1, PRIO>;
   __shared__ u32x4 lds[G::kLds];
   const int ntd = (p.d + BM - 1) / BM;
   const int ntt = (p.M + BN - 1) / BN;
@@ -577,8 +642,8 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
 
   G g;
   g.zero();
-  const Src a = make_src(p.WoT, m0, p.e, E::kSize, p.d - m0, p.e);
-  const Src b = make_src(p.Y, n0, p.e, E::kSize, p.M - n0, p.e);
+  const Src a = make_src(p.WoT, m0, p.e, E::kSize, p.d - m0, BM, p.e);
+  const Src b = make_src(p.Y, n0, p.e, E::kSize, p.M - n0, BN, p.e);
   const int nk = (p.e * E::kSize + kStageBytes - 1) / kStageBytes;
   g.run(lds, nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
@@ -595,21 +660,27 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
 }
 
 // ------------------------------------------------------------------------------ tile shapes
-// (BM, BN, waves along M, waves along N) per kernel and element type.
+// (BM, BN, waves along M, waves along N[, register prefetch depth]) per kernel and element type.
+// The two large GEMMs run 8 waves per block: a single wave per SIMD cannot issue matrix
+// instructions back to back, two can.
 template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
-  static constexpr int kProjBM = 256, kProjBN = 128, kProjWM = 2, kProjWN = 2;
+  static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
   static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kStatesDepth = 4;
   static constexpr int kMixBM = 128, kMixBN = 128, kMixWM = 2, kMixWN = 2;
-  static constexpr int kOutBM = 128, kOutBN = 256, kOutWM = 2, kOutWN = 2;
+  static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2;
+  static constexpr bool kOutPrio = true;
 };
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
   static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kStatesDepth = 2;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2;
+  static constexpr bool kOutPrio = false;
 };
 
 // ------------------------------------------------------------------------------ host side
@@ -679,7 +750,8 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   };
   for (int64_t g : grids)
     if (g > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
-  if (cdiv(std::max(std::max(d, e), s), 64) > 65535) return FLASHGAU_ERR_BAD_SHAPE;
+  const int64_t pack_tiles = cdiv(d, 64) * (2 * cdiv(e, 64) + cdiv(s, 64)) + cdiv(e, 64) * cdiv(d, 64);
+  if (pack_tiles > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
   return FLASHGAU_OK;
 }
 
@@ -721,13 +793,19 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   // pack: (W_u | W_v | W_z)ᵀ and W_oᵀ
   {
     PackArgs<E> a;
-    a.job[0] = {reinterpret_cast<const T*>(W_u), WcatT, d, e};
-    a.job[1] = {reinterpret_cast<const T*>(W_v), WcatT + int64_t(e) * d, d, e};
-    a.job[2] = {reinterpret_cast<const T*>(W_z), WcatT + int64_t(2 * e) * d, d, s};
-    a.job[3] = {reinterpret_cast<const T*>(W_o), WoT, e, d};
-    const int64_t mx = std::max(std::max(d, e), s);
-    dim3 grid(unsigned(cdiv(mx, 64)), unsigned(cdiv(mx, 64)), 4);
-    hipLaunchKernelGGL(pack_kernel<E>, grid, dim3(256), 0, stream, a);
+    const int R[4] = {d, d, d, e};
+    const int C[4] = {e, e, s, d};
+    const T* src[4] = {reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
+                       reinterpret_cast<const T*>(W_z), reinterpret_cast<const T*>(W_o)};
+    T* dst[4] = {WcatT, WcatT + int64_t(e) * d, WcatT + int64_t(2 * e) * d, WoT};
+    int tiles = 0;
+    for (int i = 0; i < 4; ++i) {
+      const int tr = int(cdiv(R[i], 64)), tc = int(cdiv(C[i], 64));
+      a.job[i] = {src[i], dst[i], R[i], C[i], tc, tiles};
+      tiles += tr * tc;
+    }
+    a.njobs = 4;
+    hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(tiles)), dim3(256), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
@@ -748,7 +826,8 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   {
     StatesArgs<E> a{Klt, Vt, St, int(pl.B), int(pl.G), s, e, c, causal, float(1.0 / double(pl.n))};
     const int64_t nb = pl.B * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
-    hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN>),
+    hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN,
+                                      S::kStatesDepth>),
                        dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
@@ -762,7 +841,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   {
     OutArgs<E> a{WoT, Y, reinterpret_cast<T*>(O), M, d, e};
     const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
-    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN>),
+    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutPrio>),
                        dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
