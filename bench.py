@@ -130,7 +130,20 @@ def main():
     ap.add_argument("--workload", default=None, help="name in inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit: the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.calibrate_copy_mib:
+        import torch
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.calibrate_copy_mib, "launches": 3}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

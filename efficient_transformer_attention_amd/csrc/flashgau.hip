@@ -139,12 +139,18 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ Src make_src(const void* base, int64_t row0, int64_t ld_elems, int esz,
                                         int rows, int max_rows, int k_elems) {
   Src s;
-  const char* p = reinterpret_cast<const char*>(base) + row0 * ld_elems * esz;
+  // Every argument is block-uniform; readfirstlane states that, so the descriptor lives in
+  // scalar registers (a descriptor in vector registers forces a loop over lanes per load).
+  const uint64_t addr =
+      reinterpret_cast<uint64_t>(reinterpret_cast<const char*>(base) + row0 * ld_elems * esz);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(addr));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(addr >> 32));
   const int r = rows < 0 ? 0 : (rows > max_rows ? max_rows : rows);
-  s.ld = uint32_t(ld_elems * esz);
-  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, int(uint32_t(r) * s.ld),
-                                             kBufferFlags);
-  s.kbytes = k_elems * esz;
+  s.ld = __builtin_amdgcn_readfirstlane(uint32_t(ld_elems * esz));
+  const int nbytes = __builtin_amdgcn_readfirstlane(int(uint32_t(r) * s.ld));
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                             nbytes, kBufferFlags);
+  s.kbytes = __builtin_amdgcn_readfirstlane(k_elems * esz);
   return s;
 }
 
@@ -259,10 +265,22 @@ struct TileGemm {
 
   // Runs K-tiles 0..nt-1. tiles(t, a, ka, b, kb) names the operands and byte offsets of tile t;
   // pre(t) runs right before tile t is multiplied (it may read the accumulators).
+  // Every global load is issued unconditionally (past the last tile it re-reads the last tile,
+  // which is never stored): loads under branches would make the compiler's wait counting fall
+  // back to draining every load in flight, which removes the prefetch.
   template <class Tiles, class Pre>
   __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, int tid,
                                       int wm, int wn, int lane) {
+    run(lds, nt, tiles, pre, [](int) { return false; }, tid, wm, wn, lane);
+  }
+
+  // skip(t) (wave-uniform) lets a wave leave out the products of tile t when they are known to
+  // be zero for its fragments; loads, LDS stores and barriers still run for the whole block.
+  template <class Tiles, class Pre, class Skip>
+  __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, Skip&& skip,
+                                      int tid, int wm, int wn, int lane) {
     if (nt <= 0) return;
+    const int last = nt - 1;
     if constexpr (DEPTH == 1) {
       load(slot[0], tiles, 0, tid);
       stage_store(lds, slot[0], tid);
@@ -270,22 +288,20 @@ struct TileGemm {
       for (int t = 0; t < nt; ++t) {
         u32x4* cur = lds + (t & 1) * kStage;
         u32x4* nxt = lds + ((t + 1) & 1) * kStage;
-        const bool more = t + 1 < nt;
-        if (more) load(slot[0], tiles, t + 1, tid);
+        load(slot[0], tiles, min(t + 1, last), tid);
         pre(t);
-        compute(cur, wm, wn, lane);
-        if (more) stage_store(nxt, slot[0], tid);
+        if (!skip(t)) compute(cur, wm, wn, lane);
+        if (t < last) stage_store(nxt, slot[0], tid);
         __syncthreads();
       }
     } else {
-      // tile k always travels in register slot k % DEPTH. Tile 0 goes to LDS stage 0 before
-      // its slot is reused for tile DEPTH; tiles 1..DEPTH then wait in the ring.
+      // Tile k travels in register slot k % DEPTH. Tile 0 goes to LDS stage 0 before its slot
+      // is reused for tile DEPTH; tiles 1..DEPTH then wait in the ring.
       load(slot[0], tiles, 0, tid);
 #pragma unroll
-      for (int u = 1; u < DEPTH; ++u)
-        if (u < nt) load(slot[u], tiles, u, tid);
+      for (int u = 1; u < DEPTH; ++u) load(slot[u], tiles, min(u, last), tid);
       stage_store(lds, slot[0], tid);
-      if (DEPTH < nt) load(slot[0], tiles, DEPTH, tid);
+      load(slot[0], tiles, min(DEPTH, last), tid);
       __syncthreads();
       for (int t0 = 0; t0 < nt; t0 += DEPTH) {
 #pragma unroll
@@ -293,14 +309,12 @@ struct TileGemm {
           const int t = t0 + u;
           if (t < nt) {
             pre(t);
-            compute(lds + (t & 1) * kStage, wm, wn, lane);
-            if (t + 1 < nt) {
-              Slot& sl = slot[(u + 1) % DEPTH];  // holds tile t+1
-              stage_store(lds + ((t + 1) & 1) * kStage, sl, tid);
-              if (t + 1 + DEPTH < nt) load(sl, tiles, t + 1 + DEPTH, tid);
-            }
-            __syncthreads();
+            if (!skip(t)) compute(lds + (t & 1) * kStage, wm, wn, lane);
           }
+          Slot& sl = slot[(u + 1) % DEPTH];  // holds tile t+1
+          if (t < last) stage_store(lds + ((t + 1) & 1) * kStage, sl, tid);
+          load(sl, tiles, min(t + 1 + DEPTH, last), tid);
+          __syncthreads();
         }
       }
     }
@@ -321,6 +335,23 @@ struct TileGemm {
 struct NoPre {
   __device__ __forceinline__ void operator()(int) const {}
 };
+
+// Wave w of a workgroup runs on SIMD w % 4, so with 8 waves, waves w and w + 4 share a SIMD.
+// For kernels whose work per wave grows with wn (causal key ranges), pair a short range with a
+// long one on every SIMD. Other shapes use the plain row-major mapping.
+template <int WM, int WN>
+__device__ __forceinline__ void balanced_wave(int w, int& wm, int& wn) {
+  if constexpr (WM * WN == 8 && WN == 4) {
+    wm = w >> 2;
+    wn = w < 4 ? w : 7 - w;
+  } else if constexpr (WM * WN == 8 && WN == 2) {
+    wm = w >> 1;
+    wn = (w & 1) ^ ((w >> 2) & 1);
+  } else {
+    wm = w / WN;
+    wn = w % WN;
+  }
+}
 
 // ------------------------------------------------------------------------------ pack
 // Transposes src [R, C] into dst [C, R] in 64x64 tiles: 16-byte row reads, an LDS tile padded by
@@ -579,10 +610,12 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   const int nt = rem / nte, mt = rem % nte;
   const int m0 = mt * BM, n0 = nt * BN;  // m: value column (e), n: token inside the chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  int wm, wn;
+  balanced_wave<WM, WN>(wave, wm, wn);
 
   // Causal: tokens n0..n0+BN-1 attend to keys 0..n0+BN-1 of their chunk only; P is zero above
-  // the diagonal, so stopping the key range there is exact.
+  // the diagonal, so stopping the key range there is exact. Inside the block, a wave whose
+  // tokens all precede a key tile skips that tile's products.
   const int keys = p.causal ? min(p.c, n0 + BN) : p.c;
   const int nk0 = (keys * E::kSize + kStageBytes - 1) / kStageBytes;
   const int nk1 = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
@@ -592,6 +625,9 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   const Src b0 = make_src(p.P, tok0 + n0, p.c, E::kSize, p.c - n0, BN, p.c);
   const Src a1 = make_src(p.St, slot * p.e + m0, p.s, E::kSize, p.e - m0, BM, p.s);
   const Src b1 = make_src(p.Ql, tok0 + n0, p.s, E::kSize, p.c - n0, BN, p.s);
+
+  constexpr int kKeysPerTile = kStageBytes / E::kSize;
+  const int last_token = n0 + (wn + 1) * G::WTN - 1;  // of this wave
 
   G g;
   g.zero();
@@ -607,7 +643,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
             ka = kb = (t - nk0) * kStageBytes;
           }
         },
-        NoPre(), tid, wm, wn, lane);
+        NoPre(), [&](int t) { return p.causal && t < nk0 && t * kKeysPerTile > last_token; },
+        tid, wm, wn, lane);
 
   g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
     const int j = m0 + r, i = n0 + cl;  // j: value column (4 consecutive), i: token
@@ -669,7 +706,9 @@ template <> struct Shapes<BF16> {
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
   static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesDepth = 4;
-  static constexpr int kMixBM = 128, kMixBN = 128, kMixWM = 2, kMixWN = 2;
+  // mix: tokens of a whole 256-chunk per block when c >= 256, else 128 tokens per block
+  static constexpr int kMixBM = 256, kMixBN = 256, kMixWM = 2, kMixWN = 4;
+  static constexpr int kMixSmallBN = 128, kMixSmallWM = 4, kMixSmallWN = 2;
   static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2;
   static constexpr bool kOutPrio = true;
 };
@@ -679,6 +718,7 @@ template <> struct Shapes<F32> {
   static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesDepth = 2;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2;
+  static constexpr int kMixSmallBN = 64, kMixSmallWM = 2, kMixSmallWN = 2;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2;
   static constexpr bool kOutPrio = false;
 };
@@ -833,9 +873,16 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal};
-    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
-    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN>),
-                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+    if (c >= S::kMixBN) {
+      const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
+      hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN>),
+                         dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+    } else {
+      const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixSmallBN);
+      hipLaunchKernelGGL(
+          (mix_kernel<E, S::kMixBM, S::kMixSmallBN, S::kMixSmallWM, S::kMixSmallWN>),
+          dim3(unsigned(nb)), dim3(64 * S::kMixSmallWM * S::kMixSmallWN), 0, stream, a);
+    }
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
