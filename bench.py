@@ -67,6 +67,28 @@ def alg_bytes(B, n, d, e, s, c, causal, esz):
     }
 
 
+PROFILE_BYTES = os.path.join(ROOT, "profiles", "flash_layer_c3_hbm_bytes.txt")
+LIB_SOURCE = os.path.join(ROOT, "efficient_transformer_attention_amd", "csrc", "flashgau.hip")
+
+
+def measured_traffic(kernel, workload):
+    """Per-launch HBM-side bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of `kernel` from the
+    committed rocprofv3 summary, or None when the summary is for another workload or the library
+    source has changed since the counters were taken."""
+    import hashlib
+    if workload != "c3_causal_bf16_n4096" or not os.path.exists(PROFILE_BYTES):
+        return None
+    sha = hashlib.sha256(open(LIB_SOURCE, "rb").read()).hexdigest()
+    text = open(PROFILE_BYTES).read()
+    if f"library source sha256: {sha}" not in text:
+        return None
+    for line in text.splitlines():
+        parts = line.split()
+        if parts and parts[0] == kernel and len(parts) == 6:
+            return int(parts[5])
+    return None
+
+
 BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "mix": "hbm",
          "out": "mfma"}
 
@@ -229,7 +251,8 @@ def main():
     else:
         achieved, pk, unit = nbytes_alg[dom] / t_dom / 1e9, HBM_PEAK, "GB/s"
     roofline = {"kernel": dom, "bound": BOUND[dom], "achieved": round(achieved, 2), "peak": pk,
-                "unit": unit, "frac": round(achieved / pk, 4), "traffic": None}
+                "unit": unit, "frac": round(achieved / pk, 4),
+                "traffic": measured_traffic(dom, name)}
 
     cpu = None
     max_rel_err = None
