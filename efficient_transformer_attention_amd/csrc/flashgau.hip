@@ -164,6 +164,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Logical tile id -> (row tile, column tile): groups of `gm` row tiles are walked column by
+// column, so the tiles in flight on one XCD share a few row blocks and a few column blocks.
+__device__ __forceinline__ void grouped_tile(int lid, int ntm, int ntn, int gm, int& mt, int& nt) {
+  const int per_group = gm * ntn;
+  const int grp = lid / per_group;
+  const int first = grp * gm;
+  const int rows = min(gm, ntm - first);
+  const int local = lid - grp * per_group;
+  nt = local / rows;
+  mt = first + local % rows;
+}
+
 // Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of 16x16 accumulator fragments.
 // DEPTH = 1: the global loads of tile t+1 are issued before tile t is multiplied. DEPTH > 1: a
@@ -320,6 +332,91 @@ struct TileGemm {
     }
   }
 
+  // Output staging for results whose memory layout is contiguous along the tile's rows (the
+  // four consecutive rows a lane holds): conv(row, col, acc) returns the four output values of a
+  // fragment lane (already rounded to the element type T); they are written to this wave's LDS
+  // region as [col][row] rows of WTM elements (16-byte chunks XOR-swizzled by col), read back
+  // as 16-byte chunks and handed to emit(col, row, chunk) with row a multiple of 16/sizeof(T).
+  // Consecutive lanes then cover whole rows, so global stores are full 16-byte runs. The LDS
+  // tile stages must be idle (after run() returns) and each wave only touches its own region.
+  template <class T, class Conv, class Emit>
+  __device__ __forceinline__ void stage_rows(u32x4* lds, int wave, int wm, int wn, int lane,
+                                             Conv&& conv, Emit&& emit) const {
+    constexpr int kCpr = WTM * int(sizeof(T)) / 16;  // 16-byte chunks per staged row
+    constexpr int kRegionBytes = WTM * WTN * int(sizeof(T));
+    static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "staged row must be 2^k chunks");
+    static_assert(WM * WN * kRegionBytes <= kLds * 16, "staging regions exceed the LDS tiles");
+    char* region = reinterpret_cast<char*>(lds) + wave * kRegionBytes;
+    const int lr = lane & 15;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = i * 16 + q * 4;  // wave-local
+        const int col = j * 16 + lr;
+        T v[4];
+        conv(wm * WTM + row, wn * WTN + col, acc[i][j], v);
+        const int byte = row * int(sizeof(T));
+        char* dst = region + col * (kCpr * 16) + (((byte >> 4) ^ (col & (kCpr - 1))) << 4) + (byte & 15);
+        if constexpr (sizeof(T) == 2) {
+          u32x2 w;
+          w[0] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+          w[1] = uint32_t(v[2]) | (uint32_t(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(dst) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < WTN * kCpr / 64; ++k) {
+      const int idx = lane + k * 64;
+      const int col = idx / kCpr, ch = idx % kCpr;
+      const u32x4 chunk = *reinterpret_cast<const u32x4*>(
+          region + col * (kCpr * 16) + ((ch ^ (col & (kCpr - 1))) << 4));
+      emit(wn * WTN + col, wm * WTM + ch * (16 / int(sizeof(T))), chunk);
+    }
+  }
+
+  // The same for results contiguous along the tile's columns: staged as [row][col] rows of WTN
+  // elements (element-wise LDS writes), handed out as emit(row, col, chunk) with col a multiple
+  // of 16/sizeof(T).
+  template <class T, class Conv, class Emit>
+  __device__ __forceinline__ void stage_cols(u32x4* lds, int wave, int wm, int wn, int lane,
+                                             Conv&& conv, Emit&& emit) const {
+    constexpr int kCpr = WTN * int(sizeof(T)) / 16;
+    constexpr int kRegionBytes = WTM * WTN * int(sizeof(T));
+    static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "staged row must be 2^k chunks");
+    static_assert(WM * WN * kRegionBytes <= kLds * 16, "staging regions exceed the LDS tiles");
+    char* region = reinterpret_cast<char*>(lds) + wave * kRegionBytes;
+    const int lr = lane & 15;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = i * 16 + q * 4;
+        const int col = j * 16 + lr;
+        T v[4];
+        conv(wm * WTM + row, wn * WTN + col, acc[i][j], v);
+        const int byte = col * int(sizeof(T));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rr = row + k;
+          char* dst = region + rr * (kCpr * 16) + (((byte >> 4) ^ (rr & (kCpr - 1))) << 4) + (byte & 15);
+          *reinterpret_cast<T*>(dst) = v[k];
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < WTM * kCpr / 64; ++k) {
+      const int idx = lane + k * 64;
+      const int row = idx / kCpr, ch = idx % kCpr;
+      const u32x4 chunk = *reinterpret_cast<const u32x4*>(
+          region + row * (kCpr * 16) + ((ch ^ (row & (kCpr - 1))) << 4));
+      emit(wm * WTM + row, wn * WTN + ch * (16 / int(sizeof(T))), chunk);
+    }
+  }
+
   // Calls f(row, col, acc) for each 16x16 fragment: rows row..row+3 of column col (tile-local).
   template <class F>
   __device__ __forceinline__ void epilogue(int wm, int wn, int lane, F&& f) const {
@@ -431,7 +528,8 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   const int ntn = (ncols + BN - 1) / BN;
   const int ntm = (p.M + BM - 1) / BM;
   const int lid = xcd_remap(blockIdx.x, ntm * ntn);
-  const int mt = lid / ntn, nt = lid % ntn;
+  int mt, nt;
+  grouped_tile(lid, ntm, ntn, 8, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -449,7 +547,34 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
         },
         NoPre(), tid, wm, wn, lane);
 
+  using T = typename E::T;
   const int e = p.e, s = p.s, c = p.c;
+  // A wave whose columns all fall in U or all in V stages its tile through LDS and writes full
+  // 16-byte runs (U row-major, V chunk-transposed); other waves store element-wise.
+  const int wc0 = n0 + wn * G::WTN, wc1 = wc0 + G::WTN;
+  auto silu4 = [&](int, int, const f32x4& v, T* out) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
+  };
+  if (wc1 <= e) {
+    g.template stage_cols<T>(lds, wave, wm, wn, lane, silu4,
+                             [&](int r, int cl, const u32x4& chunk) {
+                               const int row = m0 + r, col = n0 + cl;
+                               if (row < p.M)
+                                 *reinterpret_cast<u32x4*>(p.U + int64_t(row) * e + col) = chunk;
+                             });
+    return;
+  }
+  if (wc0 >= e && wc1 <= 2 * e) {
+    g.template stage_rows<T>(lds, wave, wm, wn, lane, silu4,
+                             [&](int cl, int r, const u32x4& chunk) {
+                               const int row = m0 + r, col = n0 + cl;
+                               if (row >= p.M) return;
+                               const int64_t bg = row / c, t = row % c;  // 8 rows, one chunk
+                               *reinterpret_cast<u32x4*>(p.Vt + (bg * e + (col - e)) * c + t) = chunk;
+                             });
+    return;
+  }
   g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
     const int row = m0 + r, col = n0 + cl;
     if (row >= p.M || col >= ncols) return;
@@ -646,14 +771,23 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
         NoPre(), [&](int t) { return p.causal && t < nk0 && t * kKeysPerTile > last_token; },
         tid, wm, wn, lane);
 
-  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
-    const int j = m0 + r, i = n0 + cl;  // j: value column (4 consecutive), i: token
-    if (j >= p.e || i >= p.c) return;
-    const int64_t o = (tok0 + i) * p.e + j;
-    float u[4];
-    load4(p.U + o, u);
-    store4(p.Y + o, u[0] * v[0], u[1] * v[1], u[2] * v[2], u[3] * v[3]);
-  });
+  // Y = U ⊙ (P V + Q_lin S / n): the product is formed in fp32 from the fragment's U values,
+  // rounded once, and staged through LDS so that every token row of Y is written as full
+  // 16-byte runs.
+  using T = typename E::T;
+  g.template stage_rows<T>(
+      lds, wave, wm, wn, lane,
+      [&](int r, int cl, const f32x4& v, T* out) {
+        const int j = m0 + r, i = n0 + cl;  // j: value column (4 consecutive), i: token
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        if (j < p.e && i < p.c) load4(p.U + (tok0 + i) * p.e + j, u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(u[k] * v[k]);
+      },
+      [&](int cl, int r, const u32x4& chunk) {
+        const int j = m0 + r, i = n0 + cl;
+        if (j < p.e && i < p.c) *reinterpret_cast<u32x4*>(p.Y + (tok0 + i) * p.e + j) = chunk;
+      });
 }
 
 // ------------------------------------------------------------------------------ out
@@ -689,11 +823,17 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
           ka = kb = t * kStageBytes;
         },
         NoPre(), tid, wm, wn, lane);
-  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
-    const int j = m0 + r, i = n0 + cl;  // j: feature (4 consecutive), i: token
-    if (j >= p.d || i >= p.M) return;
-    store4(p.O + int64_t(i) * p.d + j, v[0], v[1], v[2], v[3]);
-  });
+  using T = typename E::T;
+  g.template stage_rows<T>(
+      lds, wave, wm, wn, lane,
+      [&](int, int, const f32x4& v, T* out) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
+      },
+      [&](int cl, int r, const u32x4& chunk) {
+        const int j = m0 + r, i = n0 + cl;  // j: first of the chunk's features, i: token
+        if (j < p.d && i < p.M) *reinterpret_cast<u32x4*>(p.O + int64_t(i) * p.d + j) = chunk;
+      });
 }
 
 // ------------------------------------------------------------------------------ tile shapes
