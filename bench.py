@@ -47,21 +47,30 @@ def alg_flops(B, n, d, e, s, c, causal):
     states = 2 * n_state * s * e
     readout = 2 * n_state * s * e
     out = 2 * N * e * d
-    return {"pack": 0, "proj": proj, "scores": scores, "states": states, "mix": pv + readout,
-            "out": out}
+    return {"pack": 0, "proj": proj, "scores": scores, "states": states, "carry": 0,
+            "mix": pv + readout, "out": out}
 
 
-def alg_bytes(B, n, d, e, s, c, causal, esz):
-    """Bytes each kernel must move at least once between HBM and the chip."""
+def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
+    """Bytes each kernel must move at least once between HBM and the chip (ng: chunk groups of
+    the states stage)."""
     N = B * n
     G = n // c
+    gs = -(-G // ng)
     nst = (B * G if causal else B) * e * s
+    if causal:
+        carry = (2 * B * (G - gs) * e * s + B * (ng - 1) * e * s) * esz if ng > 1 else 0
+        states_out = nst + B * (ng - 1) * e * s
+    else:
+        carry = (B * ng * e * s + B * e * s) * esz if ng > 1 else 0
+        states_out = B * ng * e * s if ng > 1 else nst
     pc = (c * (c + 1) // 2) if causal else c * c  # P entries the mix reads per chunk
     return {
         "pack": 2 * ((2 * e + s) * d + e * d) * esz,
         "proj": (N * d + (2 * e + s) * d + N * (2 * e + 4 * s)) * esz,
         "scores": (2 * N * s + B * G * c * c) * esz,
-        "states": (N * (e + s) + nst) * esz,
+        "states": (N * (e + s) + states_out) * esz,
+        "carry": carry,
         "mix": (N * e * 2 + B * G * pc + N * s + nst + N * e) * esz,
         "out": (N * e + e * d + N * d) * esz,
     }
@@ -89,8 +98,8 @@ def measured_traffic(kernel, workload):
     return None
 
 
-BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "mix": "hbm",
-         "out": "mfma"}
+BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "carry": "hbm",
+         "mix": "hbm", "out": "mfma"}
 
 
 class HipEvents:
@@ -233,7 +242,7 @@ def main():
     stage_avg = {st: statistics.mean(v) for st, v in stage_ms.items()}
 
     flops = alg_flops(B, n, d, e, s, c, causal)
-    nbytes_alg = alg_bytes(B, n, d, e, s, c, causal, esz)
+    nbytes_alg = alg_bytes(B, n, d, e, s, c, causal, esz, fg.state_groups(B, n, d, e, s, c, causal, dt))
     total_flops = sum(flops.values())
     tokens = B * n
     value = tokens / (ms_step / 1e3)

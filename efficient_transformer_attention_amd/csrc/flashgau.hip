@@ -658,12 +658,19 @@ __global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
 }
 
 // ------------------------------------------------------------------------------ states
+// The n/c chunks of a sequence are split into ng groups of gs consecutive chunks; one workgroup
+// owns (sequence, chunk group, state-row tile, value-column tile) and runs its accumulator over
+// the group's chunks in order, so the accumulator is the exclusive prefix inside the group when
+// each chunk starts. The group total goes to the carry buffer; the carry stage adds the totals of
+// earlier groups.
 template <class E>
 struct StatesArgs {
   const typename E::T* Klt;  // [B*G, s, c]
   const typename E::T* Vt;   // [B*G, e, c]
   typename E::T* St;         // causal [B*G, e, s], non-causal [B, e, s]
+  typename E::T* Carry;      // [B, ng, e, s]
   int B, G, s, e, c, causal;
+  int ng, gs;
   float inv_n;
 };
 
@@ -673,42 +680,140 @@ __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
   __shared__ u32x4 lds[G::kLds];
   const int nts = (p.s + BM - 1) / BM;
   const int nte = (p.e + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, p.B * nts * nte);
-  const int b = lid / (nts * nte);
-  const int rem = lid % (nts * nte);
-  const int mt = rem / nte, nt = rem % nte;
+  const int lid = xcd_remap(blockIdx.x, p.B * p.ng * nts * nte);
+  // neighbouring workgroups share a chunk group, hence its K_lin and V rows
+  const int nt = lid % nte;
+  int rest = lid / nte;
+  const int mt = rest % nts;
+  rest /= nts;
+  const int grp = rest % p.ng;
+  const int b = rest / p.ng;
   const int m0 = mt * BM, n0 = nt * BN;  // m: state row (s), n: value column (e)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
   const int nk = (p.c * E::kSize + kStageBytes - 1) / kStageBytes;
-  const int64_t seq0 = int64_t(b) * p.G;
+  const int g0 = grp * p.gs;
+  const int nchunks = min(p.G, g0 + p.gs) - g0;
+  const int64_t chunk0 = int64_t(b) * p.G + g0;
 
-  auto write_state = [&](G& gg, int64_t slot) {
-    typename E::T* St = p.St + slot * p.e * p.s;
+  auto write_state = [&](G& gg, typename E::T* dst) __attribute__((always_inline)) {
     gg.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
       const int i = m0 + r, j = n0 + cl;
       if (i >= p.s || j >= p.e) return;
-      store4(St + int64_t(j) * p.s + i, v[0] * p.inv_n, v[1] * p.inv_n, v[2] * p.inv_n,
+      store4(dst + int64_t(j) * p.s + i, v[0] * p.inv_n, v[1] * p.inv_n, v[2] * p.inv_n,
              v[3] * p.inv_n);
     });
   };
+  const int64_t es = int64_t(p.e) * p.s;
+  const bool write_local = p.causal && (p.gs > 1 || p.ng == 1);
 
   G g;
   g.zero();
-  g.run(lds, p.G * nk,
+  g.run(lds, nchunks * nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-          const int64_t chunk = seq0 + t / nk;
+          const int64_t chunk = chunk0 + t / nk;
           sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, BM, p.c);
           sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, BN, p.c);
           ka = kb = (t % nk) * kStageBytes;
         },
         [&](int t) {
-          // exclusive prefix: chunk g reads the sum of chunks before it
-          if (p.causal && t % nk == 0) write_state(g, seq0 + t / nk);
+          // exclusive prefix inside the group: chunk g reads the group's chunks before it. With
+          // one chunk per group that prefix is zero; the carry stage then writes every state
+          // (unless there is only one group, i.e. one chunk).
+          if (write_local && t % nk == 0) write_state(g, p.St + (chunk0 + t / nk) * es);
         },
         tid, wm, wn, lane);
-  if (!p.causal) write_state(g, b);
+  if (!p.causal && p.ng == 1)
+    write_state(g, p.St + int64_t(b) * es);
+  else if (!p.causal || grp < p.ng - 1)  // the last group's total is never read when causal
+    write_state(g, p.Carry + (int64_t(b) * p.ng + grp) * es);
+}
+
+// ------------------------------------------------------------------------------ carry
+template <class E>
+struct CarryArgs {
+  typename E::T* St;           // causal [B*G, e, s], non-causal [B, e, s]
+  const typename E::T* Carry;  // [B, ng, e, s]
+  int B, G, ng, gs, causal;
+  int64_t es;                  // e * s, a multiple of 8
+};
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(v[k] << 16);
+    o[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = a[k];
+    o[4 + k] = b[k];
+  }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+  u32x4 w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = uint32_t(f32_to_bf16(v[2 * k])) | (uint32_t(f32_to_bf16(v[2 * k + 1])) << 16);
+  *reinterpret_cast<u32x4*>(p) = w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// One thread per 8 consecutive state elements of one sequence, walking the chunk groups in order.
+template <class E>
+__global__ __launch_bounds__(256) void carry_kernel(CarryArgs<E> p) {
+  const int64_t per_seq = p.es / 8;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= p.B * per_seq) return;
+  const int b = int(idx / per_seq);
+  const int64_t j = (idx % per_seq) * 8;
+  float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float v[8];
+  if (p.causal && p.gs == 1) {
+    // one chunk per group: the states stage left only the chunk totals; write the exclusive
+    // prefix of every chunk directly
+    for (int g = 0; g < p.G; ++g) {
+      store8(p.St + (int64_t(b) * p.G + g) * p.es + j, run);
+      if (g < p.G - 1) {
+        load8(p.Carry + (int64_t(b) * p.ng + g) * p.es + j, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) run[q] += v[q];
+      }
+    }
+  } else if (p.causal) {
+    for (int k = 0; k < p.ng; ++k) {
+      if (k > 0) {
+        const int g1 = min(p.G, (k + 1) * p.gs);
+        for (int g = k * p.gs; g < g1; ++g) {
+          typename E::T* ptr = p.St + (int64_t(b) * p.G + g) * p.es + j;
+          load8(ptr, v);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += run[q];
+          store8(ptr, v);
+        }
+      }
+      if (k < p.ng - 1) {
+        load8(p.Carry + (int64_t(b) * p.ng + k) * p.es + j, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) run[q] += v[q];
+      }
+    }
+  } else {
+    for (int k = 0; k < p.ng; ++k) {
+      load8(p.Carry + (int64_t(b) * p.ng + k) * p.es + j, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) run[q] += v[q];
+    }
+    store8(p.St + int64_t(b) * p.es + j, run);
+  }
 }
 
 // ------------------------------------------------------------------------------ mix
@@ -844,8 +949,8 @@ template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
   static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
-  static constexpr int kStatesDepth = 4;
+  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 4, kStatesWN = 2;
+  static constexpr int kStatesDepth = 1;
   // mix: tokens of a whole 256-chunk per block when c >= 256, else 128 tokens per block
   static constexpr int kMixBM = 256, kMixBN = 256, kMixWM = 2, kMixWN = 4;
   static constexpr int kMixSmallBN = 128, kMixSmallWM = 4, kMixSmallWN = 2;
@@ -855,17 +960,23 @@ template <> struct Shapes<BF16> {
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
-  static constexpr int kStatesDepth = 2;
+  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kStatesDepth = 1;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2;
   static constexpr int kMixSmallBN = 64, kMixSmallWM = 2, kMixSmallWN = 2;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2;
   static constexpr bool kOutPrio = false;
 };
 
+// The host plan sizes the chunk groups of the states stage with a 128 x 128 tile.
+static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 128 &&
+                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 128,
+              "states tile differs from the host plan");
+
 // ------------------------------------------------------------------------------ host side
 struct Plan {
   int64_t B, n, d, e, s, c, G, M, nbg, ncols;
+  int64_t ng, gs;  // chunk groups per sequence in the states stage, chunks per group
   int64_t esz;
   size_t off[FLASHGAU_WS_COUNT];
   size_t total;
@@ -877,6 +988,9 @@ constexpr int64_t kInt32Max = 2147483647;
 constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-bit grid
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// states tile (both element types) and the workgroup count the chunk grouping aims for
+constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
 
 int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
               flashgau_dtype dtype, Plan* p) {
@@ -894,6 +1008,14 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   p->nbg = B * p->G;
   p->ncols = 2 * e + s;
   if (d > kInt32Max || p->ncols > kInt32Max || chunk > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
+  // About two thousand states workgroups: enough chunk groups to fill the chip many times over.
+  {
+    const int64_t base = B * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN);
+    int64_t ng = base > 0 ? cdiv(kStatesTargetBlocks, base) : 1;
+    ng = std::max<int64_t>(1, std::min<int64_t>(ng, std::max<int64_t>(p->G, 1)));
+    p->gs = p->G > 0 ? cdiv(p->G, ng) : 1;
+    p->ng = p->G > 0 ? cdiv(p->G, p->gs) : 1;
+  }
   if (M == 0) {
     p->total = 0;
     return FLASHGAU_OK;
@@ -911,6 +1033,8 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   if (!mul_ok(causal ? p->nbg : B, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_ST]))
     return FLASHGAU_ERR_BAD_SHAPE;
   cnt[FLASHGAU_WS_Y] = cnt[FLASHGAU_WS_U];
+  if (!mul_ok(B * p->ng, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_CARRY]))
+    return FLASHGAU_ERR_BAD_SHAPE;
   size_t off = 0;
   for (int i = 0; i < FLASHGAU_WS_COUNT; ++i) {
     int64_t bytes;
@@ -924,7 +1048,8 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   const int64_t grids[] = {
       cdiv(M, 128) * cdiv(p->ncols, 128),
       p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64),
-      B * cdiv(s, 128) * cdiv(e, 64),
+      B * p->ng * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN),
+      cdiv(B * e * s / 8, 256),
       p->nbg * cdiv(e, 128) * cdiv(chunk, 64),
       cdiv(d, 128) * cdiv(M, 128),
   };
@@ -967,6 +1092,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   T* P = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_P]);
   T* St = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_ST]);
   T* Y = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_Y]);
+  T* Carry = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_CARRY]);
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
 
   if (!mark()) return FLASHGAU_ERR_HIP;
@@ -1004,11 +1130,19 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
-    StatesArgs<E> a{Klt, Vt, St, int(pl.B), int(pl.G), s, e, c, causal, float(1.0 / double(pl.n))};
-    const int64_t nb = pl.B * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
+    StatesArgs<E> a{Klt, Vt, St, Carry, int(pl.B), int(pl.G), s, e, c, causal,
+                    int(pl.ng), int(pl.gs), float(1.0 / double(pl.n))};
+    const int64_t nb = pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
     hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN,
                                       S::kStatesDepth>),
                        dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
+  }
+  if (!mark()) return FLASHGAU_ERR_HIP;
+  if (pl.ng > 1) {
+    CarryArgs<E> a{St, Carry, int(pl.B), int(pl.G), int(pl.ng), int(pl.gs), causal,
+                   int64_t(e) * s};
+    const int64_t nb = cdiv(pl.B * e * s / 8, 256);
+    hipLaunchKernelGGL(carry_kernel<E>, dim3(unsigned(nb)), dim3(256), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
@@ -1093,6 +1227,16 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
                             events);
   return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, O, ws, stream,
                          events);
+}
+
+int flashgau_state_groups(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                          int causal, flashgau_dtype dtype, int64_t* out_groups) {
+  if (!out_groups) return FLASHGAU_ERR_NULL_PTR;
+  Plan p;
+  const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &p);
+  if (rc != FLASHGAU_OK) return rc;
+  *out_groups = p.ng;
+  return FLASHGAU_OK;
 }
 
 int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const void* W_z,

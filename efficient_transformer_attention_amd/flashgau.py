@@ -27,13 +27,13 @@ ERR_ALIASING = -6
 ERR_HIP = -7
 
 # Order of the workspace buffers (FLASHGAU_WS_* in include/flashgau.h).
-WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y")
+WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CARRY")
 
-EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flash_gau_forward",
-           "flash_gau_forward_timed", "flashgau_strerror")
+EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_state_groups",
+           "flash_gau_forward", "flash_gau_forward_timed", "flashgau_strerror")
 
 # Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
-STAGES = ("pack", "proj", "scores", "states", "mix", "out")
+STAGES = ("pack", "proj", "scores", "states", "carry", "mix", "out")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.flashgau_workspace_size.restype = ctypes.c_int
     L.flashgau_workspace_offsets.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
     L.flashgau_workspace_offsets.restype = ctypes.c_int
+    L.flashgau_state_groups.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64)]
+    L.flashgau_state_groups.restype = ctypes.c_int
     vp = ctypes.c_void_p
     L.flash_gau_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
@@ -88,6 +90,14 @@ def workspace_offsets(B, n, d, e, s, chunk, causal, dtype) -> dict:
     if rc != OK:
         raise FlashGauError(rc, "flashgau_workspace_offsets")
     return dict(zip(WS_NAMES, list(arr)))
+
+
+def state_groups(B, n, d, e, s, chunk, causal, dtype) -> int:
+    out = ctypes.c_int64(0)
+    rc = lib().flashgau_state_groups(B, n, d, e, s, chunk, int(bool(causal)), dtype, ctypes.byref(out))
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_state_groups")
+    return out.value
 
 
 def forward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
@@ -170,6 +180,7 @@ def workspace_views(workspace, B, n, d, e, s, chunk, causal, dtype):
         "WCAT_T": (2 * e + s, d), "WO_T": (d, e), "U": (M, e), "VT": (B * G, e, chunk),
         "QQ": (M, s), "KQ": (M, s), "QL": (M, s), "KLT": (B * G, s, chunk),
         "P": (B * G, chunk, chunk), "ST": ((B * G) if causal else B, e, s), "Y": (M, e),
+        "CARRY": (B, state_groups(B, n, d, e, s, chunk, causal, dtype), e, s),
     }
     views = {}
     for name, shape in shapes.items():

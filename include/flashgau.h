@@ -66,7 +66,12 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  *   KLT     [B*G, s, c]   the head K_lin, transposed inside each chunk
  *   P       [B*G, c, c]   relu(Q_quad K_quadᵀ / c)² per chunk, zero above the diagonal if causal
  *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed
- *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin)                                               */
+ *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin)
+ *   CARRY   [B, NG, e, s] per sequence, the sum of K_linᵀ V over each group of consecutive
+ *                         chunks, / n, transposed. The states stage splits the n/c chunks of a
+ *                         sequence into NG groups of ceil((n/c) / NG) chunks (NG is chosen from the
+ *                         shape so that about two thousand workgroups run); the carry stage adds the
+ *                         totals of earlier groups to every chunk's state.                        */
 enum {
   FLASHGAU_WS_WCAT_T = 0,
   FLASHGAU_WS_WO_T,
@@ -79,6 +84,7 @@ enum {
   FLASHGAU_WS_P,
   FLASHGAU_WS_ST,
   FLASHGAU_WS_Y,
+  FLASHGAU_WS_CARRY,
   FLASHGAU_WS_COUNT
 };
 
@@ -93,6 +99,11 @@ int flashgau_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t 
 int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                                int64_t chunk, int causal, flashgau_dtype dtype,
                                size_t* out_offsets);
+
+/* Number NG of chunk groups the states stage uses for this problem (the CARRY buffer holds
+ * B * NG * e * s elements). Host-only. Returns FLASHGAU_OK or an error code. */
+int flashgau_state_groups(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                          int causal, flashgau_dtype dtype, int64_t* out_groups);
 
 /* One FLASH layer forward, O = FLASH(X) as defined at the top of this header.
  *   X        [B, n, d]   dtype, device
@@ -116,13 +127,16 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       void* hip_stream);
 
 /* Stages of flash_gau_forward, in launch order (one kernel each). */
-#define FLASHGAU_NUM_STAGES 6
+#define FLASHGAU_NUM_STAGES 7
 /* 0 pack   : transpose W_u|W_v|W_z and W_o into the workspace (WCAT_T, WO_T)
  * 1 proj   : X W_u|W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
  * 2 scores : per chunk relu(Q_quad K_quadᵀ / c)², masked when causal ("Mixed Chunk", local term)
- * 3 states : per sequence the chunk prefix (causal) or total (non-causal) of K_linᵀ V, times 1/n
- * 4 mix    : per chunk P V + Q_lin S / n, gated by U ("Mixed Chunk", both terms and the gate)
- * 5 out    : Y W_o                                                                            */
+ * 3 states : K_linᵀ V summed over the chunks of each chunk group: the exclusive prefix inside the
+ *            group for every chunk (causal) and the group total, times 1/n
+ * 4 carry  : adds the totals of earlier groups to every chunk's state (causal), or sums the group
+ *            totals into the sequence's state (non-causal); launches nothing with one group
+ * 5 mix    : per chunk P V + Q_lin S / n, gated by U ("Mixed Chunk", both terms and the gate)
+ * 6 out    : Y W_o                                                                            */
 
 /* flash_gau_forward with per-stage timing: the same validation and the same launches, plus
  * hipEventRecord(stage_events[i], hip_stream) right before stage i is launched and

@@ -38,11 +38,11 @@ def test_workspace_enum_matches_binding():
     assert tuple(names) == fg.WS_NAMES
 
 
-def _expected_layout(B, n, d, e, s, c, causal, esz):
+def _expected_layout(B, n, d, e, s, c, causal, esz, ng):
     G = n // c
     M = B * n
     counts = [(2 * e + s) * d, d * e, M * e, M * e, M * s, M * s, M * s, M * s, M * c,
-              (B * G if causal else B) * e * s, M * e]
+              (B * G if causal else B) * e * s, M * e, B * ng * e * s]
     off, offs = 0, []
     for cnt in counts:
         offs.append(off)
@@ -60,7 +60,12 @@ def _expected_layout(B, n, d, e, s, c, causal, esz):
 def test_workspace_size_and_offsets(name, args):
     B, n, d, e, s, c, causal, dt = args
     esz = 2 if dt == fg.BF16 else 4
-    offs, total = _expected_layout(B, n, d, e, s, c, causal, esz)
+    ng = fg.state_groups(*args)
+    G = n // c
+    assert 1 <= ng <= G
+    gs = -(-G // ng)
+    assert -(-G // gs) == ng  # every group non-empty
+    offs, total = _expected_layout(B, n, d, e, s, c, causal, esz, ng)
     assert fg.workspace_size(*args) == total
     got = fg.workspace_offsets(*args)
     assert [got[k] for k in fg.WS_NAMES] == offs
