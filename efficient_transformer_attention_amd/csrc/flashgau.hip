@@ -123,36 +123,57 @@ __device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, 
 
 // A K-contiguous operand tile, read through a buffer resource that covers exactly its valid rows:
 // the hardware range check turns every read past the last valid row into zeros, so tile loads
-// need no per-lane branches. `kbytes` (a multiple of 16) is the valid length of each row; chunks
-// past it are zeroed when the tile is written to LDS.
+// need no per-lane branches. `kbytes` (a multiple of 16) is the valid length of each row; reads
+// of chunks past it are sent out of range and also come back as zeros.
 struct Src {
-  __amdgpu_buffer_rsrc_t rsrc;
+  u32x4 rsrc;   // buffer descriptor words (scalar registers)
   uint32_t ld;  // row pitch, bytes
   int kbytes;
 };
 
-// Raw buffer resource word 3 for gfx9-family (CDNA) parts: 32-bit data format, no swizzle.
-constexpr int kBufferFlags = 0x00020000;
+// Raw buffer descriptor for gfx9-family (CDNA) parts: base address, stride 0, byte range, and
+// word 3 = 32-bit data format, no swizzle.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset at or past the range reads zero
 
 // base: tensor base; row0: first row of the tile; rows: valid rows from row0 (may exceed the
-// tile; only `max_rows` are ever read); k_elems: valid elements per row.
+// tile; only `max_rows` are ever read); k_elems: valid elements per row. Every argument is
+// block-uniform; readfirstlane states that, so the descriptor lives in scalar registers.
 __device__ __forceinline__ Src make_src(const void* base, int64_t row0, int64_t ld_elems, int esz,
                                         int rows, int max_rows, int k_elems) {
   Src s;
-  // Every argument is block-uniform; readfirstlane states that, so the descriptor lives in
-  // scalar registers (a descriptor in vector registers forces a loop over lanes per load).
   const uint64_t addr =
       reinterpret_cast<uint64_t>(reinterpret_cast<const char*>(base) + row0 * ld_elems * esz);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(addr));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(addr >> 32));
   const int r = rows < 0 ? 0 : (rows > max_rows ? max_rows : rows);
   s.ld = __builtin_amdgcn_readfirstlane(uint32_t(ld_elems * esz));
-  const int nbytes = __builtin_amdgcn_readfirstlane(int(uint32_t(r) * s.ld));
-  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
-                                             nbytes, kBufferFlags);
+  s.rsrc[0] = __builtin_amdgcn_readfirstlane(uint32_t(addr));
+  s.rsrc[1] = __builtin_amdgcn_readfirstlane(uint32_t(addr >> 32) & 0xFFFFu);
+  s.rsrc[2] = __builtin_amdgcn_readfirstlane(uint32_t(r) * s.ld);
+  s.rsrc[3] = kBufferWord3;
   s.kbytes = __builtin_amdgcn_readfirstlane(k_elems * esz);
   return s;
 }
+
+// One wave copies 64 x 16 bytes from global memory straight into LDS (buffer_load_dwordx4 with
+// the LDS destination): lane l's 16 bytes land at byte lds_addr + 16 l, out-of-range lanes write
+// zeros. The load is counted in vmcnt; the caller waits for it explicitly (wait_vm) before a
+// barrier makes the data visible to the other waves. M0 carries the wave-uniform LDS address.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_addr)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Index of this wave inside its workgroup, as a scalar (every lane of a wave holds the same).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 
 // Hardware places consecutive workgroup ids on consecutive XCDs (round robin). Give each XCD a
 // contiguous range of logical tiles, so tiles that share operand rows also share an L2.
@@ -178,34 +199,28 @@ __device__ __forceinline__ void grouped_tile(int lid, int ntm, int ntn, int gm, 
 
 // Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of 16x16 accumulator fragments.
-// DEPTH = 1: the global loads of tile t+1 are issued before tile t is multiplied. DEPTH > 1: a
-// ring of DEPTH register stages keeps tiles t+2 .. t+DEPTH in flight while tile t is multiplied
-// (for loops whose K-tiles are small and latency-bound). PRIO raises the wave priority while it
-// issues matrix instructions.
-template <class E, int BM, int BN, int WM, int WN, int DEPTH = 1, bool PRIO = false>
+// Operand tiles travel from global memory straight into a ring of NS LDS stages (no staging
+// registers): with NS = 3 the loads of tile t+2 fly while tile t is multiplied, one barrier per
+// tile; with NS = 2 (tiles too large for three stages) the loads of tile t+2 are issued after
+// tile t has been consumed, two barriers per tile. PRIO raises the wave priority while it issues
+// matrix instructions; iglp_opt(1) asks the scheduler to interleave the LDS reads with them.
+template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false>
 struct TileGemm {
   static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaves = WM * WN;
   static constexpr int WTM = BM / WM;
   static constexpr int WTN = BN / WN;
   static constexpr int TM = WTM / 16;
   static constexpr int TN = WTN / 16;
-  static constexpr int ALD = BM * kRowChunks / kThreads;
-  static constexpr int BLD = BN * kRowChunks / kThreads;
   static constexpr int kStage = (BM + BN) * kRowChunks;  // u32x4 elements per stage
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kLds = NS * kStage;
+  static constexpr int IPW = (BM + BN) / 8 / kWaves;     // 8-row copies per wave and stage
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert((BM * kRowChunks) % kThreads == 0 && (BN * kRowChunks) % kThreads == 0,
-                "tile rows must spread evenly over the threads");
-  static_assert(DEPTH >= 1, "at least one tile in flight");
-
-  struct Slot {
-    u32x4 a[ALD];
-    u32x4 b[BLD];
-    int ka, kb, akbytes, bkbytes;
-  };
+  static_assert((BM + BN) % (8 * kWaves) == 0, "tile rows must spread evenly over the waves");
+  static_assert(NS == 2 || NS == 3, "two or three LDS stages");
+  static_assert(BM % 8 == 0, "A rows end on an 8-row boundary");
 
   f32x4 acc[TM][TN];
-  Slot slot[DEPTH];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -214,43 +229,32 @@ struct TileGemm {
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  template <int N>
-  __device__ __forceinline__ static void gload(u32x4 (&reg)[N], const Src& s, int kb0, int tid) {
+  // Copies K-tile (a at byte ka, b at byte kb) into LDS stage `stage`. Wave w copies rows
+  // [8 (w IPW + j), +8) of the stage (A rows first, then B rows); lane l fetches row + l/8, logical
+  // chunk (l % 8) ^ (l / 8), which lands at physical chunk l % 8: the XOR-swizzled layout.
+  __device__ __forceinline__ static void issue(u32x4* lds, int stage, const Src& a, int ka,
+                                               const Src& b, int kb, int wave, int lane) {
+    const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds)) + uint32_t(stage * kStage) * 16;
+    const int lchunk = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kThreads;
-      const uint32_t off = uint32_t(i >> 3) * s.ld + uint32_t(kb0 + (i & 7) * 16);
-      reg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off, 0, 0));
-    }
-  }
-
-  // Chunks at or past `kbytes` in a partial K tile are written as zeros (kb0, kbytes are
-  // block-uniform; (tid + j * kThreads) & 7 == tid & 7).
-  template <int N>
-  __device__ __forceinline__ static void lstore(u32x4* lds, const u32x4 (&reg)[N], int kb0,
-                                                int kbytes, int tid) {
-    const bool keep = kb0 + kStageBytes <= kbytes || kb0 + (tid & 7) * 16 < kbytes;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kThreads;
-      const int r = i >> 3;
-      lds[r * kRowChunks + ((i & 7) ^ (r & 7))] = keep ? reg[j] : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < IPW; ++j) {
+      const int rg = wave * IPW + j;  // wave-uniform
+      const bool is_a = rg * 8 < BM;
+      const Src& src = is_a ? a : b;
+      const int row = (is_a ? rg * 8 : rg * 8 - BM) + (lane >> 3);
+      const int koff = (is_a ? ka : kb) + lchunk * 16;
+      const uint32_t voff = koff < src.kbytes ? uint32_t(row) * src.ld + uint32_t(koff) : kOutOfRange;
+      lds_dma16(src.rsrc, voff, base + uint32_t(rg) * 1024u);
     }
   }
 
   template <class Tiles>
-  __device__ __forceinline__ void load(Slot& sl, Tiles& tiles, int t, int tid) {
+  __device__ __forceinline__ static void issue_tile(u32x4* lds, Tiles& tiles, int t, int wave,
+                                                    int lane) {
     Src a, b;
-    tiles(t, a, sl.ka, b, sl.kb);
-    sl.akbytes = a.kbytes;
-    sl.bkbytes = b.kbytes;
-    gload<ALD>(sl.a, a, sl.ka, tid);
-    gload<BLD>(sl.b, b, sl.kb, tid);
-  }
-
-  __device__ __forceinline__ static void stage_store(u32x4* stage, const Slot& sl, int tid) {
-    lstore<ALD>(stage, sl.a, sl.ka, sl.akbytes, tid);
-    lstore<BLD>(stage + BM * kRowChunks, sl.b, sl.kb, sl.bkbytes, tid);
+    int ka, kb;
+    tiles(t, a, ka, b, kb);
+    issue(lds, t % NS, a, ka, b, kb, wave, lane);
   }
 
   __device__ __forceinline__ void compute(const u32x4* stage, int wm, int wn, int lane) {
@@ -259,6 +263,7 @@ struct TileGemm {
     const int lr = lane & 15;
     const int q = lane >> 4;
     if (PRIO) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int ks = 0; ks < kRowChunks / 4; ++ks) {
       const int ch = (ks * 4 + q) ^ (lr & 7);  // rows below differ from lr by multiples of 16
@@ -276,60 +281,41 @@ struct TileGemm {
   }
 
   // Runs K-tiles 0..nt-1. tiles(t, a, ka, b, kb) names the operands and byte offsets of tile t;
-  // pre(t) runs right before tile t is multiplied (it may read the accumulators).
-  // Every global load is issued unconditionally (past the last tile it re-reads the last tile,
-  // which is never stored): loads under branches would make the compiler's wait counting fall
-  // back to draining every load in flight, which removes the prefetch.
+  // pre(t) runs right before tile t is multiplied (it may read the accumulators). Returns with
+  // every copy complete and every wave past a final barrier, so LDS may be reused.
   template <class Tiles, class Pre>
-  __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, int tid,
+  __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, int wave,
                                       int wm, int wn, int lane) {
-    run(lds, nt, tiles, pre, [](int) { return false; }, tid, wm, wn, lane);
+    run(lds, nt, tiles, pre, [](int) { return false; }, wave, wm, wn, lane);
   }
 
   // skip(t) (wave-uniform) lets a wave leave out the products of tile t when they are known to
-  // be zero for its fragments; loads, LDS stores and barriers still run for the whole block.
+  // be zero for its fragments; copies and barriers still run for the whole block.
   template <class Tiles, class Pre, class Skip>
   __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, Skip&& skip,
-                                      int tid, int wm, int wn, int lane) {
+                                      int wave, int wm, int wn, int lane) {
     if (nt <= 0) return;
-    const int last = nt - 1;
-    if constexpr (DEPTH == 1) {
-      load(slot[0], tiles, 0, tid);
-      stage_store(lds, slot[0], tid);
-      __syncthreads();
-      for (int t = 0; t < nt; ++t) {
-        u32x4* cur = lds + (t & 1) * kStage;
-        u32x4* nxt = lds + ((t + 1) & 1) * kStage;
-        load(slot[0], tiles, min(t + 1, last), tid);
-        pre(t);
-        if (!skip(t)) compute(cur, wm, wn, lane);
-        if (t < last) stage_store(nxt, slot[0], tid);
-        __syncthreads();
+    issue_tile(lds, tiles, 0, wave, lane);
+    if (nt > 1) issue_tile(lds, tiles, 1, wave, lane);
+    for (int t = 0; t < nt; ++t) {
+      // this wave's copies of tile t are done when at most those of tile t+1 are in flight
+      if (t + 1 < nt)
+        wait_vm<IPW>();
+      else
+        wait_vm<0>();
+      __syncthreads();  // tile t is in LDS for every wave
+      if constexpr (NS == 3) {
+        // stage (t+2)%3 held tile t-1, which every wave finished before the barrier above
+        if (t + 2 < nt) issue_tile(lds, tiles, t + 2, wave, lane);
       }
-    } else {
-      // Tile k travels in register slot k % DEPTH. Tile 0 goes to LDS stage 0 before its slot
-      // is reused for tile DEPTH; tiles 1..DEPTH then wait in the ring.
-      load(slot[0], tiles, 0, tid);
-#pragma unroll
-      for (int u = 1; u < DEPTH; ++u) load(slot[u], tiles, min(u, last), tid);
-      stage_store(lds, slot[0], tid);
-      load(slot[0], tiles, min(DEPTH, last), tid);
-      __syncthreads();
-      for (int t0 = 0; t0 < nt; t0 += DEPTH) {
-#pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
-          const int t = t0 + u;
-          if (t < nt) {
-            pre(t);
-            if (!skip(t)) compute(lds + (t & 1) * kStage, wm, wn, lane);
-          }
-          Slot& sl = slot[(u + 1) % DEPTH];  // holds tile t+1
-          if (t < last) stage_store(lds + ((t + 1) & 1) * kStage, sl, tid);
-          load(sl, tiles, min(t + 1 + DEPTH, last), tid);
-          __syncthreads();
-        }
+      pre(t);
+      if (!skip(t)) compute(lds + (t % NS) * kStage, wm, wn, lane);
+      if constexpr (NS == 2) {
+        __syncthreads();  // every wave is done with stage t%2
+        if (t + 2 < nt) issue_tile(lds, tiles, t + 2, wave, lane);
       }
     }
+    if constexpr (NS == 3) __syncthreads();
   }
 
   // Output staging for results whose memory layout is contiguous along the tile's rows (the
@@ -520,9 +506,9 @@ struct ProjArgs {
   int M, d, e, s, c;
 };
 
-template <class E, int BM, int BN, int WM, int WN>
+template <class E, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
   const int ncols = 2 * p.e + p.s;
   const int ntn = (ncols + BN - 1) / BN;
@@ -531,7 +517,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   int mt, nt;
   grouped_tile(lid, ntm, ntn, 8, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   G g;
@@ -545,7 +531,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
           sb = b;
           ka = kb = t * kStageBytes;
         },
-        NoPre(), tid, wm, wn, lane);
+        NoPre(), wave, wm, wn, lane);
 
   using T = typename E::T;
   const int e = p.e, s = p.s, c = p.c;
@@ -624,7 +610,7 @@ __global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
   const int rem = lid % (ntc * ntc);
   const int mt = rem / ntc, nt = rem % ntc;
   const int m0 = mt * BT, n0 = nt * BT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   G g;
@@ -642,7 +628,7 @@ __global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
             sb = b;
             ka = kb = t * kStageBytes;
           },
-          NoPre(), tid, wm, wn, lane);
+          NoPre(), wave, wm, wn, lane);
   }
   typename E::T* P = p.P + int64_t(bg) * p.c * p.c;
   g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
@@ -674,9 +660,9 @@ struct StatesArgs {
   float inv_n;
 };
 
-template <class E, int BM, int BN, int WM, int WN, int DEPTH>
+template <class E, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN, DEPTH>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
   const int nts = (p.s + BM - 1) / BM;
   const int nte = (p.e + BN - 1) / BN;
@@ -689,7 +675,7 @@ __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
   const int grp = rest % p.ng;
   const int b = rest / p.ng;
   const int m0 = mt * BM, n0 = nt * BN;  // m: state row (s), n: value column (e)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   const int nk = (p.c * E::kSize + kStageBytes - 1) / kStageBytes;
@@ -723,7 +709,7 @@ __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
           // (unless there is only one group, i.e. one chunk).
           if (write_local && t % nk == 0) write_state(g, p.St + (chunk0 + t / nk) * es);
         },
-        tid, wm, wn, lane);
+        wave, wm, wn, lane);
   if (!p.causal && p.ng == 1)
     write_state(g, p.St + int64_t(b) * es);
   else if (!p.causal || grp < p.ng - 1)  // the last group's total is never read when causal
@@ -828,9 +814,9 @@ struct MixArgs {
   int nbg, G, c, e, s, causal;
 };
 
-template <class E, int BM, int BN, int WM, int WN>
+template <class E, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
   const int nte = (p.e + BM - 1) / BM;
   const int ntt = (p.c + BN - 1) / BN;
@@ -839,7 +825,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   const int rem = lid % (nte * ntt);
   const int nt = rem / nte, mt = rem % nte;
   const int m0 = mt * BM, n0 = nt * BN;  // m: value column (e), n: token inside the chunk
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   int wm, wn;
   balanced_wave<WM, WN>(wave, wm, wn);
 
@@ -874,7 +860,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
           }
         },
         NoPre(), [&](int t) { return p.causal && t < nk0 && t * kKeysPerTile > last_token; },
-        tid, wm, wn, lane);
+        wave, wm, wn, lane);
 
   // Y = U ⊙ (P V + Q_lin S / n): the product is formed in fp32 from the fragment's U values,
   // rounded once, and staged through LDS so that every token row of Y is written as full
@@ -904,16 +890,16 @@ struct OutArgs {
   int M, d, e;
 };
 
-template <class E, int BM, int BN, int WM, int WN, bool PRIO>
+template <class E, int BM, int BN, int WM, int WN, int NS, bool PRIO>
 __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN, 1, PRIO>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS, PRIO>;
   __shared__ u32x4 lds[G::kLds];
   const int ntd = (p.d + BM - 1) / BM;
   const int ntt = (p.M + BN - 1) / BN;
   const int lid = xcd_remap(blockIdx.x, ntd * ntt);
   const int nt = lid / ntd, mt = lid % ntd;
   const int m0 = mt * BM, n0 = nt * BN;  // m: output feature (d), n: token
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   G g;
@@ -927,7 +913,7 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
           sb = b;
           ka = kb = t * kStageBytes;
         },
-        NoPre(), tid, wm, wn, lane);
+        NoPre(), wave, wm, wn, lane);
   using T = typename E::T;
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
@@ -947,24 +933,24 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
 // instructions back to back, two can.
 template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
-  static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4;
+  static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4, kProjNS = 2;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
   static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 4, kStatesWN = 2;
-  static constexpr int kStatesDepth = 1;
+  static constexpr int kStatesNS = 3;
   // mix: tokens of a whole 256-chunk per block when c >= 256, else 128 tokens per block
-  static constexpr int kMixBM = 256, kMixBN = 256, kMixWM = 2, kMixWN = 4;
-  static constexpr int kMixSmallBN = 128, kMixSmallWM = 4, kMixSmallWN = 2;
-  static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2;
+  static constexpr int kMixBM = 256, kMixBN = 256, kMixWM = 2, kMixWN = 4, kMixNS = 2;
+  static constexpr int kMixSmallBN = 128, kMixSmallWM = 4, kMixSmallWN = 2, kMixSmallNS = 3;
+  static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = true;
 };
 template <> struct Shapes<F32> {
-  static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2;
+  static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
   static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
-  static constexpr int kStatesDepth = 1;
-  static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2;
-  static constexpr int kMixSmallBN = 64, kMixSmallWM = 2, kMixSmallWN = 2;
-  static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2;
+  static constexpr int kStatesNS = 3;
+  static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
+  static constexpr int kMixSmallBN = 64, kMixSmallWM = 2, kMixSmallWN = 2, kMixSmallNS = 3;
+  static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
 };
 
@@ -1118,7 +1104,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT, U, Vt, Qq, Kq, Ql, Klt, gamma, beta,
                   M, d, e, s, c};
     const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
-    hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN>),
+    hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
@@ -1134,7 +1120,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
                     int(pl.ng), int(pl.gs), float(1.0 / double(pl.n))};
     const int64_t nb = pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
     hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN,
-                                      S::kStatesDepth>),
+                                      S::kStatesNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
@@ -1149,12 +1135,12 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal};
     if (c >= S::kMixBN) {
       const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
-      hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN>),
+      hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
                          dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
     } else {
       const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixSmallBN);
       hipLaunchKernelGGL(
-          (mix_kernel<E, S::kMixBM, S::kMixSmallBN, S::kMixSmallWM, S::kMixSmallWN>),
+          (mix_kernel<E, S::kMixBM, S::kMixSmallBN, S::kMixSmallWM, S::kMixSmallWN, S::kMixSmallNS>),
           dim3(unsigned(nb)), dim3(64 * S::kMixSmallWM * S::kMixSmallWN), 0, stream, a);
     }
   }
@@ -1162,7 +1148,8 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   {
     OutArgs<E> a{WoT, Y, reinterpret_cast<T*>(O), M, d, e};
     const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
-    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutPrio>),
+    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
+                                    S::kOutPrio>),
                        dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
