@@ -935,28 +935,26 @@ template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
   static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4, kProjNS = 2;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 4, kStatesWN = 2;
-  static constexpr int kStatesNS = 3;
-  // mix: tokens of a whole 256-chunk per block when c >= 256, else 128 tokens per block
-  static constexpr int kMixBM = 256, kMixBN = 256, kMixWM = 2, kMixWN = 4, kMixNS = 2;
-  static constexpr int kMixSmallBN = 128, kMixSmallWM = 4, kMixSmallWN = 2, kMixSmallNS = 3;
+  static constexpr int kStatesBM = 128, kStatesBN = 256, kStatesWM = 2, kStatesWN = 4;
+  static constexpr int kStatesNS = 2;
+  // mix: 256 value columns x 128 tokens per block
+  static constexpr int kMixBM = 256, kMixBN = 128, kMixWM = 4, kMixWN = 2, kMixNS = 2;
   static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = true;
 };
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
-  static constexpr int kStatesNS = 3;
+  static constexpr int kStatesBM = 128, kStatesBN = 256, kStatesWM = 2, kStatesWN = 4;
+  static constexpr int kStatesNS = 2;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
-  static constexpr int kMixSmallBN = 64, kMixSmallWM = 2, kMixSmallWN = 2, kMixSmallNS = 3;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
 };
 
-// The host plan sizes the chunk groups of the states stage with a 128 x 128 tile.
-static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 128 &&
-                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 128,
+// The host plan sizes the chunk groups of the states stage with a 128 x 256 tile.
+static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 256 &&
+                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 256,
               "states tile differs from the host plan");
 
 // ------------------------------------------------------------------------------ host side
@@ -976,7 +974,7 @@ constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-b
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // states tile (both element types) and the workgroup count the chunk grouping aims for
-constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
+constexpr int64_t kStatesTileM = 128, kStatesTileN = 256, kStatesTargetBlocks = 1024;
 
 int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
               flashgau_dtype dtype, Plan* p) {
@@ -994,7 +992,7 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   p->nbg = B * p->G;
   p->ncols = 2 * e + s;
   if (d > kInt32Max || p->ncols > kInt32Max || chunk > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
-  // About two thousand states workgroups: enough chunk groups to fill the chip many times over.
+  // About a thousand states workgroups: enough chunk groups to fill the chip four times over.
   {
     const int64_t base = B * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN);
     int64_t ng = base > 0 ? cdiv(kStatesTargetBlocks, base) : 1;
@@ -1133,16 +1131,9 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal};
-    if (c >= S::kMixBN) {
-      const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
-      hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
-                         dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
-    } else {
-      const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixSmallBN);
-      hipLaunchKernelGGL(
-          (mix_kernel<E, S::kMixBM, S::kMixSmallBN, S::kMixSmallWM, S::kMixSmallWN, S::kMixSmallNS>),
-          dim3(unsigned(nb)), dim3(64 * S::kMixSmallWM * S::kMixSmallWN), 0, stream, a);
-    }
+    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
+    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
+                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
