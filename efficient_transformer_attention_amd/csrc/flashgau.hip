@@ -172,6 +172,31 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Four consecutive elements fetched through a buffer resource (reads past its range give 0).
+template <class E> struct UVec;
+template <> struct UVec<BF16> {
+  using type = u32x2;
+  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
+  __device__ __forceinline__ static void unpack(const type& w, float* o) {
+    o[0] = __uint_as_float(w[0] << 16);
+    o[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+    o[2] = __uint_as_float(w[1] << 16);
+    o[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+  }
+};
+template <> struct UVec<F32> {
+  using type = u32x4;
+  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+  __device__ __forceinline__ static void unpack(const type& w, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(w[k]);
+  }
+};
+
 // Index of this wave inside its workgroup, as a scalar (every lane of a wave holds the same).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 
@@ -319,8 +344,9 @@ struct TileGemm {
   }
 
   // Output staging for results whose memory layout is contiguous along the tile's rows (the
-  // four consecutive rows a lane holds): conv(row, col, acc) returns the four output values of a
-  // fragment lane (already rounded to the element type T); they are written to this wave's LDS
+  // four consecutive rows a lane holds): conv(i, j, row, col, acc, out) returns in out the four
+  // output values of the lane's part of fragment (i, j), whose first row is row and column col,
+  // (already rounded to the element type T); they are written to this wave's LDS
   // region as [col][row] rows of WTM elements (16-byte chunks XOR-swizzled by col), read back
   // as 16-byte chunks and handed to emit(col, row, chunk) with row a multiple of 16/sizeof(T).
   // Consecutive lanes then cover whole rows, so global stores are full 16-byte runs. The LDS
@@ -342,7 +368,7 @@ struct TileGemm {
         const int row = i * 16 + q * 4;  // wave-local
         const int col = j * 16 + lr;
         T v[4];
-        conv(wm * WTM + row, wn * WTN + col, acc[i][j], v);
+        conv(i, j, wm * WTM + row, wn * WTN + col, acc[i][j], v);
         const int byte = row * int(sizeof(T));
         char* dst = region + col * (kCpr * 16) + (((byte >> 4) ^ (col & (kCpr - 1))) << 4) + (byte & 15);
         if constexpr (sizeof(T) == 2) {
@@ -384,7 +410,7 @@ struct TileGemm {
         const int row = i * 16 + q * 4;
         const int col = j * 16 + lr;
         T v[4];
-        conv(wm * WTM + row, wn * WTN + col, acc[i][j], v);
+        conv(i, j, wm * WTM + row, wn * WTN + col, acc[i][j], v);
         const int byte = col * int(sizeof(T));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -538,7 +564,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   // A wave whose columns all fall in U or all in V stages its tile through LDS and writes full
   // 16-byte runs (U row-major, V chunk-transposed); other waves store element-wise.
   const int wc0 = n0 + wn * G::WTN, wc1 = wc0 + G::WTN;
-  auto silu4 = [&](int, int, const f32x4& v, T* out) {
+  auto silu4 = [&](int, int, int, int, const f32x4& v, T* out) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
   };
@@ -845,6 +871,29 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   constexpr int kKeysPerTile = kStageBytes / E::kSize;
   const int last_token = n0 + (wn + 1) * G::WTN - 1;  // of this wave
 
+  // The gate operand U is fetched before the main loop, straight into the fragment layout of
+  // the accumulators (four consecutive value columns of one token per lane and fragment), so
+  // its latency hides behind the products. The buffer covers this block's valid tokens; tokens
+  // past the chunk read zeros, value columns past e read bytes of the next token row and are
+  // never stored.
+  using T = typename E::T;
+  using UFrag = typename UVec<E>::type;
+  const int valid_tok = min(BN, p.c - n0);
+  const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(p.U + (tok0 + n0) * p.e), 0, valid_tok * p.e * E::kSize, kBufferWord3);
+  UFrag uf[G::TM][G::TN];
+  {
+    const int lr = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        const int col = m0 + wm * G::WTM + i * 16 + q * 4;  // value column
+        const int tok = wn * G::WTN + j * 16 + lr;          // token inside the block
+        uf[i][j] = UVec<E>::load(urs, (tok * p.e + col) * E::kSize);
+      }
+  }
+
   G g;
   g.zero();
   g.run(lds, nk0 + nk1,
@@ -865,13 +914,11 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   // Y = U ⊙ (P V + Q_lin S / n): the product is formed in fp32 from the fragment's U values,
   // rounded once, and staged through LDS so that every token row of Y is written as full
   // 16-byte runs.
-  using T = typename E::T;
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
-      [&](int r, int cl, const f32x4& v, T* out) {
-        const int j = m0 + r, i = n0 + cl;  // j: value column (4 consecutive), i: token
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
-        if (j < p.e && i < p.c) load4(p.U + (tok0 + i) * p.e + j, u);
+      [&](int fi, int fj, int, int, const f32x4& v, T* out) {
+        float u[4];
+        UVec<E>::unpack(uf[fi][fj], u);
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(u[k] * v[k]);
       },
@@ -917,7 +964,7 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
   using T = typename E::T;
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
-      [&](int, int, const f32x4& v, T* out) {
+      [&](int, int, int, int, const f32x4& v, T* out) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
       },
@@ -933,28 +980,29 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
 // instructions back to back, two can.
 template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
-  static constexpr int kProjBM = 256, kProjBN = 256, kProjWM = 2, kProjWN = 4, kProjNS = 2;
+  static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 4, kProjNS = 2;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 256, kStatesWM = 2, kStatesWN = 4;
+  // states and mix: 64 KB of LDS, so two blocks share a CU and one's epilogue overlaps the
+  // other's loads
+  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 4;
   static constexpr int kStatesNS = 2;
-  // mix: 256 value columns x 128 tokens per block
-  static constexpr int kMixBM = 256, kMixBN = 128, kMixWM = 4, kMixWN = 2, kMixNS = 2;
+  static constexpr int kMixBM = 128, kMixBN = 128, kMixWM = 2, kMixWN = 4, kMixNS = 2;
   static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = true;
 };
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
-  static constexpr int kStatesBM = 128, kStatesBN = 256, kStatesWM = 2, kStatesWN = 4;
-  static constexpr int kStatesNS = 2;
+  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kStatesNS = 3;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
 };
 
-// The host plan sizes the chunk groups of the states stage with a 128 x 256 tile.
-static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 256 &&
-                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 256,
+// The host plan sizes the chunk groups of the states stage with a 128 x 128 tile.
+static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 128 &&
+                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 128,
               "states tile differs from the host plan");
 
 // ------------------------------------------------------------------------------ host side
@@ -974,7 +1022,7 @@ constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-b
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // states tile (both element types) and the workgroup count the chunk grouping aims for
-constexpr int64_t kStatesTileM = 128, kStatesTileN = 256, kStatesTargetBlocks = 1024;
+constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
 
 int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
               flashgau_dtype dtype, Plan* p) {
@@ -992,7 +1040,7 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   p->nbg = B * p->G;
   p->ncols = 2 * e + s;
   if (d > kInt32Max || p->ncols > kInt32Max || chunk > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
-  // About a thousand states workgroups: enough chunk groups to fill the chip four times over.
+  // About two thousand states workgroups: enough chunk groups to fill the chip many times over.
   {
     const int64_t base = B * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN);
     int64_t ng = base > 0 ? cdiv(kStatesTargetBlocks, base) : 1;

@@ -70,7 +70,7 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  *   CARRY   [B, NG, e, s] per sequence, the sum of K_linᵀ V over each group of consecutive
  *                         chunks, / n, transposed. The states stage splits the n/c chunks of a
  *                         sequence into NG groups of ceil((n/c) / NG) chunks (NG is chosen from the
- *                         shape so that about a thousand workgroups run); the carry stage adds the
+ *                         shape so that about two thousand workgroups run); the carry stage adds the
  *                         totals of earlier groups to every chunk's state.                        */
 enum {
   FLASHGAU_WS_WCAT_T = 0,
