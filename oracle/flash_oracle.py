@@ -41,9 +41,19 @@ Readings taken where the pages are silent, garbled or in conflict
 * Head order in gamma/beta rows: Q_quad, K_quad, Q_lin, K_lin.
 * The layer has no bias, norm, residual, dropout or position encoding.
 
+Decoding, one token at a time
+-----------------------------
+``decode_step`` is the causal layer in the RNN form that the csdn page (section 1.4) recommends for
+generation: a running linear-attention state, here advanced a whole chunk at a time (the causal
+"Mixed Chunk" display reads the state of the earlier chunks only), plus the keys and values of the
+current chunk for the local term. Reading: every sequence of the batch is at the same position t;
+the linear state is folded after the last token of each chunk; n in the /n of the read-out is the
+length the forward normalises by, passed in.
+
 Parity status: every function below is pinned by tests that do not re-type its formula
 (brute-force n×n matrices, the RNN recurrence, the chunk = n and A = I reductions, causality,
-permutation equivariance, closed-form values and hand-worked fixtures).
+permutation equivariance, closed-form values and hand-worked fixtures; the decode step against
+the rows of the causal forward and of the brute-force layer).
 """
 
 from __future__ import annotations
@@ -66,6 +76,9 @@ __all__ = [
     "gau_forward",
     "glu_forward",
     "quad_gau_attention",
+    "decode_init",
+    "decode_step",
+    "decode_sequence",
 ]
 
 
@@ -328,3 +341,68 @@ def quad_gau_attention(X, W_z, gamma_q, beta_q, gamma_k, beta_k, causal):
     if causal:
         A = np.tril(A)
     return A
+
+
+# ---------------------------------------------------------------------------------------------
+# Causal decoding in the RNN form.
+# ---------------------------------------------------------------------------------------------
+
+def decode_init(B, s, e, chunk):
+    """Empty decoding state for B sequences: the linear state S [B, s, e] (Σ K_linᵀ V over the
+    completed chunks) and the current chunk's K_quad [B, c, s], K_lin [B, c, s] and V [B, c, e]."""
+    return dict(S=np.zeros((B, s, e)), Kq=np.zeros((B, chunk, s)), Kl=np.zeros((B, chunk, s)),
+                V=np.zeros((B, chunk, e)))
+
+
+def decode_step(state, x, t, n, W_u, W_v, W_z, gamma, beta, W_o, chunk,
+                local_norm="c2", global_norm="n"):
+    """Output of token t (0-based, the same position in every sequence) of the causal layer, given
+    the state left by tokens 0..t-1; updates the state in place. x is [B, d]; returns o [B, d].
+
+    Steps, in the order of "Mixed Chunk" for one token i = t mod c of chunk g = t div c: project
+    and take the four heads; store k_quad, k_lin, v as row i of the chunk; local term over the keys
+    0..i of the chunk (the causal mask keeps the diagonal); global term q_lin S / n with S the sum
+    over the earlier chunks only (``global_norm="count"`` divides by the g·c tokens summed
+    instead, 0 in the first chunk); gate and output projection. After the chunk's last token,
+    S += K_lin_gᵀ V_g (the state update of the RNN form of csdn section 1.4, a chunk at a time).
+    """
+    x = _f64(x)
+    i, g = t % chunk, t // chunk
+    U, V, Z = project(x, W_u, W_v, W_z)
+    Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    s = Z.shape[-1]
+    state["Kq"][:, i] = Kq
+    state["Kl"][:, i] = Kl
+    state["V"][:, i] = V
+    scores = np.einsum("bs,bjs->bj", Qq, state["Kq"][:, : i + 1])
+    if local_norm == "c2":
+        w = np.maximum(scores / chunk, 0.0) ** 2
+    elif local_norm == "cs":
+        w = np.maximum(scores, 0.0) ** 2 / (chunk * s)
+    else:
+        raise ValueError(local_norm)
+    Vq = np.einsum("bj,bje->be", w, state["V"][:, : i + 1])
+    if global_norm == "n":
+        scale = 1.0 / n
+    elif global_norm == "count":
+        scale = 0.0 if g == 0 else 1.0 / (g * chunk)
+    else:
+        raise ValueError(global_norm)
+    Vl = np.einsum("bs,bse->be", Ql, state["S"]) * scale
+    o = combine(U, Vq, Vl, W_o)
+    if i == chunk - 1:
+        state["S"] += np.einsum("bjs,bje->bse", state["Kl"], state["V"])
+    return o
+
+
+def decode_sequence(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, n=None, **norms):
+    """Runs decode_step over tokens 0..T-1 of X [B, T, d] from an empty state; returns the outputs
+    [B, T, d] and the final state. n defaults to T."""
+    X = _f64(X)
+    B, T, _ = X.shape
+    n = T if n is None else n
+    state = decode_init(B, _f64(W_z).shape[1], _f64(W_u).shape[1], chunk)
+    out = np.zeros((B, T, _f64(W_o).shape[1]))
+    for t in range(T):
+        out[:, t] = decode_step(state, X[:, t], t, n, W_u, W_v, W_z, gamma, beta, W_o, chunk, **norms)
+    return out, state
