@@ -1,0 +1,446 @@
+// decode.hip — one causal decoding step of the FLASH layer for AMD Instinct MI355X (gfx950).
+//
+// The RNN form of causal linear attention (page "大模型训练之加速篇 -attention优化",
+// blog.csdn.net, section 1.4: a running state updated token by token serves generation), joined to
+// the causal "Mixed Chunk" layer of the page "FLASH: Possibly the Most Interesting Efficient
+// Transformer Design Recently" (kexue.fm/archives/8934): token t of chunk g = t / c, position
+// i = t mod c, reads
+//   V̂_quad = Σ_{j<=i} relu(q_quad · k_quad_j / c)² v_j      over the keys of its own chunk
+//   V̂_lin  = q_lin S / n,  S = Σ_{h<g} K_lin_hᵀ V_h           the state of the earlier chunks
+//   o      = [u ⊙ (V̂_quad + V̂_lin)] W_o
+// and after the chunk's last token the state takes in the chunk: S += K_lin_gᵀ V_g.
+//
+// One step for B sequences (all at position t) is four small launches, none of them a GEMM of
+// any size: with one token per sequence the work is reading the weights and the state once.
+//   proj   h = x (W_u | W_v | W_z) for the B tokens: each wave owns 16 weight rows of the packed
+//          (K-contiguous) weights and multiplies them with 16 token rows on the matrix cores,
+//          operands fetched straight from global memory into fragments; epilogue SiLU, the four
+//          heads, k_quad, k_lin and v written as row i of the chunk cache
+//   attn   per sequence and 256 value columns: the weights relu(q·k_j / c)² for j <= i, then
+//          Σ_j w_j v_j + q_lin S / n over the rows of the chunk cache and of the state, split over
+//          32 row slots and reduced through LDS; y = u ⊙ (·)
+//   out    o = y W_o, the same skinny matrix-core product as proj
+//   fold   (after the last token of a chunk) S += K_linᵀ V of the chunk, fp32 FMAs
+// and at t = 0 a fill kernel clears S first.
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace {
+
+// ------------------------------------------------------------------------------ skinny product
+// acc = A[16 rows] · Xr[16 rows]ᵀ over K elements for one wave: lane l feeds row l % 16 of both
+// operands and the 16-byte chunk l / 16 of each K-step (the matrix-core fragment layout), so
+// lane l ends with C[4 (l / 16) + r][l % 16], r = 0..3 (rows of A, then the Xr row). Eight
+// K-steps of loads are issued before their products to keep bytes in flight.
+template <class E>
+__device__ __forceinline__ f32x4 skinny16(const Rows& a, const Rows& xr, int K, int lane) {
+  constexpr int kElems = 16 / E::kSize;  // elements per 16-byte chunk
+  constexpr int kStep = 4 * kElems;      // K covered by one mma()
+  const int lr = lane & 15, q = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nsteps = (K + kStep - 1) / kStep;
+  for (int st = 0; st < nsteps; st += 8) {
+    u32x4 fa[8], fx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = (st + u) * kStep + q * kElems;
+      const bool in = k < K;
+      fa[u] = load16(a, in ? uint32_t(lr) * a.ld + uint32_t(k) * E::kSize : kOutOfRange);
+      fx[u] = load16(xr, in ? uint32_t(lr) * xr.ld + uint32_t(k) * E::kSize : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mma(acc, fa[u], fx[u], E());
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------------------------ proj
+template <class E>
+struct DecProjArgs {
+  const typename E::T* x;      // [B, d]
+  const typename E::T* WcatT;  // [2e+s, d]
+  const float* gamma;          // [4, s]
+  const float* beta;           // [4, s]
+  typename E::T* U;            // [B, e]
+  typename E::T* Vc;           // [B, c, e]
+  typename E::T* Qq;           // [B, s]
+  typename E::T* Kqc;          // [B, c, s]
+  typename E::T* Ql;           // [B, s]
+  typename E::T* Klc;          // [B, c, s]
+  int B, d, e, s, c, i;
+};
+
+// grid (ceil((2e+s) / 64), ceil(B / 16)), 256 threads: wave w owns weight rows 64 x + 16 w.
+template <class E>
+__global__ __launch_bounds__(256) void dec_proj_kernel(DecProjArgs<E> p) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int ncols = 2 * p.e + p.s;
+  const int col0 = blockIdx.x * 64 + wave * 16;
+  const int b0 = blockIdx.y * 16;
+  if (col0 >= ncols) return;  // wave-uniform; no barrier follows
+  const int64_t ld = int64_t(p.d) * E::kSize;
+  const Rows a = make_rows(p.WcatT, col0, ld, min(16, ncols - col0));
+  const Rows xr = make_rows(p.x, b0, ld, min(16, p.B - b0));
+  const f32x4 acc = skinny16<E>(a, xr, p.d, lane);
+
+  const int b = b0 + (lane & 15);
+  const int j = col0 + 4 * (lane >> 4);  // first of four consecutive output columns
+  if (b >= p.B || j >= ncols) return;
+  float y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = silu(acc[r]);
+  // e and s are multiples of 8, so the four columns never straddle U, V and the heads
+  if (j < p.e) {
+    store4(p.U + int64_t(b) * p.e + j, y[0], y[1], y[2], y[3]);
+  } else if (j < 2 * p.e) {
+    store4(p.Vc + (int64_t(b) * p.c + p.i) * p.e + (j - p.e), y[0], y[1], y[2], y[3]);
+  } else {
+    const int jj = j - 2 * p.e;
+    float h[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[k][r] = fmaf(p.gamma[k * p.s + jj + r], y[r], p.beta[k * p.s + jj + r]);
+    const int64_t row = int64_t(b) * p.s + jj;
+    const int64_t crow = (int64_t(b) * p.c + p.i) * p.s + jj;
+    store4(p.Qq + row, h[0][0], h[0][1], h[0][2], h[0][3]);
+    store4(p.Kqc + crow, h[1][0], h[1][1], h[1][2], h[1][3]);
+    store4(p.Ql + row, h[2][0], h[2][1], h[2][2], h[2][3]);
+    store4(p.Klc + crow, h[3][0], h[3][1], h[3][2], h[3][3]);
+  }
+}
+
+// ------------------------------------------------------------------------------ attn
+template <class E>
+struct DecAttnArgs {
+  const typename E::T* Qq;   // [B, s]
+  const typename E::T* Kqc;  // [B, c, s]
+  const typename E::T* Ql;   // [B, s]
+  const typename E::T* Vc;   // [B, c, e]
+  const float* S;            // [B, s, e]
+  const typename E::T* U;    // [B, e]
+  typename E::T* Y;          // [B, e]
+  int B, e, s, c, i;
+  float inv_c, inv_n;
+};
+
+constexpr int kAttnCols = 256;   // value columns per workgroup
+constexpr int kAttnSlots = 32;   // row slots (1024 threads = 32 slots x 32 groups of 8 columns)
+constexpr int kAttnThreads = 1024;
+
+// 8 consecutive elements as fp32 (16 bytes for bf16, two 16-byte loads for fp32).
+__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(v[k] << 16);
+    o[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = a[k];
+    o[4 + k] = b[k];
+  }
+}
+
+// grid (ceil(e / 256), B), 1024 threads, dynamic LDS (c + 2 s + 32·256) floats.
+template <class E>
+__global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p) {
+  extern __shared__ float sh[];
+  float* part = sh;                             // [32][256] partial sums
+  float* qq = part + kAttnSlots * kAttnCols;    // [s]
+  float* ql = qq + p.s;                         // [s]
+  float* w = ql + p.s;                          // [i + 1]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int col0 = blockIdx.x * kAttnCols;
+  for (int k = tid; k < p.s; k += kAttnThreads) {
+    qq[k] = to_f32(p.Qq[int64_t(b) * p.s + k]);
+    ql[k] = to_f32(p.Ql[int64_t(b) * p.s + k]) * p.inv_n;
+  }
+  __syncthreads();
+  // local weights of the keys 0..i of this chunk
+  for (int j = tid; j <= p.i; j += kAttnThreads) {
+    const typename E::T* kr = p.Kqc + (int64_t(b) * p.c + j) * p.s;
+    float dot = 0.f;
+    for (int k = 0; k < p.s; k += 8) {
+      float kv[8];
+      load8(kr + k, kv);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) dot = fmaf(qq[k + m], kv[m], dot);
+    }
+    const float r = fmaxf(dot * p.inv_c, 0.f);
+    w[j] = r * r;
+  }
+  __syncthreads();
+
+  // Σ_j w_j v_j over the cache rows and Σ_k (q_lin,k / n) S_k over the state rows; slot `sl`
+  // takes rows sl, sl + 32, ...; group `cg` owns 8 consecutive value columns.
+  const int cg = tid & 31, sl = tid >> 5;
+  const int col = col0 + cg * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col < p.e) {  // e % 8 == 0: the 8 columns are all valid or all past the end
+    const typename E::T* vb = p.Vc + int64_t(b) * p.c * p.e + col;
+#pragma unroll 4
+    for (int j = sl; j <= p.i; j += kAttnSlots) {
+      float v[8];
+      load8(vb + int64_t(j) * p.e, v);
+      const float wj = w[j];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = fmaf(wj, v[m], acc[m]);
+    }
+    const float* sb = p.S + int64_t(b) * p.s * p.e + col;
+#pragma unroll 4
+    for (int k = sl; k < p.s; k += kAttnSlots) {
+      float v[8];
+      load8(sb + int64_t(k) * p.e, v);
+      const float qk = ql[k];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = fmaf(qk, v[m], acc[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) part[sl * kAttnCols + cg * 8 + m] = acc[m];
+  __syncthreads();
+  if (tid < kAttnCols && col0 + tid < p.e) {
+    float sum = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < kAttnSlots; ++r) sum += part[r * kAttnCols + tid];
+    const int64_t o = int64_t(b) * p.e + col0 + tid;
+    p.Y[o] = from_f32<E>(to_f32(p.U[o]) * sum);
+  }
+}
+
+// ------------------------------------------------------------------------------ out
+template <class E>
+struct DecOutArgs {
+  const typename E::T* WoT;  // [d, e]
+  const typename E::T* Y;    // [B, e]
+  typename E::T* O;          // [B, d]
+  int B, d, e;
+};
+
+// grid (ceil(d / 64), ceil(B / 16)), 256 threads.
+template <class E>
+__global__ __launch_bounds__(256) void dec_out_kernel(DecOutArgs<E> p) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int col0 = blockIdx.x * 64 + wave * 16;
+  const int b0 = blockIdx.y * 16;
+  if (col0 >= p.d) return;
+  const int64_t ld = int64_t(p.e) * E::kSize;
+  const Rows a = make_rows(p.WoT, col0, ld, min(16, p.d - col0));
+  const Rows yr = make_rows(p.Y, b0, ld, min(16, p.B - b0));
+  const f32x4 acc = skinny16<E>(a, yr, p.e, lane);
+  const int b = b0 + (lane & 15);
+  const int j = col0 + 4 * (lane >> 4);
+  if (b < p.B && j < p.d) store4(p.O + int64_t(b) * p.d + j, acc[0], acc[1], acc[2], acc[3]);
+}
+
+// ------------------------------------------------------------------------------ fold
+template <class E>
+struct DecFoldArgs {
+  const typename E::T* Klc;  // [B, c, s]
+  const typename E::T* Vc;   // [B, c, e]
+  float* S;                  // [B, s, e]
+  int B, e, s, c;
+};
+
+constexpr int kFoldRows = 32;    // state rows (K_lin dimensions) per workgroup
+constexpr int kFoldTokens = 64;  // chunk tokens staged in LDS at a time
+
+// grid (ceil(e / 256), ceil(s / 32), B), 256 threads: thread = one value column, 32 state rows.
+template <class E>
+__global__ __launch_bounds__(256) void dec_fold_kernel(DecFoldArgs<E> p) {
+  __shared__ float kl[kFoldTokens][kFoldRows];
+  const int tid = threadIdx.x;
+  const int col = blockIdx.x * 256 + tid;
+  const int k0 = blockIdx.y * kFoldRows;
+  const int b = blockIdx.z;
+  float acc[kFoldRows];
+#pragma unroll
+  for (int k = 0; k < kFoldRows; ++k) acc[k] = 0.f;
+  for (int j0 = 0; j0 < p.c; j0 += kFoldTokens) {
+    __syncthreads();  // the previous tile is consumed
+    {
+      const int jj = tid >> 2, kk = (tid & 3) * 8;  // 64 tokens x 4 groups of 8 rows
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (j0 + jj < p.c && k0 + kk < p.s) load8(p.Klc + (int64_t(b) * p.c + j0 + jj) * p.s + k0 + kk, v);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kl[jj][kk + m] = v[m];
+    }
+    __syncthreads();
+    if (col < p.e) {
+      const int nt = min(kFoldTokens, p.c - j0);
+      const typename E::T* vb = p.Vc + (int64_t(b) * p.c + j0) * p.e + col;
+      for (int jj = 0; jj < nt; ++jj) {
+        const float v = to_f32(vb[int64_t(jj) * p.e]);
+#pragma unroll
+        for (int k = 0; k < kFoldRows; ++k) acc[k] = fmaf(kl[jj][k], v, acc[k]);
+      }
+    }
+  }
+  if (col < p.e) {
+#pragma unroll
+    for (int k = 0; k < kFoldRows; ++k)
+      if (k0 + k < p.s) p.S[(int64_t(b) * p.s + k0 + k) * p.e + col] += acc[k];
+  }
+}
+
+// ------------------------------------------------------------------------------ clear
+__global__ __launch_bounds__(256) void dec_clear_kernel(float* S, int64_t n4) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k = blockIdx.x * int64_t(256) + threadIdx.x; k < n4; k += int64_t(gridDim.x) * 256)
+    reinterpret_cast<f32x4*>(S)[k] = z;
+}
+
+// ------------------------------------------------------------------------------ host side
+struct DecodePlan {
+  int64_t B, d, e, s, c, esz, ncols;
+  size_t off[FLASHGAU_DS_COUNT];
+  size_t total;
+};
+
+int make_decode_plan(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                     flashgau_dtype dtype, DecodePlan* p) {
+  if (dtype != FLASHGAU_F32 && dtype != FLASHGAU_BF16) return FLASHGAU_ERR_UNSUPPORTED;
+  if (B < 0 || d < 1 || e < 1 || s < 1 || chunk < 1) return FLASHGAU_ERR_BAD_SHAPE;
+  if (d % 8 || e % 8 || s % 8) return FLASHGAU_ERR_UNSUPPORTED;
+  // the attention kernel keeps the chunk's weights and both query heads in LDS next to its
+  // 32 KB of partial sums (64 KB in all)
+  if (chunk + 2 * s + kAttnSlots * kAttnCols > 16384) return FLASHGAU_ERR_UNSUPPORTED;
+  p->B = B, p->d = d, p->e = e, p->s = s, p->c = chunk;
+  p->esz = dtype == FLASHGAU_BF16 ? 2 : 4;
+  p->ncols = 2 * e + s;
+  int64_t bce, bcs, bse;
+  if (!mul_ok(B * chunk, e, &bce) || !mul_ok(B * chunk, s, &bcs) || !mul_ok(B * s, e, &bse) ||
+      B > kInt32Max / 16 || p->ncols > kInt32Max || B * chunk > kInt32Max || bce > kInt32Max ||
+      bse > kInt32Max || d * p->esz > kInt32Max / 16 || e * p->esz > kInt32Max / 16)
+    return FLASHGAU_ERR_BAD_SHAPE;
+  const int64_t counts[FLASHGAU_DS_COUNT] = {bse, bcs, bcs, bce, B * e, B * s, B * s, B * e};
+  size_t off = 0;
+  for (int k = 0; k < FLASHGAU_DS_COUNT; ++k) {
+    int64_t bytes;
+    const int64_t esz = k == FLASHGAU_DS_S ? 4 : p->esz;  // the state is always fp32
+    if (!mul_ok(counts[k], esz, &bytes)) return FLASHGAU_ERR_BAD_SHAPE;
+    p->off[k] = off;
+    const size_t padded = (size_t(bytes) + 255) & ~size_t(255);
+    if (__builtin_add_overflow(off, padded, &off)) return FLASHGAU_ERR_BAD_SHAPE;
+  }
+  p->total = off;
+  return FLASHGAU_OK;
+}
+
+template <class E>
+int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_t wo_off,
+                  const float* gamma, const float* beta, int64_t t, int64_t n, void* o, char* st,
+                  hipStream_t stream) {
+  using T = typename E::T;
+  const int B = int(pl.B), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
+  const int i = int(t % pl.c);
+  float* S = reinterpret_cast<float*>(st + pl.off[FLASHGAU_DS_S]);
+  T* Kqc = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_KQ]);
+  T* Klc = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_KL]);
+  T* Vc = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_V]);
+  T* U = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_U]);
+  T* Qq = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_QQ]);
+  T* Ql = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_QL]);
+  T* Y = reinterpret_cast<T*>(st + pl.off[FLASHGAU_DS_Y]);
+  const T* WcatT = reinterpret_cast<const T*>(packed);
+  const T* WoT = reinterpret_cast<const T*>(packed + wo_off);
+
+  if (t == 0) {
+    const int64_t n4 = pl.B * pl.s * pl.e / 4;
+    const int64_t nb = std::min<int64_t>(cdiv(n4, 256), 4096);
+    hipLaunchKernelGGL(dec_clear_kernel, dim3(unsigned(nb)), dim3(256), 0, stream, S, n4);
+  }
+  {
+    DecProjArgs<E> a{reinterpret_cast<const T*>(x), WcatT, gamma, beta, U, Vc, Qq, Kqc, Ql, Klc,
+                     B, d, e, s, c, i};
+    hipLaunchKernelGGL(dec_proj_kernel<E>, dim3(unsigned(cdiv(pl.ncols, 64)), unsigned(cdiv(B, 16))),
+                       dim3(256), 0, stream, a);
+  }
+  {
+    DecAttnArgs<E> a{Qq, Kqc, Ql, Vc, S, U, Y, B, e, s, c, i, float(1.0 / double(c)),
+                     float(1.0 / double(n))};
+    const size_t lds = size_t(kAttnSlots * kAttnCols + 2 * s + c) * sizeof(float);
+    hipLaunchKernelGGL(dec_attn_kernel<E>, dim3(unsigned(cdiv(e, kAttnCols)), unsigned(B)),
+                       dim3(kAttnThreads), lds, stream, a);
+  }
+  {
+    DecOutArgs<E> a{WoT, Y, reinterpret_cast<T*>(o), B, d, e};
+    hipLaunchKernelGGL(dec_out_kernel<E>, dim3(unsigned(cdiv(d, 64)), unsigned(cdiv(B, 16))),
+                       dim3(256), 0, stream, a);
+  }
+  if (i == c - 1) {
+    DecFoldArgs<E> a{Klc, Vc, S, B, e, s, c};
+    hipLaunchKernelGGL(dec_fold_kernel<E>,
+                       dim3(unsigned(cdiv(e, 256)), unsigned(cdiv(s, kFoldRows)), unsigned(B)),
+                       dim3(256), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flashgau_decode_state_size(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                               flashgau_dtype dtype, size_t* out_bytes) {
+  if (!out_bytes) return FLASHGAU_ERR_NULL_PTR;
+  DecodePlan pl;
+  const int rc = make_decode_plan(B, d, e, s, chunk, dtype, &pl);
+  if (rc != FLASHGAU_OK) return rc;
+  *out_bytes = pl.total;
+  return FLASHGAU_OK;
+}
+
+int flashgau_decode_state_offsets(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                                  flashgau_dtype dtype, size_t* out_offsets) {
+  if (!out_offsets) return FLASHGAU_ERR_NULL_PTR;
+  DecodePlan pl;
+  const int rc = make_decode_plan(B, d, e, s, chunk, dtype, &pl);
+  if (rc != FLASHGAU_OK) return rc;
+  memcpy(out_offsets, pl.off, sizeof(pl.off));
+  return FLASHGAU_OK;
+}
+
+int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes,
+                          const float* gamma, const float* beta, int64_t chunk, int64_t t,
+                          int64_t n, int64_t B, int64_t d, int64_t e, int64_t s,
+                          flashgau_dtype dtype, void* o, void* state, size_t state_bytes,
+                          void* hip_stream) {
+  DecodePlan pl;
+  int rc = make_decode_plan(B, d, e, s, chunk, dtype, &pl);
+  if (rc != FLASHGAU_OK) return rc;
+  if (n < 1 || t < 0 || t >= n) return FLASHGAU_ERR_BAD_SHAPE;
+  size_t wo_off = 0, packed_total = 0;
+  rc = packed_plan(d, e, s, dtype, &wo_off, &packed_total);
+  if (rc != FLASHGAU_OK) return rc;
+  if (B == 0) return FLASHGAU_OK;
+  if (!x || !packed || !gamma || !beta || !o || !state) return FLASHGAU_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(packed) || misaligned(gamma) || misaligned(beta) ||
+      misaligned(o) || misaligned(state))
+    return FLASHGAU_ERR_MISALIGNED;
+  if (packed_bytes < packed_total || state_bytes < pl.total) return FLASHGAU_ERR_WORKSPACE;
+  const size_t nx = size_t(B * d * pl.esz), no = nx, ng = size_t(4 * s * 4);
+  const void* ins[4] = {x, packed, gamma, beta};
+  const size_t in_sz[4] = {nx, packed_total, ng, ng};
+  for (int k = 0; k < 4; ++k)
+    if (overlaps(o, no, ins[k], in_sz[k]) || overlaps(state, pl.total, ins[k], in_sz[k]))
+      return FLASHGAU_ERR_ALIASING;
+  if (overlaps(o, no, state, pl.total)) return FLASHGAU_ERR_ALIASING;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  char* st = reinterpret_cast<char*>(state);
+  const char* pk = reinterpret_cast<const char*>(packed);
+  return dtype == FLASHGAU_BF16
+             ? launch_decode<BF16>(pl, x, pk, wo_off, gamma, beta, t, n, o, st, stream)
+             : launch_decode<F32>(pl, x, pk, wo_off, gamma, beta, t, n, o, st, stream);
+}
+
+}  // extern "C"

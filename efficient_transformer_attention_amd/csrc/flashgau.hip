@@ -31,196 +31,9 @@
 #include <algorithm>
 
 #include "flashgau.h"
+#include "common.h"
 
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, each with a private L2
-constexpr int kRowChunks = 8;   // 16-byte chunks per LDS row and K-stage (128 bytes)
-constexpr int kStageBytes = kRowChunks * 16;
-
-// ------------------------------------------------------------------------------ element types
-struct BF16 {
-  using T = uint16_t;  // raw bf16 bits
-  static constexpr int kSize = 2;
-};
-struct F32 {
-  using T = float;
-  static constexpr int kSize = 4;
-};
-
-__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
-__device__ __forceinline__ float to_f32(float v) { return v; }
-
-// fp32 -> bf16, round to nearest even on the 16 dropped bits.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-template <class E>
-__device__ __forceinline__ typename E::T from_f32(float f);
-template <>
-__device__ __forceinline__ uint16_t from_f32<BF16>(float f) { return f32_to_bf16(f); }
-template <>
-__device__ __forceinline__ float from_f32<F32>(float f) { return f; }
-
-// Store four consecutive elements (8-byte aligned for bf16, 16-byte aligned for fp32).
-__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
-  u32x2 v;
-  v[0] = uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
-  v[1] = uint32_t(f32_to_bf16(c)) | (uint32_t(f32_to_bf16(d)) << 16);
-  *reinterpret_cast<u32x2*>(p) = v;
-}
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  f32x4 v = {a, b, c, d};
-  *reinterpret_cast<f32x4*>(p) = v;
-}
-__device__ __forceinline__ void load4(const uint16_t* p, float* o) {
-  u32x2 v = *reinterpret_cast<const u32x2*>(p);
-  o[0] = __uint_as_float(v[0] << 16);
-  o[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-  o[2] = __uint_as_float(v[1] << 16);
-  o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-}
-__device__ __forceinline__ void load4(const float* p, float* o) {
-  f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  o[0] = v[0];
-  o[1] = v[1];
-  o[2] = v[2];
-  o[3] = v[3];
-}
-
-// SiLU(x) = x · sigmoid(x) ("Initial Power": Swish on U and V; read as phi_z too).
-// e^{-x} is evaluated as 2^{-x·log2 e} on the hardware base-2 exponential (v_exp_f32) and the
-// quotient through the hardware reciprocal (v_rcp_f32). Large negative x gives 2^{+big} = inf,
-// rcp(inf) = 0 and the exact limit -0.
-__device__ __forceinline__ float silu(float x) {
-  const float t = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
-  return x * __builtin_amdgcn_rcpf(1.0f + t);
-}
-
-// ------------------------------------------------------------------------------ matrix cores
-// One 16-byte chunk per lane and operand: 8 bf16 (one 16x16x32 MFMA) or 4 fp32 (four 16x16x4
-// MFMAs, component j of every lane group forming one k-slice). Lane l supplies row (l % 16) of A
-// and column (l % 16) of B; lane group l / 16 selects the chunk, identically for A and B, so the
-// sum over all chunks is the full contraction.
-__device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, BF16) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x4& acc, const u32x4& a, const u32x4& b, F32) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
-}
-
-// A K-contiguous operand tile, read through a buffer resource that covers exactly its valid rows:
-// the hardware range check turns every read past the last valid row into zeros, so tile loads
-// need no per-lane branches. `kbytes` (a multiple of 16) is the valid length of each row; reads
-// of chunks past it are sent out of range and also come back as zeros.
-struct Src {
-  u32x4 rsrc;   // buffer descriptor words (scalar registers)
-  uint32_t ld;  // row pitch, bytes
-  int kbytes;
-};
-
-// Raw buffer descriptor for gfx9-family (CDNA) parts: base address, stride 0, byte range, and
-// word 3 = 32-bit data format, no swizzle.
-constexpr uint32_t kBufferWord3 = 0x00020000u;
-constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset at or past the range reads zero
-
-// base: tensor base; row0: first row of the tile; rows: valid rows from row0 (may exceed the
-// tile; only `max_rows` are ever read); k_elems: valid elements per row. Every argument is
-// block-uniform; readfirstlane states that, so the descriptor lives in scalar registers.
-__device__ __forceinline__ Src make_src(const void* base, int64_t row0, int64_t ld_elems, int esz,
-                                        int rows, int max_rows, int k_elems) {
-  Src s;
-  const uint64_t addr =
-      reinterpret_cast<uint64_t>(reinterpret_cast<const char*>(base) + row0 * ld_elems * esz);
-  const int r = rows < 0 ? 0 : (rows > max_rows ? max_rows : rows);
-  s.ld = __builtin_amdgcn_readfirstlane(uint32_t(ld_elems * esz));
-  s.rsrc[0] = __builtin_amdgcn_readfirstlane(uint32_t(addr));
-  s.rsrc[1] = __builtin_amdgcn_readfirstlane(uint32_t(addr >> 32) & 0xFFFFu);
-  s.rsrc[2] = __builtin_amdgcn_readfirstlane(uint32_t(r) * s.ld);
-  s.rsrc[3] = kBufferWord3;
-  s.kbytes = __builtin_amdgcn_readfirstlane(k_elems * esz);
-  return s;
-}
-
-// One wave copies 64 x 16 bytes from global memory straight into LDS (buffer_load_dwordx4 with
-// the LDS destination): lane l's 16 bytes land at byte lds_addr + 16 l, out-of-range lanes write
-// zeros. The load is counted in vmcnt; the caller waits for it explicitly (wait_vm) before a
-// barrier makes the data visible to the other waves. M0 carries the wave-uniform LDS address.
-__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voffset, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "s"(lds_addr)
-               : "memory");
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left open).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Four consecutive elements fetched through a buffer resource (reads past its range give 0).
-template <class E> struct UVec;
-template <> struct UVec<BF16> {
-  using type = u32x2;
-  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  }
-  __device__ __forceinline__ static void unpack(const type& w, float* o) {
-    o[0] = __uint_as_float(w[0] << 16);
-    o[1] = __uint_as_float(w[0] & 0xFFFF0000u);
-    o[2] = __uint_as_float(w[1] << 16);
-    o[3] = __uint_as_float(w[1] & 0xFFFF0000u);
-  }
-};
-template <> struct UVec<F32> {
-  using type = u32x4;
-  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  }
-  __device__ __forceinline__ static void unpack(const type& w, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(w[k]);
-  }
-};
-
-// Index of this wave inside its workgroup, as a scalar (every lane of a wave holds the same).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
-
-// Hardware places consecutive workgroup ids on consecutive XCDs (round robin). Give each XCD a
-// contiguous range of logical tiles, so tiles that share operand rows also share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int xcd = bid % kXcds;
-  const int local = bid / kXcds;
-  const int per = nblocks / kXcds;
-  const int rem = nblocks % kXcds;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
-}
-
-// Logical tile id -> (row tile, column tile): groups of `gm` row tiles are walked column by
-// column, so the tiles in flight on one XCD share a few row blocks and a few column blocks.
-__device__ __forceinline__ void grouped_tile(int lid, int ntm, int ntn, int gm, int& mt, int& nt) {
-  const int per_group = gm * ntn;
-  const int grp = lid / per_group;
-  const int first = grp * gm;
-  const int rows = min(gm, ntm - first);
-  const int local = lid - grp * per_group;
-  nt = local / rows;
-  mt = first + local % rows;
-}
 
 // Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of 16x16 accumulator fragments.
@@ -1014,13 +827,6 @@ struct Plan {
   size_t total;
 };
 
-bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
-
-constexpr int64_t kInt32Max = 2147483647;
-constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-bit grid
-
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // states tile (both element types) and the workgroup count the chunk grouping aims for
 constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
 
@@ -1092,13 +898,26 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   return FLASHGAU_OK;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || na == 0 || nb == 0) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
+// pack: (W_u | W_v | W_z)ᵀ into WcatT [2e+s, d] and W_oᵀ into WoT [d, e], one launch.
+template <class E>
+void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* W_o, int d, int e,
+                 int s, typename E::T* WcatT, typename E::T* WoT, hipStream_t stream) {
+  using T = typename E::T;
+  PackArgs<E> a;
+  const int R[4] = {d, d, d, e};
+  const int C[4] = {e, e, s, d};
+  const T* src[4] = {reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
+                     reinterpret_cast<const T*>(W_z), reinterpret_cast<const T*>(W_o)};
+  T* dst[4] = {WcatT, WcatT + int64_t(e) * d, WcatT + int64_t(2 * e) * d, WoT};
+  int tiles = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int tr = int(cdiv(R[i], 64)), tc = int(cdiv(C[i], 64));
+    a.job[i] = {src[i], dst[i], R[i], C[i], tc, tiles};
+    tiles += tr * tc;
+  }
+  a.njobs = 4;
+  hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(tiles)), dim3(256), 0, stream, a);
 }
-
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 template <class E>
 int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
@@ -1128,23 +947,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
 
   if (!mark()) return FLASHGAU_ERR_HIP;
-  // pack: (W_u | W_v | W_z)ᵀ and W_oᵀ
-  {
-    PackArgs<E> a;
-    const int R[4] = {d, d, d, e};
-    const int C[4] = {e, e, s, d};
-    const T* src[4] = {reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
-                       reinterpret_cast<const T*>(W_z), reinterpret_cast<const T*>(W_o)};
-    T* dst[4] = {WcatT, WcatT + int64_t(e) * d, WcatT + int64_t(2 * e) * d, WoT};
-    int tiles = 0;
-    for (int i = 0; i < 4; ++i) {
-      const int tr = int(cdiv(R[i], 64)), tc = int(cdiv(C[i], 64));
-      a.job[i] = {src[i], dst[i], R[i], C[i], tc, tiles};
-      tiles += tr * tc;
-    }
-    a.njobs = 4;
-    hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(tiles)), dim3(256), 0, stream, a);
-  }
+  launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT, U, Vt, Qq, Kq, Ql, Klt, gamma, beta,
@@ -1287,6 +1090,42 @@ int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, con
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, hip_stream,
                       reinterpret_cast<hipEvent_t const*>(stage_events));
+}
+
+int flashgau_packed_weights_size(int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,
+                                 size_t* out_bytes) {
+  if (!out_bytes) return FLASHGAU_ERR_NULL_PTR;
+  size_t wo_off, total;
+  const int rc = packed_plan(d, e, s, dtype, &wo_off, &total);
+  if (rc != FLASHGAU_OK) return rc;
+  *out_bytes = total;
+  return FLASHGAU_OK;
+}
+
+int flashgau_pack_weights(const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                          int64_t d, int64_t e, int64_t s, flashgau_dtype dtype, void* packed,
+                          size_t packed_bytes, void* hip_stream) {
+  size_t wo_off, total;
+  const int rc = packed_plan(d, e, s, dtype, &wo_off, &total);
+  if (rc != FLASHGAU_OK) return rc;
+  if (!W_u || !W_v || !W_z || !W_o || !packed) return FLASHGAU_ERR_NULL_PTR;
+  if (misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o) || misaligned(packed))
+    return FLASHGAU_ERR_MISALIGNED;
+  if (packed_bytes < total) return FLASHGAU_ERR_WORKSPACE;
+  const size_t esz = dtype == FLASHGAU_BF16 ? 2 : 4;
+  const size_t nde = size_t(d) * size_t(e) * esz, nds = size_t(d) * size_t(s) * esz;
+  if (overlaps(packed, total, W_u, nde) || overlaps(packed, total, W_v, nde) ||
+      overlaps(packed, total, W_z, nds) || overlaps(packed, total, W_o, nde))
+    return FLASHGAU_ERR_ALIASING;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  char* base = reinterpret_cast<char*>(packed);
+  if (dtype == FLASHGAU_BF16)
+    launch_pack<BF16>(W_u, W_v, W_z, W_o, int(d), int(e), int(s), reinterpret_cast<uint16_t*>(base),
+                      reinterpret_cast<uint16_t*>(base + wo_off), stream);
+  else
+    launch_pack<F32>(W_u, W_v, W_z, W_o, int(d), int(e), int(s), reinterpret_cast<float*>(base),
+                     reinterpret_cast<float*>(base + wo_off), stream);
+  return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
 }
 
 const char* flashgau_strerror(int code) {

@@ -29,8 +29,13 @@ ERR_HIP = -7
 # Order of the workspace buffers (FLASHGAU_WS_* in include/flashgau.h).
 WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CARRY")
 
+# Order of the decoding-state buffers (FLASHGAU_DS_* in include/flashgau.h).
+DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
+
 EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_state_groups",
-           "flash_gau_forward", "flash_gau_forward_timed", "flashgau_strerror")
+           "flash_gau_forward", "flash_gau_forward_timed", "flashgau_packed_weights_size",
+           "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
+           "flash_gau_decode_step", "flashgau_strerror")
 
 # Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
 STAGES = ("pack", "proj", "scores", "states", "carry", "mix", "out")
@@ -66,6 +71,17 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_forward.restype = ctypes.c_int
     L.flash_gau_forward_timed.argtypes = L.flash_gau_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
     L.flash_gau_forward_timed.restype = ctypes.c_int
+    L.flashgau_packed_weights_size.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_packed_weights_size.restype = ctypes.c_int
+    L.flashgau_pack_weights.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
+    L.flashgau_pack_weights.restype = ctypes.c_int
+    L.flashgau_decode_state_size.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_decode_state_size.restype = ctypes.c_int
+    L.flashgau_decode_state_offsets.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_decode_state_offsets.restype = ctypes.c_int
+    L.flash_gau_decode_step.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_int, vp, vp, sz, vp]
+    L.flash_gau_decode_step.restype = ctypes.c_int
     L.flashgau_strerror.argtypes = [ctypes.c_int]
     L.flashgau_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -190,3 +206,117 @@ def workspace_views(workspace, B, n, d, e, s, chunk, causal, dtype):
         raw = workspace[off[name]: off[name] + count * esz]
         views[name] = raw.view(tdt).view(shape)
     return views
+
+
+# ------------------------------------------------------------------------------ decoding
+
+
+def packed_weights_size(d, e, s, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().flashgau_packed_weights_size(d, e, s, dtype, ctypes.byref(out))
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_packed_weights_size")
+    return out.value
+
+
+def decode_state_size(B, d, e, s, chunk, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().flashgau_decode_state_size(B, d, e, s, chunk, dtype, ctypes.byref(out))
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_decode_state_size")
+    return out.value
+
+
+def decode_state_offsets(B, d, e, s, chunk, dtype) -> dict:
+    arr = (ctypes.c_size_t * len(DS_NAMES))()
+    rc = lib().flashgau_decode_state_offsets(B, d, e, s, chunk, dtype, arr)
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_decode_state_offsets")
+    return dict(zip(DS_NAMES, list(arr)))
+
+
+def pack_weights_raw(W_u, W_v, W_z, W_o, d, e, s, dtype, packed, packed_bytes, stream) -> int:
+    """Direct call of flashgau_pack_weights with integer addresses; returns the library's code."""
+    return lib().flashgau_pack_weights(W_u, W_v, W_z, W_o, d, e, s, dtype, packed, packed_bytes, stream)
+
+
+def decode_step_raw(x, packed, packed_bytes, gamma, beta, chunk, t, n, B, d, e, s, dtype, o, state,
+                    state_bytes, stream) -> int:
+    """Direct call of flash_gau_decode_step with integer addresses; returns the library's code."""
+    return lib().flash_gau_decode_step(x, packed, packed_bytes, gamma, beta, chunk, t, n, B, d, e, s,
+                                       dtype, o, state, state_bytes, stream)
+
+
+def pack_weights(W_u, W_v, W_z, W_o, stream=None):
+    """Packs the weights for decoding (one transpose launch): returns a uint8 device tensor."""
+    import torch
+    d, e = W_u.shape
+    s = W_z.shape[1]
+    dt = _dtype_code(W_u.dtype)
+    for name, t, shape in (("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)), ("W_o", W_o, (e, d))):
+        if tuple(t.shape) != shape or t.dtype != W_u.dtype:
+            raise ValueError(f"{name} must be {W_u.dtype} {shape}")
+    if any(not t.is_contiguous() or t.device != W_u.device for t in (W_u, W_v, W_z, W_o)):
+        raise ValueError("weights must be contiguous and on one GPU")
+    nbytes = packed_weights_size(d, e, s, dt)
+    packed = torch.empty((nbytes,), dtype=torch.uint8, device=W_u.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(W_u.device).cuda_stream
+    rc = pack_weights_raw(W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), W_o.data_ptr(), d, e, s, dt,
+                          packed.data_ptr(), nbytes, stream)
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_pack_weights")
+    return packed
+
+
+class DecodeState:
+    """Caller-owned decoding state of B sequences (one uint8 device buffer, layout in
+    include/flashgau.h). The step at t = 0 clears the linear state itself."""
+
+    def __init__(self, B, d, e, s, chunk, dtype, device):
+        import torch
+        self.B, self.d, self.e, self.s, self.chunk = B, d, e, s, chunk
+        self.dt = _dtype_code(dtype)
+        self.nbytes = decode_state_size(B, d, e, s, chunk, self.dt)
+        self.buf = torch.empty((max(self.nbytes, 1),), dtype=torch.uint8, device=device)
+
+    def views(self):
+        """Typed views of the state's buffers."""
+        import torch
+        tdt = torch.bfloat16 if self.dt == BF16 else torch.float32
+        esz = 2 if self.dt == BF16 else 4
+        off = decode_state_offsets(self.B, self.d, self.e, self.s, self.chunk, self.dt)
+        B, e, s, c = self.B, self.e, self.s, self.chunk
+        shapes = {"S": (B, s, e), "KQ": (B, c, s), "KL": (B, c, s), "V": (B, c, e), "U": (B, e),
+                  "QQ": (B, s), "QL": (B, s), "Y": (B, e)}
+        views = {}
+        for name, shape in shapes.items():
+            count = 1
+            for x in shape:
+                count *= x
+            if name == "S":
+                views[name] = self.buf[off[name]: off[name] + count * 4].view(torch.float32).view(shape)
+            else:
+                views[name] = self.buf[off[name]: off[name] + count * esz].view(tdt).view(shape)
+        return views
+
+
+def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, stream=None):
+    """One causal decoding step on the GPU: x [B, d] holds token t of each sequence; returns
+    o [B, d]. ``packed`` comes from pack_weights, ``state`` is a DecodeState advanced in place."""
+    import torch
+    B, d = x.shape
+    if (B, d) != (state.B, state.d) or _dtype_code(x.dtype) != state.dt:
+        raise ValueError("x does not match the decoding state")
+    if not x.is_contiguous() or any(not g.is_contiguous() or g.dtype != torch.float32 for g in (gamma, beta)):
+        raise ValueError("x must be contiguous; gamma and beta contiguous float32 [4, s]")
+    if out is None:
+        out = torch.empty((B, d), dtype=x.dtype, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = decode_step_raw(x.data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
+                         beta.data_ptr(), chunk, t, n, B, d, state.e, state.s, state.dt,
+                         out.data_ptr(), state.buf.data_ptr(), state.buf.numel(), stream)
+    if rc != OK:
+        raise FlashGauError(rc, "flash_gau_decode_step")
+    return out

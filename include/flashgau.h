@@ -152,6 +152,86 @@ int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, con
                             size_t workspace_bytes, void* hip_stream, void* const* stage_events,
                             int num_events);
 
+/* ---------------------------------------------------------------------------------------------
+ * Causal decoding, one token per sequence (the RNN form).
+ *
+ * Page "大模型训练之加速篇 -attention优化" (blog.csdn.net), section 1.4: causal linear attention
+ * can run as a recurrence over a state, the form suited to generation. Joined to the causal
+ * "Mixed Chunk" layer above, token t (0-based) of chunk g = t / c, at position i = t mod c,
+ * produces
+ *   o_t = [u_t ⊙ (Σ_{j<=i} relu(q_quad,t · k_quad,j / c)² v_j + q_lin,t S / n)] W_o
+ * where j runs over the tokens of its own chunk so far and S = Σ_{h<g} K_lin_hᵀ V_h is the state
+ * of the completed chunks; after the last token of a chunk, S += K_lin_gᵀ V_g. Stepping t from 0
+ * to n-1 reproduces the rows of the causal flash_gau_forward (same readings: relu²(q·k/c), /n with
+ * n the normalising length, SiLU for Z). Every sequence of the batch is at the same position t.
+ * ------------------------------------------------------------------------------------------- */
+
+/* The decoder reads the weights transposed, as the forward's first stage writes them:
+ * packed = [ (W_u | W_v | W_z)ᵀ  [2e+s, d] | pad to 256 B | W_oᵀ [d, e] ] in dtype.
+ * flashgau_packed_weights_size: bytes of that buffer (host-only). d, e, s >= 1 and multiples of
+ * 8. Returns FLASHGAU_OK or an error code. */
+int flashgau_packed_weights_size(int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,
+                                 size_t* out_bytes);
+
+/* Enqueues one transpose kernel that fills `packed` (packed_bytes >= the size above) from W_u,
+ * W_v [d, e], W_z [d, s], W_o [e, d] on hip_stream. 16-byte aligned device pointers; `packed`
+ * must not overlap the weights. Done once per set of weights, not per decoding step. */
+int flashgau_pack_weights(const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                          int64_t d, int64_t e, int64_t s, flashgau_dtype dtype, void* packed,
+                          size_t packed_bytes, void* hip_stream);
+
+/* The decoding state, one caller-owned device buffer holding, at the byte offsets given by
+ * flashgau_decode_state_offsets (each 256-byte aligned), with element type = dtype unless noted:
+ *   S   [B, s, e]  fp32   Σ K_linᵀ V over the completed chunks (not divided by n)
+ *   KQ  [B, c, s]         k_quad of the current chunk's tokens 0..i (rows past i are stale)
+ *   KL  [B, c, s]         k_lin of the same tokens
+ *   V   [B, c, e]         v of the same tokens
+ *   U   [B, e]            u of the last token (scratch of one step)
+ *   QQ, QL [B, s]         q_quad, q_lin of the last token (scratch)
+ *   Y   [B, e]            u ⊙ (V̂_quad + V̂_lin) of the last token (scratch)
+ * The state carries everything a step needs from the earlier tokens; the step at t = 0 clears S
+ * itself, so a fresh buffer needs no initialisation. One state buffer serves one stream of steps
+ * at a time. */
+enum {
+  FLASHGAU_DS_S = 0,
+  FLASHGAU_DS_KQ,
+  FLASHGAU_DS_KL,
+  FLASHGAU_DS_V,
+  FLASHGAU_DS_U,
+  FLASHGAU_DS_QQ,
+  FLASHGAU_DS_QL,
+  FLASHGAU_DS_Y,
+  FLASHGAU_DS_COUNT
+};
+
+/* Bytes of the decoding state for B sequences (host-only). B >= 0; d, e, s >= 1 and multiples
+ * of 8; chunk >= 1 with chunk + 2 s <= 8192. Returns FLASHGAU_OK or an error code. */
+int flashgau_decode_state_size(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                               flashgau_dtype dtype, size_t* out_bytes);
+
+/* Byte offsets of the FLASHGAU_DS_* buffers inside the state, written to
+ * out_offsets[0 .. FLASHGAU_DS_COUNT-1] (host-only). */
+int flashgau_decode_state_offsets(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
+                                  flashgau_dtype dtype, size_t* out_offsets);
+
+/* One decoding step: o = the layer's output for token t of each of the B sequences.
+ *   x      [B, d]  dtype, device: the tokens at position t
+ *   packed, packed_bytes: weights packed by flashgau_pack_weights (same d, e, s, dtype)
+ *   gamma, beta [4, s] fp32, device (rows Q_quad, K_quad, Q_lin, K_lin)
+ *   chunk  c; t the position (0 <= t < n); n the normalising length of the global term
+ *   o      [B, d]  dtype, device; fully overwritten
+ *   state, state_bytes: the decoding state (>= flashgau_decode_state_size bytes) left by the step
+ *          at t - 1 of the same sequences (any contents at t = 0); updated in place
+ * Steps of one state must be issued in order of t on one stream. 16-byte aligned pointers; o
+ * and the state must not overlap each other or any input. B == 0 succeeds and launches nothing.
+ * Returns FLASHGAU_OK or an error code (FLASHGAU_ERR_WORKSPACE when packed_bytes or state_bytes
+ * is too small). */
+int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes,
+                          const float* gamma, const float* beta, int64_t chunk, int64_t t,
+                          int64_t n, int64_t B, int64_t d, int64_t e, int64_t s,
+                          flashgau_dtype dtype, void* o, void* state, size_t state_bytes,
+                          void* hip_stream);
+
 /* Static, human-readable text for a return code ("unknown error" for other values). */
 const char* flashgau_strerror(int code);
 

@@ -151,3 +151,113 @@ def test_strerror_covers_every_code():
     texts = {c: fg.strerror(c) for c in range(-7, 1)}
     assert len(set(texts.values())) == 8
     assert fg.strerror(-99) == "unknown error"
+
+
+# ------------------------------------------------------------------------------ decoding
+
+def test_decode_state_enum_matches_binding():
+    text = open(HEADER).read()
+    names = re.findall(r"FLASHGAU_DS_(\w+)\s*(?:=\s*0)?,", text)
+    assert tuple(names) == fg.DS_NAMES
+
+
+@pytest.mark.parametrize("B,d,e,s,c,dt", [(8, 768, 1536, 128, 256, fg.BF16), (3, 64, 136, 24, 8, fg.F32),
+                                          (17, 40, 88, 16, 4, fg.BF16), (0, 64, 64, 8, 1, fg.BF16)])
+def test_decode_state_layout(B, d, e, s, c, dt):
+    esz = 2 if dt == fg.BF16 else 4
+    sizes = [B * s * e * 4, B * c * s * esz, B * c * s * esz, B * c * e * esz, B * e * esz,
+             B * s * esz, B * s * esz, B * e * esz]
+    off, offs = 0, []
+    for nbytes in sizes:
+        offs.append(off)
+        off += (nbytes + 255) // 256 * 256
+    assert fg.decode_state_size(B, d, e, s, c, dt) == off
+    got = fg.decode_state_offsets(B, d, e, s, c, dt)
+    assert [got[k] for k in fg.DS_NAMES] == offs
+
+
+def test_packed_weights_layout_matches_forward_workspace():
+    # the packed weights are the first two buffers of the forward's workspace
+    d, e, s = 200, 136, 24
+    for dt, esz in ((fg.BF16, 2), (fg.F32, 4)):
+        wcat = ((2 * e + s) * d * esz + 255) // 256 * 256
+        assert fg.packed_weights_size(d, e, s, dt) == wcat + (d * e * esz + 255) // 256 * 256
+        ws = fg.workspace_offsets(2, 216, d, e, s, 72, True, dt)
+        assert ws["WCAT_T"] == 0 and ws["WO_T"] == wcat
+
+
+@pytest.mark.parametrize("args,code", [
+    ((2, 64, 100, 24, 8), fg.ERR_UNSUPPORTED),   # e not a multiple of 8
+    ((2, 60, 96, 24, 8), fg.ERR_UNSUPPORTED),    # d not a multiple of 8
+    ((2, 64, 96, 24, 0), fg.ERR_BAD_SHAPE),      # chunk 0
+    ((-1, 64, 96, 24, 8), fg.ERR_BAD_SHAPE),     # negative batch
+    ((2, 64, 96, 4096, 64), fg.ERR_UNSUPPORTED),  # chunk + 2 s beyond the attention kernel's LDS
+])
+def test_decode_shape_validation(args, code):
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.decode_state_size(*args, fg.BF16)
+    assert ei.value.code == code
+
+
+DEC = dict(B=2, d=64, e=96, s=24, c=8)
+
+
+def _dcall(t=3, n=16, **over):
+    B, d, e, s, c = (DEC[k] for k in ("B", "d", "e", "s", "c"))
+    st = fg.decode_state_size(B, d, e, s, c, fg.BF16)
+    pk = fg.packed_weights_size(d, e, s, fg.BF16)
+    base = 1 << 40
+    ptrs = dict(x=base, packed=base + (1 << 30), gamma=base + (2 << 30), beta=base + (3 << 30),
+                o=base + (4 << 30), state=base + (5 << 30), packed_bytes=pk, state_bytes=st)
+    ptrs.update(over)
+    return fg.decode_step_raw(ptrs["x"], ptrs["packed"], ptrs["packed_bytes"], ptrs["gamma"],
+                              ptrs["beta"], c, t, n, B, d, e, s, fg.BF16, ptrs["o"], ptrs["state"],
+                              ptrs["state_bytes"], None)
+
+
+@pytest.mark.parametrize("t,n", [(16, 16), (-1, 16), (0, 0), (20, 16)])
+def test_decode_position_must_lie_in_the_sequence(t, n):
+    assert _dcall(t=t, n=n) == fg.ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("which", ["x", "packed", "gamma", "beta", "o", "state"])
+def test_decode_null_pointer_rejected(which):
+    assert _dcall(**{which: None}) == fg.ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("which", ["x", "packed", "o", "state"])
+def test_decode_misaligned_pointer_rejected(which):
+    base = {"x": 1 << 40, "packed": (1 << 40) + (1 << 30), "o": (1 << 40) + (4 << 30),
+            "state": (1 << 40) + (5 << 30)}[which]
+    assert _dcall(**{which: base + 8}) == fg.ERR_MISALIGNED
+
+
+def test_decode_small_buffers_rejected():
+    assert _dcall(state_bytes=256) == fg.ERR_WORKSPACE
+    assert _dcall(packed_bytes=256) == fg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("over", [
+    dict(o=1 << 40),                            # o is x
+    dict(state=(1 << 40) + (1 << 30) + 512),     # state inside the packed weights
+    dict(o=(1 << 40) + (5 << 30) + 1024),        # o inside the state
+    dict(state=(1 << 40) + (2 << 30)),           # state over gamma
+])
+def test_decode_aliasing_rejected(over):
+    assert _dcall(**over) == fg.ERR_ALIASING
+
+
+def test_decode_empty_batch_succeeds_without_pointers():
+    rc = fg.decode_step_raw(None, None, 0, None, None, 8, 0, 16, 0, 64, 96, 24, fg.BF16, None, None, 0, None)
+    assert rc == fg.OK
+
+
+def test_pack_weights_validation():
+    base = 1 << 40
+    pk = fg.packed_weights_size(64, 96, 24, fg.BF16)
+    w = [base, base + (1 << 30), base + (2 << 30), base + (3 << 30)]
+    assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, None, pk, None) == fg.ERR_NULL_PTR
+    assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, base + (4 << 30), 256, None) == fg.ERR_WORKSPACE
+    assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, base + 8 + (4 << 30), pk, None) == fg.ERR_MISALIGNED
+    assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, base + 256, pk, None) == fg.ERR_ALIASING
+    assert fg.pack_weights_raw(*w, 64, 100, 24, fg.BF16, base + (4 << 30), pk, None) == fg.ERR_UNSUPPORTED
