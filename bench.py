@@ -3,14 +3,20 @@
 
 Default workload: causal, bf16 storage with fp32 accumulation, B = 8, n = 4096, d = 768,
 e = 1536, s = 128, chunk 256, seeded synthetic inputs (X ~ N(0,1), weights ~ N(0, 1/fan_in),
-gamma ~ N(1, 0.02), beta = 0). A step is one full forward call: all six kernels (pack, proj,
-scores, states, mix, out) over the whole batch, with inputs already resident in HBM.
+gamma ~ N(1, 0.02), beta = 0). A step is one full forward call: all seven kernels (pack, proj,
+scores, states, carry, mix, out) over the whole batch, with inputs already resident in HBM.
 
 Prints one JSON line. `value` is tokens/s = B*n / (wall time of one step), timed over exactly
 --steps calls between two device synchronisations. Each call also records a HIP event before
 every kernel on the library's stream, which gives every kernel's average duration; the roofline
 object reports the kernel that takes the longest. The CPU baseline is the fp64 oracle timed on
 the host on one sequence of the same batch; its output also checks the GPU's on that sequence.
+
+For a causal workload the line also carries a "decode" object: the same batch and dimensions
+decoded one token per sequence per step (flash_gau_decode_step), timed over one whole chunk of
+positions (c .. 2c-1, the last step folding the chunk into the state) after chunk 0 has filled the
+state untimed, with its HBM roofline (algorithmic bytes per step, see decode_bytes) and the
+oracle's decode step timed on the host.
 """
 
 import argparse
@@ -153,6 +159,87 @@ def cpu_baseline(inp, seconds):
     return rec, ref
 
 
+def decode_bytes(B, d, e, s, c, esz, i):
+    """Algorithmic HBM bytes of one decoding step at position i of its chunk (B sequences): the
+    packed weights once, the token in and out, the cache rows 0..i and the fp32 state read, the
+    new cache row and the per-step scratch (u, the query heads, y) written and read back, and
+    after the chunk's last token the fold (cache read, state read and written)."""
+    w = ((2 * e + s) * d + d * e) * esz
+    io = 2 * B * d * esz
+    reads = B * (i + 1) * (s + e) * esz + B * s * e * 4
+    writes = B * (2 * s + e) * esz + 2 * B * (2 * e + 2 * s) * esz
+    fold = (B * c * (s + e) * esz + 2 * B * s * e * 4) if i == c - 1 else 0
+    return w + io + reads + writes + fold
+
+
+def decode_measure(inp, dtype, torch, fg, dev, cpu_seconds):
+    """Times one chunk of causal decoding steps (positions c .. 2c-1, after chunk 0 has filled the
+    state untimed) for the workload's batch and dimensions. Returns the record for the JSON line."""
+    B, n, d, e, s = inp.shape
+    c = inp.chunk
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    esz = 2 if dtype == "bf16" else 4
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    W = [up(a) for a in (inp.W_u, inp.W_v, inp.W_z, inp.W_o)]
+    gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
+    packed = fg.pack_weights(*W)
+    state = fg.DecodeState(B, d, e, s, c, tdt, dev)
+    xs = up(inp.X[:, : 2 * c]).transpose(0, 1).contiguous()  # [2c, B, d]: one contiguous token row per step
+    o = torch.empty((B, d), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+
+    def step(t):
+        rc = fg.decode_step_raw(xs[t].data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
+                                beta.data_ptr(), c, t, n, B, d, e, s, dt, o.data_ptr(),
+                                state.buf.data_ptr(), state.buf.numel(), stream)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_decode_step")
+
+    print(f"[bench] decode: {c} untimed steps, then {c} timed", file=sys.stderr, flush=True)
+    for t in range(c):
+        step(t)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[0]), ctypes.c_void_p(stream))
+    for t in range(c, 2 * c):
+        step(t)
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev.ms(ev.handles[0], ev.handles[1])
+    ev.close()
+    nbytes = sum(decode_bytes(B, d, e, s, c, esz, i) for i in range(c)) / c
+    us_step = gpu_ms * 1e3 / c
+    achieved = nbytes / (us_step * 1e-6) / 1e9
+    rec = {"metric": "decode tokens/s (causal, one token per sequence per step)",
+           "value": round(B * c / (wall), 1), "unit": "tokens/s", "steps": c, "batch": B,
+           "positions": [c, 2 * c - 1], "us_per_step": round(us_step, 2),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                        "bytes_per_step": int(nbytes)}}
+    if cpu_seconds > 0:
+        import oracle
+        st = oracle.decode_init(B, s, e, c)
+        times, t = [], 0
+        t_start = time.perf_counter()
+        while t < c + 8 and (t < c or time.perf_counter() - t_start < cpu_seconds):
+            t1 = time.perf_counter()
+            oracle.decode_step(st, inp.X[:, t], t, n, inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta,
+                               inp.W_o, c)
+            times.append(time.perf_counter() - t1)
+            t += 1
+        med = statistics.median(times)
+        rec["cpu_baseline"] = {"value": round(B / med, 1), "unit": "tokens/s", "kind": "oracle",
+                               "sample": f"fp64 oracle decode_step for the same {B} sequences, "
+                                         f"median of {len(times)} steps ({med * 1e3:.1f} ms each)"}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +248,8 @@ def main():
     ap.add_argument("--workload", default=None, help="name in inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the causal decoding measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -271,6 +360,10 @@ def main():
         got = O[:1].float().cpu().numpy().astype(np.float64)
         max_rel_err = float(np.abs(got - ref).max() / np.abs(ref).max())
 
+    decode = None
+    if causal and not args.no_decode:
+        decode = decode_measure(inp, dtype, torch, fg, dev, min(args.cpu_seconds, 5.0))
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -294,6 +387,7 @@ def main():
         "stages": stages,
         "cpu_baseline": cpu,
         "max_rel_err_seq0": max_rel_err,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 
