@@ -439,47 +439,64 @@ struct ScoresArgs {
   float inv_c;
 };
 
-template <class E, int BT, int WM, int WN>
+// Per chunk P = relu(Q_quad K_quadᵀ / c)², computed as Pᵀ tiles (keys x tokens) so that each
+// lane holds four consecutive keys of one token and the tile leaves through LDS as 16-byte runs of
+// P rows. Causal: only the tile pairs on or below the diagonal are launched (tiles entirely above
+// it are never read: every wave of the mix stage skips them), and entries above the diagonal
+// inside them are written as zeros.
+template <class E, int BT, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
-  using G = TileGemm<E, BT, BT, WM, WN>;
+  using G = TileGemm<E, BT, BT, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
   const int ntc = (p.c + BT - 1) / BT;
-  const int lid = xcd_remap(blockIdx.x, p.nbg * ntc * ntc);
-  const int bg = lid / (ntc * ntc);
-  const int rem = lid % (ntc * ntc);
-  const int mt = rem / ntc, nt = rem % ntc;
-  const int m0 = mt * BT, n0 = nt * BT;
+  const int per_chunk = p.causal ? ntc * (ntc + 1) / 2 : ntc * ntc;
+  const int lid = xcd_remap(blockIdx.x, p.nbg * per_chunk);
+  const int bg = lid / per_chunk;
+  const int rem = lid % per_chunk;
+  int tt, kt;  // token tile, key tile
+  if (p.causal) {
+    // rem = tt (tt + 1) / 2 + kt with 0 <= kt <= tt
+    tt = int((sqrtf(8.0f * float(rem) + 1.0f) - 1.0f) * 0.5f);
+    while (tt * (tt + 1) / 2 > rem) --tt;
+    while ((tt + 1) * (tt + 2) / 2 <= rem) ++tt;
+    kt = rem - tt * (tt + 1) / 2;
+  } else {
+    tt = rem / ntc;
+    kt = rem % ntc;
+  }
+  const int k0 = kt * BT, t0 = tt * BT;  // m: key, n: token
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   G g;
   g.zero();
-  // A tile entirely above the diagonal (every key after every query) stays zero when causal.
-  const bool live = !(p.causal && n0 > m0 + BT - 1);
-  if (live) {
-    const int64_t base = int64_t(bg) * p.c;
-    const Src a = make_src(p.Qq, base + m0, p.s, E::kSize, p.c - m0, BT, p.s);
-    const Src b = make_src(p.Kq, base + n0, p.s, E::kSize, p.c - n0, BT, p.s);
-    const int nk = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
-    g.run(lds, nk,
-          [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-            sa = a;
-            sb = b;
-            ka = kb = t * kStageBytes;
-          },
-          NoPre(), wave, wm, wn, lane);
-  }
-  typename E::T* P = p.P + int64_t(bg) * p.c * p.c;
-  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
-    const int i = m0 + r, j = n0 + cl;
-    if (i >= p.c || j >= p.c) return;
+  const int64_t base = int64_t(bg) * p.c;
+  const Src a = make_src(p.Kq, base + k0, p.s, E::kSize, p.c - k0, BT, p.s);
+  const Src b = make_src(p.Qq, base + t0, p.s, E::kSize, p.c - t0, BT, p.s);
+  const int nk = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
+  g.run(lds, nk,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          sa = a;
+          sb = b;
+          ka = kb = t * kStageBytes;
+        },
+        NoPre(), wave, wm, wn, lane);
+  using T = typename E::T;
+  T* P = p.P + base * p.c;
+  g.template stage_rows<T>(
+      lds, wave, wm, wn, lane,
+      [&](int, int, int r, int cl, const f32x4& v, T* out) {
+        const int key = k0 + r, tok = t0 + cl;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float x = fmaxf(v[k] * p.inv_c, 0.0f);
-      const float w = (p.causal && j > i + k) ? 0.0f : x * x;
-      P[int64_t(i + k) * p.c + j] = from_f32<E>(w);
-    }
-  });
+        for (int k = 0; k < 4; ++k) {
+          const float x = fmaxf(v[k] * p.inv_c, 0.0f);
+          out[k] = from_f32<E>((p.causal && key + k > tok) ? 0.0f : x * x);
+        }
+      },
+      [&](int cl, int r, const u32x4& chunk) {
+        const int key = k0 + r, tok = t0 + cl;
+        if (key < p.c && tok < p.c) *reinterpret_cast<u32x4*>(P + int64_t(tok) * p.c + key) = chunk;
+      });
 }
 
 // ------------------------------------------------------------------------------ states
@@ -651,6 +668,7 @@ struct MixArgs {
   const typename E::T* U;   // [B*G*c, e]
   typename E::T* Y;         // [B*G*c, e]
   int nbg, G, c, e, s, causal;
+  int lin;  // 0: no global term (causal with a single chunk: its prefix state is empty)
 };
 
 template <class E, int BM, int BN, int WM, int WN, int NS>
@@ -673,7 +691,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   // tokens all precede a key tile skips that tile's products.
   const int keys = p.causal ? min(p.c, n0 + BN) : p.c;
   const int nk0 = (keys * E::kSize + kStageBytes - 1) / kStageBytes;
-  const int nk1 = (p.s * E::kSize + kStageBytes - 1) / kStageBytes;
+  const int nk1 = p.lin ? (p.s * E::kSize + kStageBytes - 1) / kStageBytes : 0;
   const int64_t tok0 = int64_t(bg) * p.c;
   const int64_t slot = p.causal ? bg : bg / p.G;
   const Src a0 = make_src(p.Vt, int64_t(bg) * p.e + m0, p.c, E::kSize, p.e - m0, BM, p.c);
@@ -794,7 +812,7 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
 template <class E> struct Shapes;
 template <> struct Shapes<BF16> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 4, kProjNS = 2;
-  static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
+  static constexpr int kScoresBT = 128, kScoresWM = 2, kScoresWN = 4, kScoresNS = 2;
   // states and mix: 64 KB of LDS, so two blocks share a CU and one's epilogue overlaps the
   // other's loads
   static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 4;
@@ -805,13 +823,24 @@ template <> struct Shapes<BF16> {
 };
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
-  static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2;
+  static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2, kScoresNS = 3;
   static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesNS = 3;
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
 };
+
+// The scores stage leaves P tiles entirely above the diagonal unwritten. The mix stage never
+// multiplies them as long as each of its token tiles is one scores token tile (so a wave's tokens
+// all lie in one scores tile) and its key tiles nest in the scores key tiles.
+template <class E>
+constexpr bool scores_cover_mix() {
+  using S = Shapes<E>;
+  return S::kScoresBT == S::kMixBN && S::kScoresBT % (kStageBytes / E::kSize) == 0;
+}
+static_assert(scores_cover_mix<BF16>() && scores_cover_mix<F32>(),
+              "unwritten causal P tiles could be read by the mix stage");
 
 // The host plan sizes the chunk groups of the states stage with a 128 x 128 tile.
 static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 128 &&
@@ -959,12 +988,16 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     ScoresArgs<E> a{Qq, Kq, P, int(pl.nbg), c, s, causal, 1.0f / float(c)};
-    const int64_t nb = pl.nbg * cdiv(c, S::kScoresBT) * cdiv(c, S::kScoresBT);
-    hipLaunchKernelGGL((scores_kernel<E, S::kScoresBT, S::kScoresWM, S::kScoresWN>),
+    const int64_t ntc = cdiv(c, S::kScoresBT);
+    const int64_t nb = pl.nbg * (causal ? ntc * (ntc + 1) / 2 : ntc * ntc);
+    hipLaunchKernelGGL((scores_kernel<E, S::kScoresBT, S::kScoresWM, S::kScoresWN, S::kScoresNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kScoresWM * S::kScoresWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
-  {
+  // Causal with a single chunk: the only chunk reads an empty prefix, so there is no global
+  // term at all; the states and carry stages launch nothing and ST is left unwritten.
+  const bool lin = !(causal && pl.G == 1);
+  if (lin) {
     StatesArgs<E> a{Klt, Vt, St, Carry, int(pl.B), int(pl.G), s, e, c, causal,
                     int(pl.ng), int(pl.gs), float(1.0 / double(pl.n))};
     const int64_t nb = pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
@@ -973,7 +1006,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
                        dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
-  if (pl.ng > 1) {
+  if (lin && pl.ng > 1) {
     CarryArgs<E> a{St, Carry, int(pl.B), int(pl.G), int(pl.ng), int(pl.gs), causal,
                    int64_t(e) * s};
     const int64_t nb = cdiv(pl.B * e * s / 8, 256);
@@ -981,7 +1014,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
-    MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal};
+    MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal, int(lin)};
     const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
     hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);

@@ -64,8 +64,12 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  *   VT      [B*G, e, c]   SiLU(X W_v), transposed inside each chunk (token index fastest)
  *   QQ, KQ, QL [B*n, s]   the heads Q_quad, K_quad, Q_lin
  *   KLT     [B*G, s, c]   the head K_lin, transposed inside each chunk
- *   P       [B*G, c, c]   relu(Q_quad K_quadᵀ / c)² per chunk, zero above the diagonal if causal
- *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed
+ *   P       [B*G, c, c]   relu(Q_quad K_quadᵀ / c)² per chunk. Causal: the entries above the
+ *                         diagonal that the mix stage reads are zero; blocks of entries lying
+ *                         entirely above the diagonal are left unwritten (never read)
+ *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed.
+ *                         Left unwritten when causal and n == chunk (the one chunk's prefix is
+ *                         empty, so the global term vanishes and its stages launch nothing)
  *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin)
  *   CARRY   [B, NG, e, s] per sequence, the sum of K_linᵀ V over each group of consecutive
  *                         chunks, / n, transposed. The states stage splits the n/c chunks of a
@@ -132,7 +136,8 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
  * 1 proj   : X W_u|W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
  * 2 scores : per chunk relu(Q_quad K_quadᵀ / c)², masked when causal ("Mixed Chunk", local term)
  * 3 states : K_linᵀ V summed over the chunks of each chunk group: the exclusive prefix inside the
- *            group for every chunk (causal) and the group total, times 1/n
+ *            group for every chunk (causal) and the group total, times 1/n; launches nothing
+ *            when causal and n == chunk
  * 4 carry  : adds the totals of earlier groups to every chunk's state (causal), or sums the group
  *            totals into the sequence's state (non-causal); launches nothing with one group
  * 5 mix    : per chunk P V + Q_lin S / n, gated by U ("Mixed Chunk", both terms and the gate)
