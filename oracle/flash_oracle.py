@@ -39,7 +39,12 @@ Readings taken where the pages are silent, garbled or in conflict
 * Causal local mask: entries with key index j > query index i (inside the chunk) are zero; the
   diagonal is kept.
 * Head order in gamma/beta rows: Q_quad, K_quad, Q_lin, K_lin.
-* The layer has no bias, norm, residual, dropout or position encoding.
+* The layer has no bias, norm, residual or dropout, and by default no position encoding.
+* Optional rotary position embedding (``rope_base``): the FLASH page ("Experimental Analysis")
+  says every model of the paper uses RoPE but does not define it. Reading: the standard rotary
+  form, interleaved pairs (x_{2k}, x_{2k+1}) of a head vector at position m rotated by the angle
+  m·θ_k with θ_k = base^{-2k/s}; m is the token's index inside its sequence (0-based); it is
+  applied to all four heads after their scale and offset.
 
 Decoding, one token at a time
 -----------------------------
@@ -76,6 +81,7 @@ __all__ = [
     "gau_forward",
     "glu_forward",
     "quad_gau_attention",
+    "rotary",
     "decode_init",
     "decode_step",
     "decode_sequence",
@@ -113,6 +119,25 @@ def scale_offset_heads(Z, gamma, beta):
     Returns the tuple (Q_quad, K_quad, Q_lin, K_lin), each shaped like Z."""
     Z, gamma, beta = _f64(Z), _f64(gamma), _f64(beta)
     return tuple(Z * gamma[h] + beta[h] for h in range(4))
+
+
+def rotary(x, positions, base):
+    """Rotary position embedding of head vectors x [..., n, s] (s even) at integer positions [n]:
+    each pair (x_{2k}, x_{2k+1}) is rotated by the angle m·θ_k, θ_k = base^{-2k/s} (the standard
+    rotary form; the FLASH page names RoPE in "Experimental Analysis" without defining it)."""
+    x = _f64(x)
+    s = x.shape[-1]
+    if s % 2:
+        raise ValueError("rotary embedding needs an even head size")
+    k = np.arange(s // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * k / s)
+    angle = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    cos, sin = np.cos(angle), np.sin(angle)
+    even, odd = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = even * cos - odd * sin
+    out[..., 1::2] = even * sin + odd * cos
+    return out
 
 
 def _chunks(n, chunk):
@@ -212,13 +237,14 @@ def combine(U, Vq, Vl, W_o):
 
 
 def flash_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal,
-                  local_norm="c2", global_norm="n", return_intermediates=False):
+                  local_norm="c2", global_norm="n", return_intermediates=False, rope_base=None):
     """One FLASH layer forward in the chunked form, steps in the order of "Mixed Chunk".
 
     X is [B, n, d] (a 2-D [n, d] input is treated as B = 1). Returns O [B, n, d] in float64, and
     with ``return_intermediates`` also a dict of U, V, Z, the four heads, the local weights P
     [B, G, c, c], the chunk summaries T and the prefix states S [B, G, s, e], V̂_quad, V̂_lin and
-    the gated product Y = U ⊙ (V̂_quad + V̂_lin).
+    the gated product Y = U ⊙ (V̂_quad + V̂_lin). With ``rope_base`` the four heads are rotated
+    (``rotary``) at their positions 0..n-1 before any use.
     """
     X = _f64(X)
     squeeze = X.ndim == 2
@@ -227,6 +253,9 @@ def flash_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal,
     n = X.shape[1]
     U, V, Z = project(X, W_u, W_v, W_z)
     Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    if rope_base is not None:
+        pos = np.arange(n)
+        Qq, Kq, Ql, Kl = (rotary(h, pos, rope_base) for h in (Qq, Kq, Ql, Kl))
     Vq, P = local_quad(Qq, Kq, V, chunk, causal, local_norm=local_norm, return_weights=True)
     T = chunk_states(Kl, V, chunk)
     S = prefix_states(T, causal)
@@ -245,7 +274,7 @@ def flash_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal,
 # Independent formulations used to pin the chunked oracle.
 # ---------------------------------------------------------------------------------------------
 
-def brute_force_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal):
+def brute_force_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_base=None):
     """The same layer with both attention matrices materialised as full n×n arrays.
 
     "Mixed Chunk" says the local term is attention restricted to the block diagonal (masked to the
@@ -253,13 +282,16 @@ def brute_force_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal):
     Q_lin, K_lin in R^{n×s}; for a decoder only keys in earlier chunks are visible. Here
     A_quad[i, j] = relu(q_i·k_j / c)² when i, j share a chunk (and j <= i if causal),
     A_lin[i, j] = ql_i·kl_j / n when chunk(j) < chunk(i) (causal) or always (non-causal), and
-    O = (U ⊙ (A_quad + A_lin) V) W_o, the form of equation (mix).
+    O = (U ⊙ (A_quad + A_lin) V) W_o, the form of equation (mix). ``rope_base`` rotates the
+    heads as in flash_forward.
     """
     X = _f64(X)
     B, n, _ = X.shape
     _chunks(n, chunk)
     U, V, Z = project(X, W_u, W_v, W_z)
     Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    if rope_base is not None:
+        Qq, Kq, Ql, Kl = (rotary(h, np.arange(n), rope_base) for h in (Qq, Kq, Ql, Kl))
     idx = np.arange(n)
     cid = idx // chunk
     same = cid[:, None] == cid[None, :]
@@ -355,7 +387,7 @@ def decode_init(B, s, e, chunk):
 
 
 def decode_step(state, x, t, n, W_u, W_v, W_z, gamma, beta, W_o, chunk,
-                local_norm="c2", global_norm="n"):
+                local_norm="c2", global_norm="n", rope_base=None):
     """Output of token t (0-based, the same position in every sequence) of the causal layer, given
     the state left by tokens 0..t-1; updates the state in place. x is [B, d]; returns o [B, d].
 
@@ -365,11 +397,14 @@ def decode_step(state, x, t, n, W_u, W_v, W_z, gamma, beta, W_o, chunk,
     over the earlier chunks only (``global_norm="count"`` divides by the g·c tokens summed
     instead, 0 in the first chunk); gate and output projection. After the chunk's last token,
     S += K_lin_gᵀ V_g (the state update of the RNN form of csdn section 1.4, a chunk at a time).
+    ``rope_base`` rotates the heads at position t, as flash_forward does.
     """
     x = _f64(x)
     i, g = t % chunk, t // chunk
     U, V, Z = project(x, W_u, W_v, W_z)
     Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    if rope_base is not None:
+        Qq, Kq, Ql, Kl = (rotary(h[:, None, :], [t], rope_base)[:, 0] for h in (Qq, Kq, Ql, Kl))
     s = Z.shape[-1]
     state["Kq"][:, i] = Kq
     state["Kl"][:, i] = Kl
