@@ -194,7 +194,7 @@ def decode_measure(inp, dtype, torch, fg, dev, cpu_seconds):
 
     def step(t):
         rc = fg.decode_step_raw(xs[t].data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
-                                beta.data_ptr(), c, t, n, B, d, e, s, dt, o.data_ptr(),
+                                beta.data_ptr(), c, t, n, 0.0, B, d, e, s, dt, o.data_ptr(),
                                 state.buf.data_ptr(), state.buf.numel(), stream)
         if rc != fg.OK:
             raise fg.FlashGauError(rc, "flash_gau_decode_step")

@@ -176,6 +176,26 @@ template <> struct UVec<F32> {
   }
 };
 
+// Rotary position embedding (the standard rotary form: the pair (x_{2k}, x_{2k+1}) of a head
+// vector at position m turns by the angle m·θ_k, θ_k = base^{-2k/s}). rope_angle gives cos and
+// sin of m·θ_k in double precision (positions reach 2^31, where a float angle has lost its
+// phase); rope_apply rotates one pair member: x is feature j of the head, xp its partner j ^ 1.
+__device__ __forceinline__ double rope_theta(int j, int s, double log2_base) {
+  return exp2(-double(2 * (j >> 1)) / double(s) * log2_base);
+}
+__device__ __forceinline__ void rope_angle(int64_t m, double theta, double* cs, double* sn) {
+  sincos(double(m) * theta, sn, cs);
+}
+__device__ __forceinline__ float rope_apply(float x, float xp, int j, double cs, double sn) {
+  return (j & 1) ? float(double(xp) * sn + double(x) * cs) : float(double(x) * cs - double(xp) * sn);
+}
+
+// Value of the neighbouring lane l ^ 1 (DPP quad permutation [1, 0, 3, 2]); every lane of the
+// wave must execute it.
+__device__ __forceinline__ float swap_adjacent_lanes(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
 // A block of consecutive rows of a row-major tensor behind a buffer descriptor that covers
 // exactly its valid rows: reads past them (or at offset kOutOfRange) return zeros.
 struct Rows {

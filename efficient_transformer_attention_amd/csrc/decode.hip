@@ -24,6 +24,7 @@
 // and at t = 0 a fill kernel clears S first.
 
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 
@@ -70,6 +71,9 @@ struct DecProjArgs {
   typename E::T* Ql;           // [B, s]
   typename E::T* Klc;          // [B, c, s]
   int B, d, e, s, c, i;
+  int64_t t;         // position of the token
+  int rope;          // rotate the four heads (rotary position embedding)
+  double log2_base;  // log2 of the rotary base
 };
 
 // grid (ceil((2e+s) / 64), ceil(B / 16)), 256 threads: wave w owns weight rows 64 x + 16 w.
@@ -98,11 +102,25 @@ __global__ __launch_bounds__(256) void dec_proj_kernel(DecProjArgs<E> p) {
     store4(p.Vc + (int64_t(b) * p.c + p.i) * p.e + (j - p.e), y[0], y[1], y[2], y[3]);
   } else {
     const int jj = j - 2 * p.e;
-    float h[4][4];
+    float h[4][4];  // [head][feature jj + r]
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) h[k][r] = fmaf(p.gamma[k * p.s + jj + r], y[r], p.beta[k * p.s + jj + r]);
+    if (p.rope) {
+      // jj % 4 == 0: the lane holds the rotary pairs (jj, jj+1) and (jj+2, jj+3) itself
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        double cs, sn;
+        rope_angle(p.t, rope_theta(jj + r, p.s, p.log2_base), &cs, &sn);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = h[k][r], x1 = h[k][r + 1];
+          h[k][r] = rope_apply(x0, x1, jj + r, cs, sn);
+          h[k][r + 1] = rope_apply(x1, x0, jj + r + 1, cs, sn);
+        }
+      }
+    }
     const int64_t row = int64_t(b) * p.s + jj;
     const int64_t crow = (int64_t(b) * p.c + p.i) * p.s + jj;
     store4(p.Qq + row, h[0][0], h[0][1], h[0][2], h[0][3]);
@@ -338,8 +356,8 @@ int make_decode_plan(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
 
 template <class E>
 int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_t wo_off,
-                  const float* gamma, const float* beta, int64_t t, int64_t n, void* o, char* st,
-                  hipStream_t stream) {
+                  const float* gamma, const float* beta, int64_t t, int64_t n, float rope_base,
+                  void* o, char* st, hipStream_t stream) {
   using T = typename E::T;
   const int B = int(pl.B), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
   const int i = int(t % pl.c);
@@ -361,7 +379,8 @@ int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_
   }
   {
     DecProjArgs<E> a{reinterpret_cast<const T*>(x), WcatT, gamma, beta, U, Vc, Qq, Kqc, Ql, Klc,
-                     B, d, e, s, c, i};
+                     B, d, e, s, c, i, t, rope_base > 0.0f ? 1 : 0,
+                     rope_base > 0.0f ? log2(double(rope_base)) : 0.0};
     hipLaunchKernelGGL(dec_proj_kernel<E>, dim3(unsigned(cdiv(pl.ncols, 64)), unsigned(cdiv(B, 16))),
                        dim3(256), 0, stream, a);
   }
@@ -412,20 +431,21 @@ int flashgau_decode_state_offsets(int64_t B, int64_t d, int64_t e, int64_t s, in
 
 int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes,
                           const float* gamma, const float* beta, int64_t chunk, int64_t t,
-                          int64_t n, int64_t B, int64_t d, int64_t e, int64_t s,
+                          int64_t n, float rope_base, int64_t B, int64_t d, int64_t e, int64_t s,
                           flashgau_dtype dtype, void* o, void* state, size_t state_bytes,
                           void* hip_stream) {
   DecodePlan pl;
   int rc = make_decode_plan(B, d, e, s, chunk, dtype, &pl);
   if (rc != FLASHGAU_OK) return rc;
   if (n < 1 || t < 0 || t >= n) return FLASHGAU_ERR_BAD_SHAPE;
+  if (!(rope_base >= 0.0f) || !std::isfinite(rope_base)) return FLASHGAU_ERR_BAD_SHAPE;
   size_t wo_off = 0, packed_total = 0;
   rc = packed_plan(d, e, s, dtype, &wo_off, &packed_total);
   if (rc != FLASHGAU_OK) return rc;
   if (B == 0) return FLASHGAU_OK;
   if (!x || !packed || !gamma || !beta || !o || !state) return FLASHGAU_ERR_NULL_PTR;
-  if (misaligned(x) || misaligned(packed) || misaligned(gamma) || misaligned(beta) ||
-      misaligned(o) || misaligned(state))
+  if (misaligned(x) || misaligned(packed) || misaligned(o) || misaligned(state) ||
+      (reinterpret_cast<uintptr_t>(gamma) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u))
     return FLASHGAU_ERR_MISALIGNED;
   if (packed_bytes < packed_total || state_bytes < pl.total) return FLASHGAU_ERR_WORKSPACE;
   const size_t nx = size_t(B * d * pl.esz), no = nx, ng = size_t(4 * s * 4);
@@ -439,8 +459,8 @@ int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes
   char* st = reinterpret_cast<char*>(state);
   const char* pk = reinterpret_cast<const char*>(packed);
   return dtype == FLASHGAU_BF16
-             ? launch_decode<BF16>(pl, x, pk, wo_off, gamma, beta, t, n, o, st, stream)
-             : launch_decode<F32>(pl, x, pk, wo_off, gamma, beta, t, n, o, st, stream);
+             ? launch_decode<BF16>(pl, x, pk, wo_off, gamma, beta, t, n, rope_base, o, st, stream)
+             : launch_decode<F32>(pl, x, pk, wo_off, gamma, beta, t, n, rope_base, o, st, stream);
 }
 
 }  // extern "C"

@@ -29,6 +29,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "flashgau.h"
 #include "common.h"
@@ -343,6 +344,9 @@ struct ProjArgs {
   const float* gamma;          // [4, s]
   const float* beta;           // [4, s]
   int M, d, e, s, c;
+  int n;             // sequence length: a token's position is its row modulo n
+  int rope;          // rotate the four heads (rotary position embedding)
+  double log2_base;  // log2 of the rotary base
 };
 
 template <class E, int BM, int BN, int WM, int WN, int NS>
@@ -402,10 +406,16 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   }
   g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
     const int row = m0 + r, col = n0 + cl;
-    if (row >= p.M || col >= ncols) return;
-    float y[4];
+    float y[4], yp[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) y[k] = silu(v[k]);
+    if (p.rope) {
+      // the rotary partner (feature col ^ 1, same four tokens) sits in the neighbouring lane;
+      // exchanged before any lane leaves
+#pragma unroll
+      for (int k = 0; k < 4; ++k) yp[k] = swap_adjacent_lanes(y[k]);
+    }
+    if (row >= p.M || col >= ncols) return;
     const int64_t bg = row / c, t = row % c;  // c % 8 == 0: rows row..row+3 share a chunk
     if (col < e) {
 #pragma unroll
@@ -414,17 +424,35 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
       store4(p.Vt + (bg * e + (col - e)) * c + t, y[0], y[1], y[2], y[3]);
     } else {
       const int j = col - 2 * e;
-      const float g0 = p.gamma[j], g1 = p.gamma[s + j], g2 = p.gamma[2 * s + j], g3 = p.gamma[3 * s + j];
-      const float b0 = p.beta[j], b1 = p.beta[s + j], b2 = p.beta[2 * s + j], b3 = p.beta[3 * s + j];
+      float h[4][4];  // [head][token]
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float gq = p.gamma[q * s + j], bq = p.beta[q * s + j];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[q][k] = fmaf(gq, y[k], bq);
+      }
+      if (p.rope) {
+        const int jp = j ^ 1;
+        const double theta = rope_theta(j, s, p.log2_base);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          double cs, sn;
+          rope_angle((row + k) % p.n, theta, &cs, &sn);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float partner = fmaf(p.gamma[q * s + jp], yp[k], p.beta[q * s + jp]);
+            h[q][k] = rope_apply(h[q][k], partner, j, cs, sn);
+          }
+        }
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t o = int64_t(row + k) * s + j;
-        p.Qq[o] = from_f32<E>(fmaf(g0, y[k], b0));
-        p.Kq[o] = from_f32<E>(fmaf(g1, y[k], b1));
-        p.Ql[o] = from_f32<E>(fmaf(g2, y[k], b2));
+        p.Qq[o] = from_f32<E>(h[0][k]);
+        p.Kq[o] = from_f32<E>(h[1][k]);
+        p.Ql[o] = from_f32<E>(h[2][k]);
       }
-      store4(p.Klt + (bg * s + j) * c + t, fmaf(g3, y[0], b3), fmaf(g3, y[1], b3),
-             fmaf(g3, y[2], b3), fmaf(g3, y[3], b3));
+      store4(p.Klt + (bg * s + j) * c + t, h[3][0], h[3][1], h[3][2], h[3][3]);
     }
   });
 }
@@ -950,8 +978,8 @@ void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* 
 
 template <class E>
 int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
-               const float* gamma, const float* beta, const void* W_o, int causal, void* O,
-               char* ws, hipStream_t stream, hipEvent_t const* events) {
+               const float* gamma, const float* beta, const void* W_o, int causal, float rope_base,
+               void* O, char* ws, hipStream_t stream, hipEvent_t const* events) {
   using T = typename E::T;
   using S = Shapes<E>;
   // events (optional): events[i] is recorded right before stage i is launched, and
@@ -980,7 +1008,8 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT, U, Vt, Qq, Kq, Ql, Klt, gamma, beta,
-                  M, d, e, s, c};
+                  M, d, e, s, c, int(pl.n), rope_base > 0.0f ? 1 : 0,
+                  rope_base > 0.0f ? log2(double(rope_base)) : 0.0};
     const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
     hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
@@ -1060,10 +1089,11 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
                         const float* gamma, const float* beta, const void* W_o, int64_t chunk,
                         int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                         flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
-                        void* hip_stream, hipEvent_t const* events) {
+                        void* hip_stream, hipEvent_t const* events, float rope_base) {
   Plan pl;
   const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &pl);
   if (rc != FLASHGAU_OK) return rc;
+  if (!(rope_base >= 0.0f) || !std::isfinite(rope_base)) return FLASHGAU_ERR_BAD_SHAPE;
   if (pl.M == 0) return FLASHGAU_OK;
   if (!X || !W_u || !W_v || !W_z || !gamma || !beta || !W_o || !O || !workspace)
     return FLASHGAU_ERR_NULL_PTR;
@@ -1085,10 +1115,10 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == FLASHGAU_BF16)
-    return launch_all<BF16>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, O, ws, stream,
-                            events);
-  return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, O, ws, stream,
-                         events);
+    return launch_all<BF16>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
+                            ws, stream, events);
+  return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
+                         ws, stream, events);
 }
 
 int flashgau_state_groups(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
@@ -1107,7 +1137,17 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
                       void* hip_stream) {
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
-                      workspace, workspace_bytes, hip_stream, nullptr);
+                      workspace, workspace_bytes, hip_stream, nullptr, 0.0f);
+}
+
+int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                           const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                           int causal, float rope_base, int64_t B, int64_t n, int64_t d, int64_t e,
+                           int64_t s, flashgau_dtype dtype, void* O, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  if (!(rope_base > 0.0f)) return FLASHGAU_ERR_BAD_SHAPE;
+  return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                      workspace, workspace_bytes, hip_stream, nullptr, rope_base);
 }
 
 int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, const void* W_z,
@@ -1122,7 +1162,7 @@ int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, con
     if (!stage_events[i]) return FLASHGAU_ERR_NULL_PTR;
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, hip_stream,
-                      reinterpret_cast<hipEvent_t const*>(stage_events));
+                      reinterpret_cast<hipEvent_t const*>(stage_events), 0.0f);
 }
 
 int flashgau_packed_weights_size(int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,
@@ -1165,7 +1205,9 @@ const char* flashgau_strerror(int code) {
   switch (code) {
     case FLASHGAU_OK: return "success";
     case FLASHGAU_ERR_NULL_PTR: return "a required pointer is NULL";
-    case FLASHGAU_ERR_BAD_SHAPE: return "bad shape (size < 1, n % chunk != 0, or a size overflows)";
+    case FLASHGAU_ERR_BAD_SHAPE:
+      return "bad shape or argument (size < 1, n % chunk != 0, a size overflows, position or "
+             "rotary base out of range)";
     case FLASHGAU_ERR_UNSUPPORTED: return "unsupported (dtype, or d, e, s, chunk not a multiple of 8)";
     case FLASHGAU_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
     case FLASHGAU_ERR_WORKSPACE: return "workspace smaller than flashgau_workspace_size()";

@@ -33,7 +33,8 @@ WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y"
 DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
 
 EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_state_groups",
-           "flash_gau_forward", "flash_gau_forward_timed", "flashgau_packed_weights_size",
+           "flash_gau_forward", "flash_gau_forward_rope", "flash_gau_forward_timed",
+           "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
            "flash_gau_decode_step", "flashgau_strerror")
 
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_forward.restype = ctypes.c_int
+    L.flash_gau_forward_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, ctypes.c_float,
+                                         i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
+    L.flash_gau_forward_rope.restype = ctypes.c_int
     L.flash_gau_forward_timed.argtypes = L.flash_gau_forward.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
     L.flash_gau_forward_timed.restype = ctypes.c_int
     L.flashgau_packed_weights_size.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
@@ -79,8 +83,8 @@ def lib() -> ctypes.CDLL:
     L.flashgau_decode_state_size.restype = ctypes.c_int
     L.flashgau_decode_state_offsets.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.POINTER(sz)]
     L.flashgau_decode_state_offsets.restype = ctypes.c_int
-    L.flash_gau_decode_step.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, i64, i64, i64, i64,
-                                        ctypes.c_int, vp, vp, sz, vp]
+    L.flash_gau_decode_step.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, ctypes.c_float, i64, i64,
+                                        i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_decode_step.restype = ctypes.c_int
     L.flashgau_strerror.argtypes = [ctypes.c_int]
     L.flashgau_strerror.restype = ctypes.c_char_p
@@ -123,6 +127,14 @@ def forward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s
                                    B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream)
 
 
+def forward_rope_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_base, B, n, d, e, s,
+                     dtype, O, workspace, workspace_bytes, stream) -> int:
+    """Direct call of flash_gau_forward_rope with integer addresses; returns the library's code."""
+    return lib().flash_gau_forward_rope(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
+                                        float(rope_base), B, n, d, e, s, dtype, O, workspace,
+                                        workspace_bytes, stream)
+
+
 def forward_timed_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, stream, events) -> int:
     """flash_gau_forward_timed with integer addresses; ``events`` is a sequence of
@@ -143,11 +155,12 @@ def _dtype_code(t):
 
 
 def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=None, workspace=None,
-                      stream=None):
+                      stream=None, rope_base=None):
     """One FLASH layer forward on the GPU. X [B, n, d]; W_u, W_v [d, e]; W_z [d, s]; gamma, beta
     [4, s] float32 (heads Q_quad, K_quad, Q_lin, K_lin); W_o [e, d]. X and the weights share one
     dtype (bfloat16 or float32). Returns O [B, n, d] of that dtype. ``workspace`` (uint8, on the
-    same device) receives the intermediates; it is allocated when not given."""
+    same device) receives the intermediates; it is allocated when not given. ``rope_base`` (e.g.
+    10000.0) selects flash_gau_forward_rope: the heads are rotated at their positions."""
     import torch
     B, n, d = X.shape
     e = W_u.shape[1]
@@ -175,11 +188,16 @@ def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=Non
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = forward_raw(X.data_ptr(), W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), gamma.data_ptr(),
-                     beta.data_ptr(), W_o.data_ptr(), chunk, causal, B, n, d, e, s, dt,
-                     out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    ptrs = (X.data_ptr(), W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), gamma.data_ptr(),
+            beta.data_ptr(), W_o.data_ptr())
+    if rope_base is None:
+        rc = forward_raw(*ptrs, chunk, causal, B, n, d, e, s, dt, out.data_ptr(), workspace.data_ptr(),
+                         workspace.numel(), stream)
+    else:
+        rc = forward_rope_raw(*ptrs, chunk, causal, rope_base, B, n, d, e, s, dt, out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), stream)
     if rc != OK:
-        raise FlashGauError(rc, "flash_gau_forward")
+        raise FlashGauError(rc, "flash_gau_forward" if rope_base is None else "flash_gau_forward_rope")
     return out
 
 
@@ -240,11 +258,11 @@ def pack_weights_raw(W_u, W_v, W_z, W_o, d, e, s, dtype, packed, packed_bytes, s
     return lib().flashgau_pack_weights(W_u, W_v, W_z, W_o, d, e, s, dtype, packed, packed_bytes, stream)
 
 
-def decode_step_raw(x, packed, packed_bytes, gamma, beta, chunk, t, n, B, d, e, s, dtype, o, state,
-                    state_bytes, stream) -> int:
+def decode_step_raw(x, packed, packed_bytes, gamma, beta, chunk, t, n, rope_base, B, d, e, s, dtype, o,
+                    state, state_bytes, stream) -> int:
     """Direct call of flash_gau_decode_step with integer addresses; returns the library's code."""
-    return lib().flash_gau_decode_step(x, packed, packed_bytes, gamma, beta, chunk, t, n, B, d, e, s,
-                                       dtype, o, state, state_bytes, stream)
+    return lib().flash_gau_decode_step(x, packed, packed_bytes, gamma, beta, chunk, t, n, float(rope_base),
+                                       B, d, e, s, dtype, o, state, state_bytes, stream)
 
 
 def pack_weights(W_u, W_v, W_z, W_o, stream=None):
@@ -301,9 +319,11 @@ class DecodeState:
         return views
 
 
-def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, stream=None):
+def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, stream=None,
+                          rope_base=0.0):
     """One causal decoding step on the GPU: x [B, d] holds token t of each sequence; returns
-    o [B, d]. ``packed`` comes from pack_weights, ``state`` is a DecodeState advanced in place."""
+    o [B, d]. ``packed`` comes from pack_weights, ``state`` is a DecodeState advanced in place.
+    ``rope_base`` > 0 rotates the heads at position t (as flash_gau_forward(rope_base=...))."""
     import torch
     B, d = x.shape
     if (B, d) != (state.B, state.d) or _dtype_code(x.dtype) != state.dt:
@@ -315,7 +335,7 @@ def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, 
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     rc = decode_step_raw(x.data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
-                         beta.data_ptr(), chunk, t, n, B, d, state.e, state.s, state.dt,
+                         beta.data_ptr(), chunk, t, n, rope_base, B, d, state.e, state.s, state.dt,
                          out.data_ptr(), state.buf.data_ptr(), state.buf.numel(), stream)
     if rc != OK:
         raise FlashGauError(rc, "flash_gau_decode_step")

@@ -48,7 +48,8 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
 /* Return codes. */
 #define FLASHGAU_OK 0
 #define FLASHGAU_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
-#define FLASHGAU_ERR_BAD_SHAPE (-2)   /* negative/zero size, n % chunk != 0, or a size overflows */
+#define FLASHGAU_ERR_BAD_SHAPE (-2)   /* negative/zero size, n % chunk != 0, a size overflows, or a
+                                       position / rotary base out of range */
 #define FLASHGAU_ERR_UNSUPPORTED (-3) /* unknown dtype, or d, e, s, chunk not a multiple of 8 */
 #define FLASHGAU_ERR_MISALIGNED (-4)  /* a tensor pointer is not 16-byte aligned */
 #define FLASHGAU_ERR_WORKSPACE (-5)   /* workspace_bytes smaller than flashgau_workspace_size() */
@@ -129,6 +130,20 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                       flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
                       void* hip_stream);
+
+/* flash_gau_forward with a rotary position embedding of the four heads. The FLASH page
+ * ("Experimental Analysis") says the paper's models use RoPE but does not define it; the reading
+ * taken is the standard rotary form: after the scale and offset, the pairs (h_{2k}, h_{2k+1}) of
+ * each head vector of the token at position m (its index inside its sequence, 0-based) are
+ * rotated by the angle m·θ_k, θ_k = rope_base^(-2k/s) (s is a multiple of 8, so even). The
+ * angles are evaluated in double precision. rope_base must be > 0 and finite (10000 is the usual
+ * value); every other argument, and the workspace contents (with rotated heads), are as for
+ * flash_gau_forward. */
+int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                           const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                           int causal, float rope_base, int64_t B, int64_t n, int64_t d, int64_t e,
+                           int64_t s, flashgau_dtype dtype, void* O, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
 
 /* Stages of flash_gau_forward, in launch order (one kernel each). */
 #define FLASHGAU_NUM_STAGES 7
@@ -224,6 +239,8 @@ int flashgau_decode_state_offsets(int64_t B, int64_t d, int64_t e, int64_t s, in
  *   packed, packed_bytes: weights packed by flashgau_pack_weights (same d, e, s, dtype)
  *   gamma, beta [4, s] fp32, device (rows Q_quad, K_quad, Q_lin, K_lin)
  *   chunk  c; t the position (0 <= t < n); n the normalising length of the global term
+ *   rope_base: 0 for no position encoding; > 0 rotates the four heads at position t exactly as
+ *          flash_gau_forward_rope does (the same base must be used for every step of a state)
  *   o      [B, d]  dtype, device; fully overwritten
  *   state, state_bytes: the decoding state (>= flashgau_decode_state_size bytes) left by the step
  *          at t - 1 of the same sequences (any contents at t = 0); updated in place
@@ -233,7 +250,7 @@ int flashgau_decode_state_offsets(int64_t B, int64_t d, int64_t e, int64_t s, in
  * is too small). */
 int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes,
                           const float* gamma, const float* beta, int64_t chunk, int64_t t,
-                          int64_t n, int64_t B, int64_t d, int64_t e, int64_t s,
+                          int64_t n, float rope_base, int64_t B, int64_t d, int64_t e, int64_t s,
                           flashgau_dtype dtype, void* o, void* state, size_t state_bytes,
                           void* hip_stream);
 

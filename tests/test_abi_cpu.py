@@ -211,8 +211,8 @@ def _dcall(t=3, n=16, **over):
                 o=base + (4 << 30), state=base + (5 << 30), packed_bytes=pk, state_bytes=st)
     ptrs.update(over)
     return fg.decode_step_raw(ptrs["x"], ptrs["packed"], ptrs["packed_bytes"], ptrs["gamma"],
-                              ptrs["beta"], c, t, n, B, d, e, s, fg.BF16, ptrs["o"], ptrs["state"],
-                              ptrs["state_bytes"], None)
+                              ptrs["beta"], c, t, n, ptrs.get("rope_base", 0.0), B, d, e, s, fg.BF16,
+                              ptrs["o"], ptrs["state"], ptrs["state_bytes"], None)
 
 
 @pytest.mark.parametrize("t,n", [(16, 16), (-1, 16), (0, 0), (20, 16)])
@@ -248,7 +248,8 @@ def test_decode_aliasing_rejected(over):
 
 
 def test_decode_empty_batch_succeeds_without_pointers():
-    rc = fg.decode_step_raw(None, None, 0, None, None, 8, 0, 16, 0, 64, 96, 24, fg.BF16, None, None, 0, None)
+    rc = fg.decode_step_raw(None, None, 0, None, None, 8, 0, 16, 0.0, 0, 64, 96, 24, fg.BF16, None, None, 0,
+                            None)
     assert rc == fg.OK
 
 
@@ -261,3 +262,19 @@ def test_pack_weights_validation():
     assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, base + 8 + (4 << 30), pk, None) == fg.ERR_MISALIGNED
     assert fg.pack_weights_raw(*w, 64, 96, 24, fg.BF16, base + 256, pk, None) == fg.ERR_ALIASING
     assert fg.pack_weights_raw(*w, 64, 100, 24, fg.BF16, base + (4 << 30), pk, None) == fg.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("base", [-1.0, float("nan"), float("inf")])
+def test_decode_rotary_base_validated(base):
+    assert _dcall(rope_base=base) == fg.ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("base", [0.0, -5.0, float("nan"), float("inf")])
+def test_forward_rope_base_validated(base):
+    base_ptr = 1 << 40
+    B, n, d, e, s, c = 1, 128, 64, 128, 128, 64
+    ws = fg.workspace_size(B, n, d, e, s, c, True, fg.BF16)
+    rc = fg.forward_rope_raw(base_ptr, base_ptr + (1 << 30), base_ptr + (2 << 30), base_ptr + (3 << 30),
+                             base_ptr + (4 << 30), base_ptr + (5 << 30), base_ptr + (6 << 30), c, 1, base,
+                             B, n, d, e, s, fg.BF16, base_ptr + (7 << 30), base_ptr + (8 << 30), ws, None)
+    assert rc == fg.ERR_BAD_SHAPE
