@@ -16,7 +16,9 @@ For a causal workload the line also carries a "decode" object: the same batch an
 decoded one token per sequence per step (flash_gau_decode_step), timed over one whole chunk of
 positions (c .. 2c-1, the last step folding the chunk into the state) after chunk 0 has filled the
 state untimed, with its HBM roofline (algorithmic bytes per step, see decode_bytes) and the
-oracle's decode step timed on the host.
+oracle's decode step timed on the host. Two more objects time the same layer with the rotary
+embedding (flash_gau_forward_rope) and compare FLASH-Quad (chunk = n: one quadratic chunk, no
+global term) with FLASH (the workload's chunk) on longer causal sequences of the same width.
 """
 
 import argparse
@@ -240,6 +242,50 @@ def decode_measure(inp, dtype, torch, fg, dev, cpu_seconds):
     return rec
 
 
+def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None, steps=10, seed=0):
+    """Average time (us) of one forward call (flash_gau_forward, or flash_gau_forward_rope when
+    rope_base is given) over `steps` calls after 3 warm-up calls, between two HIP events."""
+    from efficient_transformer_attention_amd import inputs as gen
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    X, Wu, Wv, Wz, Wo = (up(a) for a in (inp.X, inp.W_u, inp.W_v, inp.W_z, inp.W_o))
+    gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, n, d), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ptrs = (X.data_ptr(), Wu.data_ptr(), Wv.data_ptr(), Wz.data_ptr(), gamma.data_ptr(),
+            beta.data_ptr(), Wo.data_ptr())
+
+    def call():
+        if rope_base is None:
+            rc = fg.forward_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
+                                nbytes, stream)
+        else:
+            rc = fg.forward_rope_raw(*ptrs, c, causal, rope_base, B, n, d, e, s, dt, O.data_ptr(),
+                                     ws.data_ptr(), nbytes, stream)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "forward")
+
+    for _ in range(3):
+        call()
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[0]), ctypes.c_void_p(stream))
+    for _ in range(steps):
+        call()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    us = ev.ms(ev.handles[0], ev.handles[1]) * 1e3 / steps
+    ev.close()
+    return us
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +296,8 @@ def main():
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the causal decoding measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the rotary-embedding and FLASH-Quad (chunk = n) timings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -364,6 +412,21 @@ def main():
     if causal and not args.no_decode:
         decode = decode_measure(inp, dtype, torch, fg, dev, min(args.cpu_seconds, 5.0))
 
+    rope = quad = None
+    if not args.no_extras:
+        print("[bench] rotary embedding and FLASH-Quad timings", file=sys.stderr, flush=True)
+        us_rope = time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=10000.0)
+        us_plain = time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype)
+        rope = {"workload": name, "rope_base": 10000.0, "us_per_step": round(us_rope, 1),
+                "tokens_per_s": round(B * n / (us_rope * 1e-6), 1),
+                "us_per_step_without": round(us_plain, 1)}
+        quad = []
+        for (qB, qn) in ((2, 8192), (1, 16384)):
+            us_q = time_forward(fg, torch, dev, qB, qn, d, e, s, qn, True, dtype, steps=5)
+            us_f = time_forward(fg, torch, dev, qB, qn, d, e, s, c, True, dtype, steps=5)
+            quad.append({"batch": qB, "seq_len": qn, "flash_quad_chunk_eq_n_us": round(us_q, 1),
+                         f"flash_chunk_{c}_us": round(us_f, 1), "flash_speedup": round(us_q / us_f, 2)})
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -388,6 +451,8 @@ def main():
         "cpu_baseline": cpu,
         "max_rel_err_seq0": max_rel_err,
         "decode": decode,
+        "rope": rope,
+        "flash_vs_flash_quad": quad,
     }
     print(json.dumps(line), flush=True)
 

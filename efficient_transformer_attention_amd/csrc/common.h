@@ -177,17 +177,22 @@ template <> struct UVec<F32> {
 };
 
 // Rotary position embedding (the standard rotary form: the pair (x_{2k}, x_{2k+1}) of a head
-// vector at position m turns by the angle m·θ_k, θ_k = base^{-2k/s}). rope_angle gives cos and
-// sin of m·θ_k in double precision (positions reach 2^31, where a float angle has lost its
-// phase); rope_apply rotates one pair member: x is feature j of the head, xp its partner j ^ 1.
+// vector at position m turns by the angle m·θ_k, θ_k = base^{-2k/s}). Positions reach 2^31,
+// where a float angle has lost its phase, so θ_k, m·θ_k and its reduction to [0, 2π) are
+// evaluated in double precision; cos and sin of the reduced angle are taken in float.
+// rope_apply rotates one pair member: x is feature j of the head, xp its partner j ^ 1.
 __device__ __forceinline__ double rope_theta(int j, int s, double log2_base) {
   return exp2(-double(2 * (j >> 1)) / double(s) * log2_base);
 }
-__device__ __forceinline__ void rope_angle(int64_t m, double theta, double* cs, double* sn) {
-  sincos(double(m) * theta, sn, cs);
+__device__ __forceinline__ void rope_angle(int64_t m, double theta, float* cs, float* sn) {
+  constexpr double kTwoPi = 6.283185307179586476925;
+  constexpr double kInvTwoPi = 0.159154943091895335769;
+  const double a = double(m) * theta;
+  const double r = fma(-kTwoPi, floor(a * kInvTwoPi), a);
+  sincosf(float(r), sn, cs);
 }
-__device__ __forceinline__ float rope_apply(float x, float xp, int j, double cs, double sn) {
-  return (j & 1) ? float(double(xp) * sn + double(x) * cs) : float(double(x) * cs - double(xp) * sn);
+__device__ __forceinline__ float rope_apply(float x, float xp, int j, float cs, float sn) {
+  return (j & 1) ? fmaf(xp, sn, x * cs) : fmaf(x, cs, -xp * sn);
 }
 
 // Value of the neighbouring lane l ^ 1 (DPP quad permutation [1, 0, 3, 2]); every lane of the

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void dec_proj_kernel(DecProjArgs<E> p) {
       // jj % 4 == 0: the lane holds the rotary pairs (jj, jj+1) and (jj+2, jj+3) itself
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
-        double cs, sn;
+        float cs, sn;
         rope_angle(p.t, rope_theta(jj + r, p.s, p.log2_base), &cs, &sn);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
         const double theta = rope_theta(j, s, p.log2_base);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          double cs, sn;
+          float cs, sn;
           rope_angle((row + k) % p.n, theta, &cs, &sn);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
