@@ -42,7 +42,8 @@ HBM_PEAK = 8000.0  # GB/s
 def alg_flops(B, n, d, e, s, c, causal):
     """Algorithmic FLOPs of one layer forward, split by kernel (multiply-add = 2)."""
     N = B * n
-    proj = 2 * N * d * (2 * e + s)
+    proj = 2 * N * d * (e + s)  # V and the heads; the gate's GEMM runs in the mix kernel
+    gate = 2 * N * d * e
     if causal:
         # query i of a chunk sees i+1 keys: scores and P·V over (c+1)/2 keys on average
         scores = N * (c + 1) * s
@@ -56,7 +57,7 @@ def alg_flops(B, n, d, e, s, c, causal):
     readout = 2 * n_state * s * e
     out = 2 * N * e * d
     return {"pack": 0, "proj": proj, "scores": scores, "states": states, "carry": 0,
-            "mix": pv + readout, "out": out}
+            "mix": gate + pv + readout, "out": out}
 
 
 def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
@@ -75,11 +76,11 @@ def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
     pc = (c * (c + 1) // 2) if causal else c * c  # P entries the mix reads per chunk
     return {
         "pack": 2 * ((2 * e + s) * d + e * d) * esz,
-        "proj": (N * d + (2 * e + s) * d + N * (2 * e + 4 * s)) * esz,
-        "scores": (2 * N * s + B * G * c * c) * esz,
+        "proj": (N * d + (e + s) * d + N * (e + 4 * s)) * esz,
+        "scores": (2 * N * s + B * G * pc) * esz,
         "states": (N * (e + s) + states_out) * esz,
         "carry": carry,
-        "mix": (N * e * 2 + B * G * pc + N * s + nst + N * e) * esz,
+        "mix": (N * e + B * G * pc + N * s + nst + N * d + e * d + N * e) * esz,
         "out": (N * e + e * d + N * d) * esz,
     }
 
@@ -107,7 +108,7 @@ def measured_traffic(kernel, workload):
 
 
 BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "carry": "hbm",
-         "mix": "hbm", "out": "mfma"}
+         "mix": "mfma", "out": "mfma"}
 
 
 class HipEvents:

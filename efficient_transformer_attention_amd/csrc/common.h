@@ -151,31 +151,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Four consecutive elements fetched through a buffer resource (reads past its range give 0).
-template <class E> struct UVec;
-template <> struct UVec<BF16> {
-  using type = u32x2;
-  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  }
-  __device__ __forceinline__ static void unpack(const type& w, float* o) {
-    o[0] = __uint_as_float(w[0] << 16);
-    o[1] = __uint_as_float(w[0] & 0xFFFF0000u);
-    o[2] = __uint_as_float(w[1] << 16);
-    o[3] = __uint_as_float(w[1] & 0xFFFF0000u);
-  }
-};
-template <> struct UVec<F32> {
-  using type = u32x4;
-  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  }
-  __device__ __forceinline__ static void unpack(const type& w, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(w[k]);
-  }
-};
-
 // Rotary position embedding (the standard rotary form: the pair (x_{2k}, x_{2k+1}) of a head
 // vector at position m turns by the angle m·θ_k, θ_k = base^{-2k/s}). Positions reach 2^31,
 // where a float angle has lost its phase, so θ_k, m·θ_k and its reduction to [0, 2π) are

@@ -10,19 +10,21 @@
 // Every step is a dense contraction, so every kernel here is one tiled matrix-core GEMM with its
 // own operand sources and epilogue:
 //   pack    W_u|W_v|W_z and W_o transposed so that every GEMM reads K-contiguous rows
-//   proj    H = X [W_u|W_v|W_z]; epilogue SiLU, the four heads, V and K_lin written chunk-transposed
+//   proj    X [W_v|W_z]; epilogue SiLU, the four heads, V and K_lin written chunk-transposed
 //   scores  per chunk P = relu(Q_quad K_quadᵀ / c)², zero above the diagonal when causal
 //   states  per (sequence, e-tile): the accumulator runs over the chunks in order, so it IS the
 //           prefix Σ_{h<g} K_lin_hᵀ V_h; it is written (scaled by 1/n) before chunk g is added
 //   mix     per chunk, (V̂_quad + V̂_lin)ᵀ = [V_gᵀ | S_gᵀ] [P_g | Q_lin_g]ᵀ, one GEMM with the local
-//           and the global term concatenated along K; epilogue Y = U ⊙ (·)
+//           and the global term concatenated along K, after the gate's own GEMM Uᵀ = SiLU(W_uᵀ Xᵀ)
+//           for the same tile; epilogue Y = U ⊙ (·) (U never goes to memory)
 //   out     O = Y W_o (computed as Oᵀ tiles so each lane stores contiguous outputs)
 //
 // Matrix-core mapping (CDNA4): bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses four
 // v_mfma_f32_16x16x4_f32. Operand tiles are staged in LDS as rows of 128 bytes (8 chunks of 16 B);
 // the 16-byte chunk index is XOR-swizzled with the row index so that both the row-wise fills and
-// the fragment reads of 16 consecutive rows are free of bank conflicts. Two LDS stages alternate:
-// global loads of tile t+1 are in flight while tile t is multiplied.
+// the fragment reads of 16 consecutive rows are free of bank conflicts. Tiles travel from global
+// memory straight into a ring of two or three LDS stages (buffer loads with an LDS destination),
+// so the copies of later K-tiles are in flight while one is multiplied.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -133,6 +135,20 @@ struct TileGemm {
   template <class Tiles, class Pre, class Skip>
   __device__ __forceinline__ void run(u32x4* lds, int nt, Tiles&& tiles, Pre&& pre, Skip&& skip,
                                       int wave, int wm, int wn, int lane) {
+    pipeline(lds, nt, tiles,
+             [&](int t, const u32x4* stage) {
+               pre(t);
+               if (!skip(t)) compute(stage, wm, wn, lane);
+             },
+             wave, lane);
+  }
+
+  // The copy pipeline alone: body(t, stage) consumes K-tile t from its LDS stage (e.g. into the
+  // accumulators of another TileGemm of the same shape). Returns with every copy complete and
+  // every wave past a final barrier, so LDS may be reused.
+  template <class Tiles, class Body>
+  __device__ __forceinline__ static void pipeline(u32x4* lds, int nt, Tiles&& tiles, Body&& body,
+                                                  int wave, int lane) {
     if (nt <= 0) return;
     issue_tile(lds, tiles, 0, wave, lane);
     if (nt > 1) issue_tile(lds, tiles, 1, wave, lane);
@@ -147,8 +163,7 @@ struct TileGemm {
         // stage (t+2)%3 held tile t-1, which every wave finished before the barrier above
         if (t + 2 < nt) issue_tile(lds, tiles, t + 2, wave, lane);
       }
-      pre(t);
-      if (!skip(t)) compute(lds + (t % NS) * kStage, wm, wn, lane);
+      body(t, lds + (t % NS) * kStage);
       if constexpr (NS == 2) {
         __syncthreads();  // every wave is done with stage t%2
         if (t + 2 < nt) issue_tile(lds, tiles, t + 2, wave, lane);
@@ -331,18 +346,19 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs<E> args) {
 }
 
 // ------------------------------------------------------------------------------ proj
+// X (W_v | W_z): V and the four heads. The gate U = SiLU(X W_u) is not materialised: the mix
+// stage recomputes it for its own tile, next to the product it gates.
 template <class E>
 struct ProjArgs {
-  const typename E::T* X;      // [M, d]
-  const typename E::T* WcatT;  // [2e+s, d]
-  typename E::T* U;            // [M, e]
-  typename E::T* Vt;           // [M/c, e, c]
-  typename E::T* Qq;           // [M, s]
-  typename E::T* Kq;           // [M, s]
-  typename E::T* Ql;           // [M, s]
-  typename E::T* Klt;          // [M/c, s, c]
-  const float* gamma;          // [4, s]
-  const float* beta;           // [4, s]
+  const typename E::T* X;     // [M, d]
+  const typename E::T* WvzT;  // [e+s, d]: rows of (W_v | W_z)ᵀ
+  typename E::T* Vt;          // [M/c, e, c]
+  typename E::T* Qq;          // [M, s]
+  typename E::T* Kq;          // [M, s]
+  typename E::T* Ql;          // [M, s]
+  typename E::T* Klt;         // [M/c, s, c]
+  const float* gamma;         // [4, s]
+  const float* beta;          // [4, s]
   int M, d, e, s, c;
   int n;             // sequence length: a token's position is its row modulo n
   int rope;          // rotate the four heads (rotary position embedding)
@@ -353,7 +369,7 @@ template <class E, int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
-  const int ncols = 2 * p.e + p.s;
+  const int ncols = p.e + p.s;  // column j < e: V, else head feature j - e
   const int ntn = (ncols + BN - 1) / BN;
   const int ntm = (p.M + BM - 1) / BM;
   const int lid = xcd_remap(blockIdx.x, ntm * ntn);
@@ -366,7 +382,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   G g;
   g.zero();
   const Src a = make_src(p.X, m0, p.d, E::kSize, p.M - m0, BM, p.d);
-  const Src b = make_src(p.WcatT, n0, p.d, E::kSize, ncols - n0, BN, p.d);
+  const Src b = make_src(p.WvzT, n0, p.d, E::kSize, ncols - n0, BN, p.d);
   const int nk = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
   g.run(lds, nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
@@ -378,29 +394,20 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
 
   using T = typename E::T;
   const int e = p.e, s = p.s, c = p.c;
-  // A wave whose columns all fall in U or all in V stages its tile through LDS and writes full
-  // 16-byte runs (U row-major, V chunk-transposed); other waves store element-wise.
+  // A wave whose columns all fall in V stages its tile through LDS and writes full 16-byte runs
+  // of the chunk-transposed V; other waves store element-wise.
   const int wc0 = n0 + wn * G::WTN, wc1 = wc0 + G::WTN;
-  auto silu4 = [&](int, int, int, int, const f32x4& v, T* out) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
-  };
   if (wc1 <= e) {
-    g.template stage_cols<T>(lds, wave, wm, wn, lane, silu4,
-                             [&](int r, int cl, const u32x4& chunk) {
-                               const int row = m0 + r, col = n0 + cl;
-                               if (row < p.M)
-                                 *reinterpret_cast<u32x4*>(p.U + int64_t(row) * e + col) = chunk;
-                             });
-    return;
-  }
-  if (wc0 >= e && wc1 <= 2 * e) {
-    g.template stage_rows<T>(lds, wave, wm, wn, lane, silu4,
+    g.template stage_rows<T>(lds, wave, wm, wn, lane,
+                             [&](int, int, int, int, const f32x4& v, T* out) {
+#pragma unroll
+                               for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
+                             },
                              [&](int cl, int r, const u32x4& chunk) {
                                const int row = m0 + r, col = n0 + cl;
                                if (row >= p.M) return;
                                const int64_t bg = row / c, t = row % c;  // 8 rows, one chunk
-                               *reinterpret_cast<u32x4*>(p.Vt + (bg * e + (col - e)) * c + t) = chunk;
+                               *reinterpret_cast<u32x4*>(p.Vt + (bg * e + col) * c + t) = chunk;
                              });
     return;
   }
@@ -418,12 +425,9 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
     if (row >= p.M || col >= ncols) return;
     const int64_t bg = row / c, t = row % c;  // c % 8 == 0: rows row..row+3 share a chunk
     if (col < e) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) p.U[int64_t(row + k) * e + col] = from_f32<E>(y[k]);
-    } else if (col < 2 * e) {
-      store4(p.Vt + (bg * e + (col - e)) * c + t, y[0], y[1], y[2], y[3]);
+      store4(p.Vt + (bg * e + col) * c + t, y[0], y[1], y[2], y[3]);
     } else {
-      const int j = col - 2 * e;
+      const int j = col - e;
       float h[4][4];  // [head][token]
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -689,12 +693,14 @@ __global__ __launch_bounds__(256) void carry_kernel(CarryArgs<E> p) {
 // ------------------------------------------------------------------------------ mix
 template <class E>
 struct MixArgs {
-  const typename E::T* Vt;  // [B*G, e, c]
-  const typename E::T* St;  // causal [B*G, e, s], non-causal [B, e, s]
-  const typename E::T* P;   // [B*G, c, c]
-  const typename E::T* Ql;  // [B*G*c, s]
-  const typename E::T* U;   // [B*G*c, e]
-  typename E::T* Y;         // [B*G*c, e]
+  const typename E::T* Vt;   // [B*G, e, c]
+  const typename E::T* St;   // causal [B*G, e, s], non-causal [B, e, s]
+  const typename E::T* P;    // [B*G, c, c]
+  const typename E::T* Ql;   // [B*G*c, s]
+  const typename E::T* X;    // [B*G*c, d]
+  const typename E::T* WuT;  // [e, d]: rows of W_uᵀ
+  typename E::T* Y;          // [B*G*c, e]
+  int d;
   int nbg, G, c, e, s, causal;
   int lin;  // 0: no global term (causal with a single chunk: its prefix state is empty)
 };
@@ -730,27 +736,23 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   constexpr int kKeysPerTile = kStageBytes / E::kSize;
   const int last_token = n0 + (wn + 1) * G::WTN - 1;  // of this wave
 
-  // The gate operand U is fetched before the main loop, straight into the fragment layout of
-  // the accumulators (four consecutive value columns of one token per lane and fragment), so
-  // its latency hides behind the products. The buffer covers this block's valid tokens; tokens
-  // past the chunk read zeros, value columns past e read bytes of the next token row and are
-  // never stored.
-  using T = typename E::T;
-  using UFrag = typename UVec<E>::type;
-  const int valid_tok = min(BN, p.c - n0);
-  const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(p.U + (tok0 + n0) * p.e), 0, valid_tok * p.e * E::kSize, kBufferWord3);
-  UFrag uf[G::TM][G::TN];
+  // The gate first: Uᵀ = W_uᵀ Xᵀ for these value columns and tokens, a GEMM over d into its own
+  // accumulators (the projection stage does not write U); then the local and the global term.
+  // Two pipelines one after the other keep the kernel within 128 registers, so two workgroups
+  // share a CU (one pipeline over all three K-ranges needs more and halves the occupancy).
+  G gu;
+  gu.zero();
   {
-    const int lr = lane & 15, q = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < G::TN; ++j) {
-        const int col = m0 + wm * G::WTM + i * 16 + q * 4;  // value column
-        const int tok = wn * G::WTN + j * 16 + lr;          // token inside the block
-        uf[i][j] = UVec<E>::load(urs, (tok * p.e + col) * E::kSize);
-      }
+    const Src au = make_src(p.WuT, m0, p.d, E::kSize, p.e - m0, BM, p.d);
+    const Src bu = make_src(p.X, tok0 + n0, p.d, E::kSize, p.c - n0, BN, p.d);
+    const int nku = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
+    gu.run(lds, nku,
+           [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+             sa = au;
+             sb = bu;
+             ka = kb = t * kStageBytes;
+           },
+           NoPre(), wave, wm, wn, lane);
   }
 
   G g;
@@ -770,16 +772,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
         NoPre(), [&](int t) { return p.causal && t < nk0 && t * kKeysPerTile > last_token; },
         wave, wm, wn, lane);
 
-  // Y = U ⊙ (P V + Q_lin S / n): the product is formed in fp32 from the fragment's U values,
-  // rounded once, and staged through LDS so that every token row of Y is written as full
-  // 16-byte runs.
+  // Y = SiLU(X W_u) ⊙ (P V + Q_lin S / n), formed in fp32 from both accumulators, rounded once,
+  // and staged through LDS so that every token row of Y is written as full 16-byte runs.
+  using T = typename E::T;
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
       [&](int fi, int fj, int, int, const f32x4& v, T* out) {
-        float u[4];
-        UVec<E>::unpack(uf[fi][fj], u);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(u[k] * v[k]);
+        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(gu.acc[fi][fj][k]) * v[k]);
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, i = n0 + cl;
@@ -920,14 +920,13 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   int64_t t0;
   if (!mul_ok(p->ncols, d, &cnt[FLASHGAU_WS_WCAT_T])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(d, e, &cnt[FLASHGAU_WS_WO_T])) return FLASHGAU_ERR_BAD_SHAPE;
-  if (!mul_ok(M, e, &cnt[FLASHGAU_WS_U])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[FLASHGAU_WS_VT] = cnt[FLASHGAU_WS_U];
+  if (!mul_ok(M, e, &cnt[FLASHGAU_WS_VT])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(M, s, &cnt[FLASHGAU_WS_QQ])) return FLASHGAU_ERR_BAD_SHAPE;
   cnt[FLASHGAU_WS_KQ] = cnt[FLASHGAU_WS_QL] = cnt[FLASHGAU_WS_KLT] = cnt[FLASHGAU_WS_QQ];
   if (!mul_ok(M, chunk, &cnt[FLASHGAU_WS_P])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(causal ? p->nbg : B, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_ST]))
     return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[FLASHGAU_WS_Y] = cnt[FLASHGAU_WS_U];
+  cnt[FLASHGAU_WS_Y] = cnt[FLASHGAU_WS_VT];
   if (!mul_ok(B * p->ng, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_CARRY]))
     return FLASHGAU_ERR_BAD_SHAPE;
   size_t off = 0;
@@ -991,7 +990,6 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   };
   T* WcatT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WCAT_T]);
   T* WoT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WO_T]);
-  T* U = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_U]);
   T* Vt = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_VT]);
   T* Qq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_QQ]);
   T* Kq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_KQ]);
@@ -1007,10 +1005,10 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
-    ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT, U, Vt, Qq, Kq, Ql, Klt, gamma, beta,
-                  M, d, e, s, c, int(pl.n), rope_base > 0.0f ? 1 : 0,
+    ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt,
+                  gamma, beta, M, d, e, s, c, int(pl.n), rope_base > 0.0f ? 1 : 0,
                   rope_base > 0.0f ? log2(double(rope_base)) : 0.0};
-    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
+    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(e + s, S::kProjBN);
     hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
   }
@@ -1043,7 +1041,8 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
-    MixArgs<E> a{Vt, St, P, Ql, U, Y, int(pl.nbg), int(pl.G), c, e, s, causal, int(lin)};
+    MixArgs<E> a{Vt, St, P, Ql, reinterpret_cast<const T*>(X), WcatT, Y, d, int(pl.nbg),
+                 int(pl.G), c, e, s, causal, int(lin)};
     const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
     hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
                        dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);

@@ -27,7 +27,7 @@ ERR_ALIASING = -6
 ERR_HIP = -7
 
 # Order of the workspace buffers (FLASHGAU_WS_* in include/flashgau.h).
-WS_NAMES = ("WCAT_T", "WO_T", "U", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CARRY")
+WS_NAMES = ("WCAT_T", "WO_T", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CARRY")
 
 # Order of the decoding-state buffers (FLASHGAU_DS_* in include/flashgau.h).
 DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
@@ -211,7 +211,7 @@ def workspace_views(workspace, B, n, d, e, s, chunk, causal, dtype):
     G = n // chunk
     M = B * n
     shapes = {
-        "WCAT_T": (2 * e + s, d), "WO_T": (d, e), "U": (M, e), "VT": (B * G, e, chunk),
+        "WCAT_T": (2 * e + s, d), "WO_T": (d, e), "VT": (B * G, e, chunk),
         "QQ": (M, s), "KQ": (M, s), "QL": (M, s), "KLT": (B * G, s, chunk),
         "P": (B * G, chunk, chunk), "ST": ((B * G) if causal else B, e, s), "Y": (M, e),
         "CARRY": (B, state_groups(B, n, d, e, s, chunk, causal, dtype), e, s),

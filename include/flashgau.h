@@ -61,7 +61,6 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  * with G = n / chunk and element type = the call's dtype:
  *   WCAT_T  [2e+s, d]     transposed, concatenated projection weights (W_u | W_v | W_z)ᵀ
  *   WO_T    [d, e]        transposed output weights W_oᵀ
- *   U       [B*n, e]      SiLU(X W_u)
  *   VT      [B*G, e, c]   SiLU(X W_v), transposed inside each chunk (token index fastest)
  *   QQ, KQ, QL [B*n, s]   the heads Q_quad, K_quad, Q_lin
  *   KLT     [B*G, s, c]   the head K_lin, transposed inside each chunk
@@ -71,7 +70,8 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed.
  *                         Left unwritten when causal and n == chunk (the one chunk's prefix is
  *                         empty, so the global term vanishes and its stages launch nothing)
- *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin)
+ *   Y       [B*n, e]      U ⊙ (V̂_quad + V̂_lin), U = SiLU(X W_u) (U itself is never stored: the
+ *                         mix stage computes it for its own tile)
  *   CARRY   [B, NG, e, s] per sequence, the sum of K_linᵀ V over each group of consecutive
  *                         chunks, / n, transposed. The states stage splits the n/c chunks of a
  *                         sequence into NG groups of ceil((n/c) / NG) chunks (NG is chosen from the
@@ -80,7 +80,6 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
 enum {
   FLASHGAU_WS_WCAT_T = 0,
   FLASHGAU_WS_WO_T,
-  FLASHGAU_WS_U,
   FLASHGAU_WS_VT,
   FLASHGAU_WS_QQ,
   FLASHGAU_WS_KQ,
@@ -148,14 +147,15 @@ int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, cons
 /* Stages of flash_gau_forward, in launch order (one kernel each). */
 #define FLASHGAU_NUM_STAGES 7
 /* 0 pack   : transpose W_u|W_v|W_z and W_o into the workspace (WCAT_T, WO_T)
- * 1 proj   : X W_u|W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
+ * 1 proj   : X W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
  * 2 scores : per chunk relu(Q_quad K_quadᵀ / c)², masked when causal ("Mixed Chunk", local term)
  * 3 states : K_linᵀ V summed over the chunks of each chunk group: the exclusive prefix inside the
  *            group for every chunk (causal) and the group total, times 1/n; launches nothing
  *            when causal and n == chunk
  * 4 carry  : adds the totals of earlier groups to every chunk's state (causal), or sums the group
  *            totals into the sequence's state (non-causal); launches nothing with one group
- * 5 mix    : per chunk P V + Q_lin S / n, gated by U ("Mixed Chunk", both terms and the gate)
+ * 5 mix    : per chunk P V + Q_lin S / n, gated by U = SiLU(X W_u) computed in the same
+ *            workgroup ("Mixed Chunk", both terms and the gate)
  * 6 out    : Y W_o                                                                            */
 
 /* flash_gau_forward with per-stage timing: the same validation and the same launches, plus

@@ -41,7 +41,7 @@ def test_workspace_enum_matches_binding():
 def _expected_layout(B, n, d, e, s, c, causal, esz, ng):
     G = n // c
     M = B * n
-    counts = [(2 * e + s) * d, d * e, M * e, M * e, M * s, M * s, M * s, M * s, M * c,
+    counts = [(2 * e + s) * d, d * e, M * e, M * s, M * s, M * s, M * s, M * c,
               (B * G if causal else B) * e * s, M * e, B * ng * e * s]
     off, offs = 0, []
     for cnt in counts:

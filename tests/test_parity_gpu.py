@@ -121,7 +121,6 @@ def test_stage_parity(name):
     tol = TOL[dtype]
     lower = np.tril(np.ones((c, c), dtype=bool))
     checks = {
-        "U": (v["U"].reshape(B, n, e), it["U"]),
         "V": (v["VT"].reshape(B, G, e, c).transpose(0, 1, 3, 2).reshape(B, n, e), it["V"]),
         "Q_quad": (v["QQ"].reshape(B, n, s), it["Qq"]),
         "K_quad": (v["KQ"].reshape(B, n, s), it["Kq"]),
