@@ -379,6 +379,13 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
+  // A tile of head features only is computed transposed (rows = features, columns = tokens):
+  // each lane then holds four consecutive features of one token, so the row-major heads leave as
+  // 8-byte stores and the rotary pairs sit inside the lane. The tiles are square, so swapping
+  // the operands is all it takes.
+  static_assert(BM == BN, "transposed head tiles need square tiles");
+  const bool heads_t = n0 >= p.e;
+
   G g;
   g.zero();
   const Src a = make_src(p.X, m0, p.d, E::kSize, p.M - m0, BM, p.d);
@@ -386,14 +393,50 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   const int nk = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
   g.run(lds, nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-          sa = a;
-          sb = b;
+          sa = heads_t ? b : a;
+          sb = heads_t ? a : b;
           ka = kb = t * kStageBytes;
         },
         NoPre(), wave, wm, wn, lane);
 
   using T = typename E::T;
   const int e = p.e, s = p.s, c = p.c;
+  if (heads_t) {
+    g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
+      const int j = n0 - e + r;  // first of four consecutive features (s % 8 == 0)
+      const int row = m0 + cl;   // token
+      if (j >= s || row >= p.M) return;
+      float y[4], h[4][4];  // [head][feature j + k]
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = silu(v[k]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[q][k] = fmaf(p.gamma[q * s + j + k], y[k], p.beta[q * s + j + k]);
+      if (p.rope) {
+        const int pos = row % p.n;
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          float cs, sn;
+          rope_angle(pos, rope_theta(j + k, s, p.log2_base), &cs, &sn);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x0 = h[q][k], x1 = h[q][k + 1];
+            h[q][k] = rope_apply(x0, x1, j + k, cs, sn);
+            h[q][k + 1] = rope_apply(x1, x0, j + k + 1, cs, sn);
+          }
+        }
+      }
+      const int64_t o = int64_t(row) * s + j;
+      store4(p.Qq + o, h[0][0], h[0][1], h[0][2], h[0][3]);
+      store4(p.Kq + o, h[1][0], h[1][1], h[1][2], h[1][3]);
+      store4(p.Ql + o, h[2][0], h[2][1], h[2][2], h[2][3]);
+      const int64_t bg = row / c, t = row % c;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p.Klt[(bg * s + j + k) * c + t] = from_f32<E>(h[3][k]);
+    });
+    return;
+  }
   // A wave whose columns all fall in V stages its tile through LDS and writes full 16-byte runs
   // of the chunk-transposed V; other waves store element-wise.
   const int wc0 = n0 + wn * G::WTN, wc1 = wc0 + G::WTN;
