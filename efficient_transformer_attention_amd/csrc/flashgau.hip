@@ -45,7 +45,7 @@ namespace {
 // tile; with NS = 2 (tiles too large for three stages) the loads of tile t+2 are issued after
 // tile t has been consumed, two barriers per tile. PRIO raises the wave priority while it issues
 // matrix instructions; iglp_opt(1) asks the scheduler to interleave the LDS reads with them.
-template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false>
+template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false, int IGLP = 1>
 struct TileGemm {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kWaves = WM * WN;
@@ -104,7 +104,7 @@ struct TileGemm {
     const int lr = lane & 15;
     const int q = lane >> 4;
     if (PRIO) __builtin_amdgcn_s_setprio(1);
-    __builtin_amdgcn_iglp_opt(1);
+    if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
 #pragma unroll
     for (int ks = 0; ks < kRowChunks / 4; ++ks) {
       const int ch = (ks * 4 + q) ^ (lr & 7);  // rows below differ from lr by multiples of 16
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
                                const int row = m0 + r, col = n0 + cl;
                                if (row >= p.M) return;
                                const int64_t bg = row / c, t = row % c;  // 8 rows, one chunk
-                               *reinterpret_cast<u32x4*>(p.Vt + (bg * e + col) * c + t) = chunk;
+                               store16_stream(p.Vt + (bg * e + col) * c + t, chunk);
                              });
     return;
   }
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, i = n0 + cl;
-        if (j < p.e && i < p.c) *reinterpret_cast<u32x4*>(p.Y + (tok0 + i) * p.e + j) = chunk;
+        if (j < p.e && i < p.c) store16_stream(p.Y + (tok0 + i) * p.e + j, chunk);
       });
 }
 
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, i = n0 + cl;  // j: first of the chunk's features, i: token
-        if (j < p.d && i < p.M) *reinterpret_cast<u32x4*>(p.O + int64_t(i) * p.d + j) = chunk;
+        if (j < p.d && i < p.M) store16_stream(p.O + int64_t(i) * p.d + j, chunk);
       });
 }
 
