@@ -58,7 +58,7 @@ def alg_flops(B, n, d, e, s, c, causal):
     states = 2 * n_state * s * e
     readout = 2 * n_state * s * e
     out = 2 * N * e * d
-    return {"pack": 0, "proj": proj, "scores": scores, "states": states, "carry": 0,
+    return {"pack": 0, "proj": proj, "scores_states": scores + states, "carry": 0,
             "mix": gate + pv + readout, "out": out}
 
 
@@ -79,8 +79,7 @@ def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
     return {
         "pack": 2 * ((2 * e + s) * d + e * d) * esz,
         "proj": (N * d + (e + s) * d + N * (e + 4 * s)) * esz,
-        "scores": (2 * N * s + B * G * pc) * esz,
-        "states": (N * (e + s) + states_out) * esz,
+        "scores_states": (2 * N * s + B * G * pc + N * (e + s) + states_out) * esz,
         "carry": carry,
         "mix": (N * e + B * G * pc + N * s + nst + N * d + e * d + N * e) * esz,
         "out": (N * e + e * d + N * d) * esz,
@@ -109,8 +108,8 @@ def measured_traffic(kernel, workload):
     return None
 
 
-BOUND = {"pack": "hbm", "proj": "mfma", "scores": "hbm", "states": "hbm", "carry": "hbm",
-         "mix": "mfma", "out": "mfma"}
+BOUND = {"pack": "hbm", "proj": "mfma", "scores_states": "hbm", "carry": "hbm", "mix": "mfma",
+         "out": "mfma"}
 
 
 class HipEvents:

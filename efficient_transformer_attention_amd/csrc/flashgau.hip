@@ -11,9 +11,11 @@
 // own operand sources and epilogue:
 //   pack    W_u|W_v|W_z and W_o transposed so that every GEMM reads K-contiguous rows
 //   proj    X [W_v|W_z]; epilogue SiLU, the four heads, V and K_lin written chunk-transposed
-//   scores  per chunk P = relu(Q_quad K_quadᵀ / c)², zero above the diagonal when causal
-//   states  per (sequence, e-tile): the accumulator runs over the chunks in order, so it IS the
-//           prefix Σ_{h<g} K_lin_hᵀ V_h; it is written (scaled by 1/n) before chunk g is added
+//   scores_states  one launch of two roles: per chunk P = relu(Q_quad K_quadᵀ / c)² (zero above
+//           the diagonal when causal), and per (sequence, chunk group, tile) the chunk summaries
+//           K_lin_hᵀ V_h, accumulated over the group's chunks in order so that the accumulator IS
+//           the exclusive prefix inside the group (written, scaled by 1/n, before a chunk is added)
+//   carry   adds the totals of earlier chunk groups to every chunk's state
 //   mix     per chunk, (V̂_quad + V̂_lin)ᵀ = [V_gᵀ | S_gᵀ] [P_g | Q_lin_g]ᵀ, one GEMM with the local
 //           and the global term concatenated along K, after the gate's own GEMM Uᵀ = SiLU(W_uᵀ Xᵀ)
 //           for the same tile; epilogue Y = U ⊙ (·) (U never goes to memory)
@@ -520,12 +522,11 @@ struct ScoresArgs {
 // it are never read: every wave of the mix stage skips them), and entries above the diagonal
 // inside them are written as zeros.
 template <class E, int BT, int WM, int WN, int NS>
-__global__ __launch_bounds__(64 * WM * WN) void scores_kernel(ScoresArgs<E> p) {
+__device__ __forceinline__ void scores_block(const ScoresArgs<E>& p, u32x4* lds, int bid) {
   using G = TileGemm<E, BT, BT, WM, WN, NS>;
-  __shared__ u32x4 lds[G::kLds];
   const int ntc = (p.c + BT - 1) / BT;
   const int per_chunk = p.causal ? ntc * (ntc + 1) / 2 : ntc * ntc;
-  const int lid = xcd_remap(blockIdx.x, p.nbg * per_chunk);
+  const int lid = xcd_remap(bid, p.nbg * per_chunk);
   const int bg = lid / per_chunk;
   const int rem = lid % per_chunk;
   int tt, kt;  // token tile, key tile
@@ -592,12 +593,11 @@ struct StatesArgs {
 };
 
 template <class E, int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
+__device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds, int bid) {
   using G = TileGemm<E, BM, BN, WM, WN, NS>;
-  __shared__ u32x4 lds[G::kLds];
   const int nts = (p.s + BM - 1) / BM;
   const int nte = (p.e + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, p.B * p.ng * nts * nte);
+  const int lid = xcd_remap(bid, p.B * p.ng * nts * nte);
   // neighbouring workgroups share a chunk group, hence its K_lin and V rows
   const int nt = lid % nte;
   int rest = lid / nte;
@@ -645,6 +645,29 @@ __global__ __launch_bounds__(64 * WM * WN) void states_kernel(StatesArgs<E> p) {
     write_state(g, p.St + int64_t(b) * es);
   else if (!p.causal || grp < p.ng - 1)  // the last group's total is never read when causal
     write_state(g, p.Carry + (int64_t(b) * p.ng + grp) * es);
+}
+
+// ------------------------------------------------------------------------------ scores + states
+// The per-chunk scores and the chunk summaries read only the projection's outputs, so one launch
+// runs both: workgroups [0, n_scores) compute score tiles, the rest summary tiles. The memory-bound
+// summaries overlap the scores instead of waiting for their last wave. n_scores is a multiple of
+// the XCD count, so both ranges keep their XCD-aware tile order (extra score workgroups return).
+template <class E, class S>
+__global__ __launch_bounds__(64 * S::kScoresWM * S::kScoresWN) void scores_states_kernel(
+    ScoresArgs<E> sp, int n_scores, int scores_blocks, StatesArgs<E> tp, int states_on) {
+  static_assert(S::kScoresWM * S::kScoresWN == S::kStatesWM * S::kStatesWN,
+                "both roles run with the same workgroup size");
+  using GS = TileGemm<E, S::kScoresBT, S::kScoresBT, S::kScoresWM, S::kScoresWN, S::kScoresNS>;
+  using GT = TileGemm<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN, S::kStatesNS>;
+  __shared__ u32x4 lds[GS::kLds > GT::kLds ? GS::kLds : GT::kLds];
+  const int bid = blockIdx.x;
+  if (bid < n_scores) {
+    if (bid < scores_blocks)
+      scores_block<E, S::kScoresBT, S::kScoresWM, S::kScoresWN, S::kScoresNS>(sp, lds, bid);
+  } else if (states_on) {
+    states_block<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN, S::kStatesNS>(
+        tp, lds, bid - n_scores);
+  }
 }
 
 // ------------------------------------------------------------------------------ carry
@@ -984,8 +1007,7 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   // Grid sizes of every launch (the largest tile counts use the smallest tiles).
   const int64_t grids[] = {
       cdiv(M, 128) * cdiv(p->ncols, 128),
-      p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64),
-      B * p->ng * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN),
+      p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64) + kXcds + B * p->ng * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN),
       cdiv(B * e * s / 8, 256),
       p->nbg * cdiv(e, 128) * cdiv(chunk, 64),
       cdiv(d, 128) * cdiv(M, 128),
@@ -1056,24 +1078,20 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
                        dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
-  {
-    ScoresArgs<E> a{Qq, Kq, P, int(pl.nbg), c, s, causal, 1.0f / float(c)};
-    const int64_t ntc = cdiv(c, S::kScoresBT);
-    const int64_t nb = pl.nbg * (causal ? ntc * (ntc + 1) / 2 : ntc * ntc);
-    hipLaunchKernelGGL((scores_kernel<E, S::kScoresBT, S::kScoresWM, S::kScoresWN, S::kScoresNS>),
-                       dim3(unsigned(nb)), dim3(64 * S::kScoresWM * S::kScoresWN), 0, stream, a);
-  }
-  if (!mark()) return FLASHGAU_ERR_HIP;
   // Causal with a single chunk: the only chunk reads an empty prefix, so there is no global
-  // term at all; the states and carry stages launch nothing and ST is left unwritten.
+  // term at all; the summary tiles and the carry stage launch nothing and ST is left unwritten.
   const bool lin = !(causal && pl.G == 1);
-  if (lin) {
-    StatesArgs<E> a{Klt, Vt, St, Carry, int(pl.B), int(pl.G), s, e, c, causal,
-                    int(pl.ng), int(pl.gs), float(1.0 / double(pl.n))};
-    const int64_t nb = pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN);
-    hipLaunchKernelGGL((states_kernel<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN,
-                                      S::kStatesNS>),
-                       dim3(unsigned(nb)), dim3(64 * S::kStatesWM * S::kStatesWN), 0, stream, a);
+  {
+    ScoresArgs<E> sa{Qq, Kq, P, int(pl.nbg), c, s, causal, 1.0f / float(c)};
+    const int64_t ntc = cdiv(c, S::kScoresBT);
+    const int64_t nsb = pl.nbg * (causal ? ntc * (ntc + 1) / 2 : ntc * ntc);
+    const int64_t nsb8 = cdiv(nsb, kXcds) * kXcds;
+    StatesArgs<E> ta{Klt, Vt, St, Carry, int(pl.B), int(pl.G), s, e, c, causal,
+                     int(pl.ng), int(pl.gs), float(1.0 / double(pl.n))};
+    const int64_t ntb = lin ? pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN) : 0;
+    hipLaunchKernelGGL((scores_states_kernel<E, S>), dim3(unsigned(nsb8 + ntb)),
+                       dim3(64 * S::kScoresWM * S::kScoresWN), 0, stream, sa, int(nsb8), int(nsb), ta,
+                       int(lin));
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   if (lin && pl.ng > 1) {

@@ -39,7 +39,7 @@ EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_st
            "flash_gau_decode_step", "flashgau_strerror")
 
 # Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
-STAGES = ("pack", "proj", "scores", "states", "carry", "mix", "out")
+STAGES = ("pack", "proj", "scores_states", "carry", "mix", "out")
 
 _lib = None
 

@@ -145,18 +145,19 @@ int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, cons
                            size_t workspace_bytes, void* hip_stream);
 
 /* Stages of flash_gau_forward, in launch order (one kernel each). */
-#define FLASHGAU_NUM_STAGES 7
-/* 0 pack   : transpose W_u|W_v|W_z and W_o into the workspace (WCAT_T, WO_T)
- * 1 proj   : X W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
- * 2 scores : per chunk relu(Q_quad K_quadᵀ / c)², masked when causal ("Mixed Chunk", local term)
- * 3 states : K_linᵀ V summed over the chunks of each chunk group: the exclusive prefix inside the
- *            group for every chunk (causal) and the group total, times 1/n; launches nothing
- *            when causal and n == chunk
- * 4 carry  : adds the totals of earlier groups to every chunk's state (causal), or sums the group
- *            totals into the sequence's state (non-causal); launches nothing with one group
- * 5 mix    : per chunk P V + Q_lin S / n, gated by U = SiLU(X W_u) computed in the same
- *            workgroup ("Mixed Chunk", both terms and the gate)
- * 6 out    : Y W_o                                                                            */
+#define FLASHGAU_NUM_STAGES 6
+/* 0 pack          : transpose W_u|W_v|W_z and W_o into the workspace (WCAT_T, WO_T)
+ * 1 proj          : X W_v|W_z with SiLU and the four heads ("Initial Power", "Weak Attention")
+ * 2 scores_states : one launch of two independent roles: per chunk relu(Q_quad K_quadᵀ / c)²,
+ *                   masked when causal ("Mixed Chunk", local term); and K_linᵀ V summed over the
+ *                   chunks of each chunk group: the exclusive prefix inside the group for every
+ *                   chunk (causal) and the group total, times 1/n (none when causal, n == chunk)
+ * 3 carry         : adds the totals of earlier groups to every chunk's state (causal), or sums
+ *                   the group totals into the sequence's state (non-causal); launches nothing
+ *                   with one group
+ * 4 mix           : per chunk P V + Q_lin S / n, gated by U = SiLU(X W_u) computed in the same
+ *                   workgroup ("Mixed Chunk", both terms and the gate)
+ * 5 out           : Y W_o                                                                    */
 
 /* flash_gau_forward with per-stage timing: the same validation and the same launches, plus
  * hipEventRecord(stage_events[i], hip_stream) right before stage i is launched and
