@@ -12,10 +12,10 @@
 //
 // One step for B sequences (all at position t) is four small launches, none of them a GEMM of
 // any size: with one token per sequence the work is reading the weights and the state once.
-//   proj   h = x (W_u | W_v | W_z) for the B tokens: each wave owns 16 weight rows of the packed
-//          (K-contiguous) weights and multiplies them with 16 token rows on the matrix cores,
-//          operands fetched straight from global memory into fragments; epilogue SiLU, the four
-//          heads, k_quad, k_lin and v written as row i of the chunk cache
+//   proj   h = x (W_u | W_v | W_z) for the B tokens: each workgroup owns 16 rows of the packed
+//          (K-contiguous) weights and multiplies them with 16 token rows on the matrix cores, its
+//          8 waves splitting K, operands fetched straight from global memory into fragments;
+//          epilogue SiLU, the four heads, k_quad, k_lin and v written as row i of the chunk cache
 //   attn   per sequence and 256 value columns: the weights relu(q·k_j / c)² for j <= i, then
 //          Σ_j w_j v_j + q_lin S / n over the rows of the chunk cache and of the state, split over
 //          32 row slots and reduced through LDS; y = u ⊙ (·)
@@ -31,30 +31,59 @@
 namespace {
 
 // ------------------------------------------------------------------------------ skinny product
-// acc = A[16 rows] · Xr[16 rows]ᵀ over K elements for one wave: lane l feeds row l % 16 of both
-// operands and the 16-byte chunk l / 16 of each K-step (the matrix-core fragment layout), so
-// lane l ends with C[4 (l / 16) + r][l % 16], r = 0..3 (rows of A, then the Xr row). Eight
-// K-steps of loads are issued before their products to keep bytes in flight.
+// With one token per sequence the projections are weight-streaming GEMVs: 16 weight rows times
+// at most 16 token rows. kSplit waves share each 16-row slice, each taking 1/kSplit of K, so that
+// enough bytes are in flight to stream the weights; their partial tiles are summed through LDS.
+constexpr int kSplit = 8;
+constexpr int kSkinnyThreads = 64 * kSplit;
+
+// acc = A[16 rows] · Xr[16 rows]ᵀ over K elements [k0, k1) for one wave: lane l feeds row l % 16
+// of both operands and the 16-byte chunk l / 16 of each K-step (the matrix-core fragment layout),
+// so lane l ends with C[4 (l / 16) + r][l % 16], r = 0..3 (rows of A, then the Xr row). Four
+// K-steps of loads are issued before their products.
 template <class E>
-__device__ __forceinline__ f32x4 skinny16(const Rows& a, const Rows& xr, int K, int lane) {
+__device__ __forceinline__ f32x4 skinny16(const Rows& a, const Rows& xr, int k0, int k1, int lane) {
   constexpr int kElems = 16 / E::kSize;  // elements per 16-byte chunk
   constexpr int kStep = 4 * kElems;      // K covered by one mma()
   const int lr = lane & 15, q = lane >> 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nsteps = (K + kStep - 1) / kStep;
-  for (int st = 0; st < nsteps; st += 8) {
-    u32x4 fa[8], fx[8];
+  for (int kb = k0; kb < k1; kb += 4 * kStep) {
+    u32x4 fa[4], fx[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = (st + u) * kStep + q * kElems;
-      const bool in = k < K;
+    for (int u = 0; u < 4; ++u) {
+      const int k = kb + u * kStep + q * kElems;
+      const bool in = k < k1;
       fa[u] = load16(a, in ? uint32_t(lr) * a.ld + uint32_t(k) * E::kSize : kOutOfRange);
       fx[u] = load16(xr, in ? uint32_t(lr) * xr.ld + uint32_t(k) * E::kSize : kOutOfRange);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mma(acc, fa[u], fx[u], E());
+    for (int u = 0; u < 4; ++u) mma(acc, fa[u], fx[u], E());
   }
   return acc;
+}
+
+// The whole workgroup's product for one 16-row slice: wave w takes its share of K (a multiple of
+// the K-step, so chunks never straddle two waves), then the partial tiles are summed through LDS.
+// Every lane of wave 0 returns the sum in its fragment position; other waves' results are unused.
+template <class E>
+__device__ __forceinline__ f32x4 skinny16_split(const Rows& a, const Rows& xr, int K, int wave,
+                                                int lane, float* red) {
+  constexpr int kStep = 4 * (16 / E::kSize);
+  const int steps = (K + kStep - 1) / kStep;
+  const int per = (steps + kSplit - 1) / kSplit;
+  const int k0 = min(K, wave * per * kStep), k1 = min(K, (wave + 1) * per * kStep);
+  const f32x4 acc = skinny16<E>(a, xr, k0, k1, lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kSplit; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[r] += red[(w * 4 + r) * 64 + lane];
+  }
+  return sum;
 }
 
 // ------------------------------------------------------------------------------ proj
@@ -76,18 +105,19 @@ struct DecProjArgs {
   double log2_base;  // log2 of the rotary base
 };
 
-// grid (ceil((2e+s) / 64), ceil(B / 16)), 256 threads: wave w owns weight rows 64 x + 16 w.
+// grid (ceil((2e+s) / 16), ceil(B / 16)), kSkinnyThreads threads: weight rows 16 x .. 16 x + 15.
 template <class E>
-__global__ __launch_bounds__(256) void dec_proj_kernel(DecProjArgs<E> p) {
+__global__ __launch_bounds__(kSkinnyThreads) void dec_proj_kernel(DecProjArgs<E> p) {
+  __shared__ float red[kSplit * 4 * 64];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int ncols = 2 * p.e + p.s;
-  const int col0 = blockIdx.x * 64 + wave * 16;
+  const int col0 = blockIdx.x * 16;
   const int b0 = blockIdx.y * 16;
-  if (col0 >= ncols) return;  // wave-uniform; no barrier follows
   const int64_t ld = int64_t(p.d) * E::kSize;
   const Rows a = make_rows(p.WcatT, col0, ld, min(16, ncols - col0));
   const Rows xr = make_rows(p.x, b0, ld, min(16, p.B - b0));
-  const f32x4 acc = skinny16<E>(a, xr, p.d, lane);
+  const f32x4 acc = skinny16_split<E>(a, xr, p.d, wave, lane, red);
+  if (wave != 0) return;
 
   const int b = b0 + (lane & 15);
   const int j = col0 + 4 * (lane >> 4);  // first of four consecutive output columns
@@ -144,9 +174,10 @@ struct DecAttnArgs {
   float inv_c, inv_n;
 };
 
-constexpr int kAttnCols = 256;   // value columns per workgroup
-constexpr int kAttnSlots = 32;   // row slots (1024 threads = 32 slots x 32 groups of 8 columns)
+constexpr int kAttnCols = 128;   // value columns per workgroup
+constexpr int kAttnGroups = kAttnCols / 8;  // groups of 8 consecutive columns
 constexpr int kAttnThreads = 1024;
+constexpr int kAttnSlots = kAttnThreads / kAttnGroups;  // row slots (64)
 
 // 8 consecutive elements as fp32 (16 bytes for bf16, two 16-byte loads for fp32).
 __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
@@ -167,11 +198,11 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
   }
 }
 
-// grid (ceil(e / 256), B), 1024 threads, dynamic LDS (c + 2 s + 32·256) floats.
+// grid (ceil(e / 128), B), 1024 threads, dynamic LDS (c + 2 s + 64·128) floats.
 template <class E>
 __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p) {
   extern __shared__ float sh[];
-  float* part = sh;                             // [32][256] partial sums
+  float* part = sh;                             // [kAttnSlots][kAttnCols] partial sums
   float* qq = part + kAttnSlots * kAttnCols;    // [s]
   float* ql = qq + p.s;                         // [s]
   float* w = ql + p.s;                          // [i + 1]
@@ -183,24 +214,35 @@ __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p
     ql[k] = to_f32(p.Ql[int64_t(b) * p.s + k]) * p.inv_n;
   }
   __syncthreads();
-  // local weights of the keys 0..i of this chunk
-  for (int j = tid; j <= p.i; j += kAttnThreads) {
-    const typename E::T* kr = p.Kqc + (int64_t(b) * p.c + j) * p.s;
+  // local weights w_j = relu(q·k_j / c)² of the keys 0..i of this chunk: four neighbouring lanes
+  // per key, each summing every fourth 8-element chunk of the dot product (independent loads in
+  // flight), combined by two lane exchanges that every lane executes
+  const int nchunk = p.s / 8;
+  for (int j0 = 0; j0 <= p.i; j0 += kAttnThreads / 4) {
+    const int j = j0 + (tid >> 2), quarter = tid & 3;
     float dot = 0.f;
-    for (int k = 0; k < p.s; k += 8) {
-      float kv[8];
-      load8(kr + k, kv);
+    if (j <= p.i) {
+      const typename E::T* kr = p.Kqc + (int64_t(b) * p.c + j) * p.s;
+#pragma unroll 4
+      for (int ch = quarter; ch < nchunk; ch += 4) {
+        float kv[8];
+        load8(kr + ch * 8, kv);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) dot = fmaf(qq[k + m], kv[m], dot);
+        for (int m = 0; m < 8; ++m) dot = fmaf(qq[ch * 8 + m], kv[m], dot);
+      }
     }
-    const float r = fmaxf(dot * p.inv_c, 0.f);
-    w[j] = r * r;
+    dot += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dot), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    dot += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dot), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    if (j <= p.i && quarter == 0) {
+      const float r = fmaxf(dot * p.inv_c, 0.f);
+      w[j] = r * r;
+    }
   }
   __syncthreads();
 
   // Σ_j w_j v_j over the cache rows and Σ_k (q_lin,k / n) S_k over the state rows; slot `sl`
-  // takes rows sl, sl + 32, ...; group `cg` owns 8 consecutive value columns.
-  const int cg = tid & 31, sl = tid >> 5;
+  // takes rows sl, sl + kAttnSlots, ...; group `cg` owns 8 consecutive value columns.
+  const int cg = tid % kAttnGroups, sl = tid / kAttnGroups;
   const int col = col0 + cg * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (col < p.e) {  // e % 8 == 0: the 8 columns are all valid or all past the end
@@ -228,7 +270,7 @@ __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p
   __syncthreads();
   if (tid < kAttnCols && col0 + tid < p.e) {
     float sum = 0.f;
-#pragma unroll 8
+#pragma unroll 16
     for (int r = 0; r < kAttnSlots; ++r) sum += part[r * kAttnCols + tid];
     const int64_t o = int64_t(b) * p.e + col0 + tid;
     p.Y[o] = from_f32<E>(to_f32(p.U[o]) * sum);
@@ -244,17 +286,18 @@ struct DecOutArgs {
   int B, d, e;
 };
 
-// grid (ceil(d / 64), ceil(B / 16)), 256 threads.
+// grid (ceil(d / 16), ceil(B / 16)), kSkinnyThreads threads.
 template <class E>
-__global__ __launch_bounds__(256) void dec_out_kernel(DecOutArgs<E> p) {
+__global__ __launch_bounds__(kSkinnyThreads) void dec_out_kernel(DecOutArgs<E> p) {
+  __shared__ float red[kSplit * 4 * 64];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int col0 = blockIdx.x * 64 + wave * 16;
+  const int col0 = blockIdx.x * 16;
   const int b0 = blockIdx.y * 16;
-  if (col0 >= p.d) return;
   const int64_t ld = int64_t(p.e) * E::kSize;
   const Rows a = make_rows(p.WoT, col0, ld, min(16, p.d - col0));
   const Rows yr = make_rows(p.Y, b0, ld, min(16, p.B - b0));
-  const f32x4 acc = skinny16<E>(a, yr, p.e, lane);
+  const f32x4 acc = skinny16_split<E>(a, yr, p.e, wave, lane, red);
+  if (wave != 0) return;
   const int b = b0 + (lane & 15);
   const int j = col0 + 4 * (lane >> 4);
   if (b < p.B && j < p.d) store4(p.O + int64_t(b) * p.d + j, acc[0], acc[1], acc[2], acc[3]);
@@ -331,6 +374,7 @@ int make_decode_plan(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
   if (d % 8 || e % 8 || s % 8) return FLASHGAU_ERR_UNSUPPORTED;
   // the attention kernel keeps the chunk's weights and both query heads in LDS next to its
   // 32 KB of partial sums (64 KB in all)
+  static_assert(kAttnSlots * kAttnCols == 8192, "32 KB of partial sums");
   if (chunk + 2 * s + kAttnSlots * kAttnCols > 16384) return FLASHGAU_ERR_UNSUPPORTED;
   p->B = B, p->d = d, p->e = e, p->s = s, p->c = chunk;
   p->esz = dtype == FLASHGAU_BF16 ? 2 : 4;
@@ -381,8 +425,8 @@ int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_
     DecProjArgs<E> a{reinterpret_cast<const T*>(x), WcatT, gamma, beta, U, Vc, Qq, Kqc, Ql, Klc,
                      B, d, e, s, c, i, t, rope_base > 0.0f ? 1 : 0,
                      rope_base > 0.0f ? log2(double(rope_base)) : 0.0};
-    hipLaunchKernelGGL(dec_proj_kernel<E>, dim3(unsigned(cdiv(pl.ncols, 64)), unsigned(cdiv(B, 16))),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dec_proj_kernel<E>, dim3(unsigned(cdiv(pl.ncols, 16)), unsigned(cdiv(B, 16))),
+                       dim3(kSkinnyThreads), 0, stream, a);
   }
   {
     DecAttnArgs<E> a{Qq, Kqc, Ql, Vc, S, U, Y, B, e, s, c, i, float(1.0 / double(c)),
@@ -393,8 +437,8 @@ int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_
   }
   {
     DecOutArgs<E> a{WoT, Y, reinterpret_cast<T*>(o), B, d, e};
-    hipLaunchKernelGGL(dec_out_kernel<E>, dim3(unsigned(cdiv(d, 64)), unsigned(cdiv(B, 16))),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dec_out_kernel<E>, dim3(unsigned(cdiv(d, 16)), unsigned(cdiv(B, 16))),
+                       dim3(kSkinnyThreads), 0, stream, a);
   }
   if (i == c - 1) {
     DecFoldArgs<E> a{Klc, Vc, S, B, e, s, c};

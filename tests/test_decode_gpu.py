@@ -129,3 +129,42 @@ def test_decode_is_deterministic():
     a, _ = run_decode_gpu(inp, T, n, dtype)
     b, _ = run_decode_gpu(inp, T, n, dtype)
     assert np.array_equal(a, b)
+
+
+def test_decode_steps_replayed_from_a_hip_graph_match_eager():
+    # Steps t0..t1-1 captured once into a HIP graph (torch.cuda.CUDAGraph); before each replay the
+    # state is restored eagerly from a saved copy; every replay must give the eager outputs bitwise.
+    torch = _torch()
+    B, d, e, s, c, n, dtype = 3, 64, 136, 24, 8, 32, "bf16"
+    t0, t1 = 6, 19  # crosses a chunk end (the fold after t = 15)
+    print("[gpu case] decode graph replay", flush=True)
+    inp = _inputs(B, d, e, s, c, 24, dtype, 0.3, 0.1, seed=9)
+    W = [_dev(w, dtype) for w in (inp.W_u, inp.W_v, inp.W_z, inp.W_o)]
+    gamma, beta = _dev(inp.gamma, "f32"), _dev(inp.beta, "f32")
+    packed = fg.pack_weights(*W)
+    X = _dev(inp.X, dtype)
+    xs = [X[:, t].contiguous() for t in range(t1)]
+    state = fg.DecodeState(B, d, e, s, c, W[0].dtype, "cuda")
+    for t in range(t0):
+        fg.flash_gau_decode_step(xs[t], packed, gamma, beta, c, t, n, state)
+    torch.cuda.synchronize()
+    saved = state.buf.clone()
+    outs = [torch.empty((B, d), dtype=W[0].dtype, device="cuda") for _ in range(t0, t1)]
+    eager = [fg.flash_gau_decode_step(xs[t], packed, gamma, beta, c, t, n, state).clone()
+             for t in range(t0, t1)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    state.buf.copy_(saved)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        for k, t in enumerate(range(t0, t1)):
+            fg.flash_gau_decode_step(xs[t], packed, gamma, beta, c, t, n, state, out=outs[k],
+                                     stream=stream.cuda_stream)
+    for rep in range(3):
+        state.buf.copy_(saved)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in range(len(outs)):
+            assert torch.equal(outs[k], eager[k]), (rep, k)
