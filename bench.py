@@ -325,6 +325,8 @@ def main():
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the causal decoding measurement")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the causal decoding measurement and print its JSON object")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rotary-embedding and FLASH-Quad (chunk = n) timings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -362,6 +364,15 @@ def main():
 
     def up(a, t=tdt):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    if args.decode_only:
+        if not causal:
+            print("--decode-only needs a causal workload", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"workload": name, "decode": decode_measure(inp, dtype, torch, fg, dev,
+                                                                    min(args.cpu_seconds, 5.0))}),
+              flush=True)
+        return
 
     X, Wu, Wv, Wz, Wo = (up(a) for a in (inp.X, inp.W_u, inp.W_v, inp.W_z, inp.W_o))
     gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
