@@ -318,7 +318,7 @@ constexpr int kFoldTokens = 64;  // chunk tokens staged in LDS at a time
 // grid (ceil(e / 256), ceil(s / 32), B), 256 threads: thread = one value column, 32 state rows.
 template <class E>
 __global__ __launch_bounds__(256) void dec_fold_kernel(DecFoldArgs<E> p) {
-  __shared__ float kl[kFoldTokens][kFoldRows];
+  __shared__ __align__(16) float kl[kFoldTokens][kFoldRows];
   const int tid = threadIdx.x;
   const int col = blockIdx.x * 256 + tid;
   const int k0 = blockIdx.y * kFoldRows;
@@ -339,10 +339,16 @@ __global__ __launch_bounds__(256) void dec_fold_kernel(DecFoldArgs<E> p) {
     if (col < p.e) {
       const int nt = min(kFoldTokens, p.c - j0);
       const typename E::T* vb = p.Vc + (int64_t(b) * p.c + j0) * p.e + col;
+#pragma unroll 4
       for (int jj = 0; jj < nt; ++jj) {
         const float v = to_f32(vb[int64_t(jj) * p.e]);
+        const f32x4* row = reinterpret_cast<const f32x4*>(kl[jj]);  // broadcast reads, 16 B each
 #pragma unroll
-        for (int k = 0; k < kFoldRows; ++k) acc[k] = fmaf(kl[jj][k], v, acc[k]);
+        for (int k4 = 0; k4 < kFoldRows / 4; ++k4) {
+          const f32x4 kv = row[k4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[4 * k4 + m] = fmaf(kv[m], v, acc[4 * k4 + m]);
+        }
       }
     }
   }
