@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the forward pass of one FLASH layer.
+"""fp64 CPU oracle for the forward and backward pass of one FLASH layer.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute this module:
 only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
@@ -55,10 +55,19 @@ current chunk for the local term. Reading: every sequence of the batch is at the
 the linear state is folded after the last token of each chunk; n in the /n of the read-out is the
 length the forward normalises by, passed in.
 
+Backward pass
+-------------
+``flash_backward`` returns the gradients of L = Σ O ⊙ dO with respect to X, the four weight
+matrices, gamma and beta. The pages motivate the chunked form by its parallel training (FLASH page,
+"Mixed Chunk"; csdn page, section 1.4) but print no gradient; each step function above has a
+``*_backward`` counterpart derived by the chain rule, and ``flash_backward`` runs them in reverse
+order. The causal cross-chunk sum turns into an exclusive suffix sum over later chunks.
+
 Parity status: every function below is pinned by tests that do not re-type its formula
 (brute-force n×n matrices, the RNN recurrence, the chunk = n and A = I reductions, causality,
 permutation equivariance, closed-form values and hand-worked fixtures; the decode step against
-the rows of the causal forward and of the brute-force layer).
+the rows of the causal forward and of the brute-force layer; the backward against central finite
+differences of the forward and the adjoint identities of its linear steps).
 """
 
 from __future__ import annotations
@@ -85,6 +94,14 @@ __all__ = [
     "decode_init",
     "decode_step",
     "decode_sequence",
+    "silu_grad",
+    "rotary_transpose",
+    "local_quad_backward",
+    "global_linear_backward",
+    "prefix_states_backward",
+    "chunk_states_backward",
+    "scale_offset_heads_backward",
+    "flash_backward",
 ]
 
 
@@ -441,3 +458,183 @@ def decode_sequence(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, n=None, **norms):
     for t in range(T):
         out[:, t] = decode_step(state, X[:, t], t, n, W_u, W_v, W_z, gamma, beta, W_o, chunk, **norms)
     return out, state
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward pass (training).
+# ---------------------------------------------------------------------------------------------
+# The FLASH page motivates the chunked form by training ("Mixed Chunk": the causal linear term
+# stays parallel over chunks through a prefix sum) and the csdn page (section 1.4) by the cost of
+# the serial recurrence; neither writes the gradients down. They follow from the forward steps
+# above by the chain rule, taken here one step at a time in reverse order, for the scalar loss
+# L = Σ O ⊙ dO (dO is the gradient of whatever loss follows the layer).
+
+
+def silu_grad(x):
+    """Derivative of SiLU: d/dx [x σ(x)] = σ(x) (1 + x (1 − σ(x)))."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-x))
+    return sig * (1.0 + x * (1.0 - sig))
+
+
+def rotary_transpose(g, positions, base):
+    """Transpose of ``rotary`` at the same positions, applied to a gradient g [..., n, s]: each
+    pair is rotated by −m·θ_k (a rotation's transpose is its inverse)."""
+    g = _f64(g)
+    s = g.shape[-1]
+    k = np.arange(s // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * k / s)
+    angle = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    cos, sin = np.cos(angle), np.sin(angle)
+    even, odd = g[..., 0::2], g[..., 1::2]
+    out = np.empty_like(g)
+    out[..., 0::2] = even * cos + odd * sin
+    out[..., 1::2] = -even * sin + odd * cos
+    return out
+
+
+def local_quad_backward(Qq, Kq, V, dVq, chunk, causal, local_norm="c2"):
+    """Gradients of ``local_quad`` (V̂_quad_g = W_g V_g, W_g = relu(Q_g K_gᵀ / c)², masked when
+    causal) with respect to Q_quad, K_quad and V, given dV̂_quad. With A = Q_g K_gᵀ:
+    dW = dV̂ V_gᵀ, dV_g = W_gᵀ dV̂, and through relu², dA = dW ⊙ 2 relu(A/c) / c (zero where masked
+    or A < 0); dQ_g = dA K_g, dK_g = dAᵀ Q_g."""
+    Qq, Kq, V, dVq = _f64(Qq), _f64(Kq), _f64(V), _f64(dVq)
+    B, n, s = Qq.shape
+    G = _chunks(n, chunk)
+    dQ, dK, dV = np.zeros_like(Qq), np.zeros_like(Kq), np.zeros_like(V)
+    keep = np.tril(np.ones((chunk, chunk), dtype=bool)) if causal else np.ones((chunk, chunk), dtype=bool)
+    for b in range(B):
+        for g in range(G):
+            rows = slice(g * chunk, (g + 1) * chunk)
+            A = Qq[b, rows] @ Kq[b, rows].T
+            if local_norm == "c2":
+                w = np.maximum(A / chunk, 0.0) ** 2
+                dw_da = 2.0 * np.maximum(A / chunk, 0.0) / chunk
+            elif local_norm == "cs":
+                w = np.maximum(A, 0.0) ** 2 / (chunk * s)
+                dw_da = 2.0 * np.maximum(A, 0.0) / (chunk * s)
+            else:
+                raise ValueError(local_norm)
+            w = np.where(keep, w, 0.0)
+            dW = dVq[b, rows] @ V[b, rows].T
+            dA = np.where(keep, dW * dw_da, 0.0)
+            dQ[b, rows] = dA @ Kq[b, rows]
+            dK[b, rows] = dA.T @ Qq[b, rows]
+            dV[b, rows] = w.T @ dVq[b, rows]
+    return dQ, dK, dV
+
+
+def global_linear_backward(Ql, S, dVl, chunk, n, global_norm="n"):
+    """Gradients of ``global_linear`` (V̂_lin_g = scale_g Q_lin_g S_g) with respect to Q_lin and the
+    prefix states: dQ_lin_g = scale_g dV̂_lin_g S_gᵀ, dS_g = scale_g Q_lin_gᵀ dV̂_lin_g."""
+    Ql, S, dVl = _f64(Ql), _f64(S), _f64(dVl)
+    B = Ql.shape[0]
+    G = _chunks(n, chunk)
+    dQl, dS = np.zeros_like(Ql), np.zeros_like(S)
+    for g in range(G):
+        rows = slice(g * chunk, (g + 1) * chunk)
+        if global_norm == "n":
+            scale = 1.0 / n
+        elif global_norm == "count":
+            scale = 0.0 if g == 0 else 1.0 / (g * chunk)
+        else:
+            raise ValueError(global_norm)
+        dQl[:, rows] = scale * (dVl[:, rows] @ np.swapaxes(S[:, g], 1, 2))
+        dS[:, g] = scale * (np.swapaxes(Ql[:, rows], 1, 2) @ dVl[:, rows])
+    return dQl, dS
+
+
+def prefix_states_backward(dS, causal):
+    """Gradient of ``prefix_states`` with respect to the chunk summaries T. Causal: S_g sums T_h over
+    h < g, so dT_h sums dS_g over the later chunks g > h (an exclusive suffix sum; the last chunk's
+    summary gets zero). Non-causal: every T_h receives the sum of all dS_g."""
+    dS = _f64(dS)
+    dT = np.zeros_like(dS)
+    G = dS.shape[1]
+    if causal:
+        run = np.zeros_like(dS[:, 0])
+        for h in range(G - 1, -1, -1):
+            dT[:, h] = run
+            run = run + dS[:, h]
+    else:
+        total = dS.sum(axis=1)
+        for h in range(G):
+            dT[:, h] = total
+    return dT
+
+
+def chunk_states_backward(Kl, V, dT, chunk):
+    """Gradients of ``chunk_states`` (T_g = K_lin_gᵀ V_g): dK_lin_g = V_g dT_gᵀ, dV_g = K_lin_g dT_g."""
+    Kl, V, dT = _f64(Kl), _f64(V), _f64(dT)
+    n = Kl.shape[1]
+    G = _chunks(n, chunk)
+    dKl, dV = np.zeros_like(Kl), np.zeros_like(V)
+    for g in range(G):
+        rows = slice(g * chunk, (g + 1) * chunk)
+        dKl[:, rows] = V[:, rows] @ np.swapaxes(dT[:, g], 1, 2)
+        dV[:, rows] = Kl[:, rows] @ dT[:, g]
+    return dKl, dV
+
+
+def scale_offset_heads_backward(Z, gamma, dheads):
+    """Gradients of ``scale_offset_heads`` (head_h = Z ⊙ γ_h + β_h) given the four head gradients:
+    dZ = Σ_h γ_h ⊙ dhead_h, dγ_h = Σ_tokens Z ⊙ dhead_h, dβ_h = Σ_tokens dhead_h."""
+    Z, gamma = _f64(Z), _f64(gamma)
+    dZ = np.zeros_like(Z)
+    dgamma = np.zeros_like(gamma)
+    dbeta = np.zeros_like(gamma)
+    for h in range(4):
+        d = _f64(dheads[h])
+        dZ += gamma[h] * d
+        dgamma[h] = (Z * d).reshape(-1, Z.shape[-1]).sum(axis=0)
+        dbeta[h] = d.reshape(-1, Z.shape[-1]).sum(axis=0)
+    return dZ, dgamma, dbeta
+
+
+def flash_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal,
+                   local_norm="c2", global_norm="n", rope_base=None):
+    """Gradients of one FLASH layer (``flash_forward``, same arguments) for the loss Σ O ⊙ dO.
+
+    Returns a dict with dX [B, n, d], dW_u, dW_v [d, e], dW_z [d, s], dgamma, dbeta [4, s] and
+    dW_o [e, d], in float64. The forward steps are undone in reverse order: output projection,
+    gate, the global term (read-out, cross-chunk sum, chunk summaries), the local term, the rotary
+    embedding, the heads, SiLU, and the projection.
+    """
+    X, W_u, W_v, W_z, W_o, dO = (_f64(a) for a in (X, W_u, W_v, W_z, W_o, dO))
+    squeeze = X.ndim == 2
+    if squeeze:
+        X, dO = X[None], dO[None]
+    n = X.shape[1]
+    _, it = flash_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, local_norm=local_norm,
+                          global_norm=global_norm, return_intermediates=True, rope_base=rope_base)
+    U, V, Z = it["U"], it["V"], it["Z"]
+    Hu, Hv, Hz = X @ W_u, X @ W_v, X @ W_z
+    Vhat = it["Vq"] + it["Vl"]
+    # O = Y W_o, Y = U ⊙ V̂
+    dW_o = np.einsum("bne,bnd->ed", it["Y"], dO)
+    dY = dO @ W_o.T
+    dU = dY * Vhat
+    dVhat = dY * U
+    # the local and the global term both receive dV̂
+    dQq, dKq, dV = local_quad_backward(it["Qq"], it["Kq"], V, dVhat, chunk, causal, local_norm)
+    dQl, dS = global_linear_backward(it["Ql"], it["S"], dVhat, chunk, n, global_norm)
+    dT = prefix_states_backward(dS, causal)
+    dKl, dV_lin = chunk_states_backward(it["Kl"], V, dT, chunk)
+    dV = dV + dV_lin
+    dheads = [dQq, dKq, dQl, dKl]
+    if rope_base is not None:
+        dheads = [rotary_transpose(h, np.arange(n), rope_base) for h in dheads]
+    dZ, dgamma, dbeta = scale_offset_heads_backward(Z, gamma, dheads)
+    dHu, dHv, dHz = dU * silu_grad(Hu), dV * silu_grad(Hv), dZ * silu_grad(Hz)
+    dX = dHu @ W_u.T + dHv @ W_v.T + dHz @ W_z.T
+    grads = dict(
+        dX=dX[0] if squeeze else dX,
+        dW_u=np.einsum("bnd,bne->de", X, dHu),
+        dW_v=np.einsum("bnd,bne->de", X, dHv),
+        dW_z=np.einsum("bnd,bns->ds", X, dHz),
+        dgamma=dgamma,
+        dbeta=dbeta,
+        dW_o=dW_o,
+    )
+    return grads
