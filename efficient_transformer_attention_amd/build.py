@@ -7,7 +7,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflashgau.so")
-SOURCES = [os.path.join(PKG, "csrc", "flashgau.hip"), os.path.join(PKG, "csrc", "decode.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name) for name in ("flashgau.hip", "decode.hip", "backward.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

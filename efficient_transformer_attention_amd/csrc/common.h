@@ -17,6 +17,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, each with a private L2
 constexpr int kRowChunks = 8;   // 16-byte chunks per LDS row and K-stage (128 bytes)
@@ -82,6 +83,13 @@ __device__ __forceinline__ void load4(const float* p, float* o) {
 __device__ __forceinline__ float silu(float x) {
   const float t = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
   return x * __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+// d/dx [x σ(x)] = σ(x) (1 + x (1 − σ(x))); 0 and 1 in the limits (e^{-x} → inf gives σ = 0).
+__device__ __forceinline__ float silu_grad(float x) {
+  const float t = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + t);
+  return sg * fmaf(x, 1.0f - sg, 1.0f);
 }
 
 // ------------------------------------------------------------------------------ matrix cores

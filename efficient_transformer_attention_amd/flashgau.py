@@ -36,7 +36,8 @@ EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_st
            "flash_gau_forward", "flash_gau_forward_rope", "flash_gau_forward_timed",
            "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
-           "flash_gau_decode_step", "flashgau_strerror")
+           "flash_gau_decode_step", "flashgau_backward_workspace_size", "flash_gau_backward",
+           "flashgau_strerror")
 
 # Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
 STAGES = ("pack", "proj", "scores_states", "carry", "mix", "out")
@@ -86,6 +87,11 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_decode_step.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, ctypes.c_float, i64, i64,
                                         i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_decode_step.restype = ctypes.c_int
+    L.flashgau_backward_workspace_size.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
+    L.flashgau_backward_workspace_size.restype = ctypes.c_int
+    L.flash_gau_backward.argtypes = [vp] * 8 + [i64, ctypes.c_int, ctypes.c_float] + [i64] * 5 + \
+        [ctypes.c_int] + [vp] * 7 + [vp, sz, vp]
+    L.flash_gau_backward.restype = ctypes.c_int
     L.flashgau_strerror.argtypes = [ctypes.c_int]
     L.flashgau_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -340,3 +346,73 @@ def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, 
     if rc != OK:
         raise FlashGauError(rc, "flash_gau_decode_step")
     return out
+
+
+# ------------------------------------------------------------------------------------- backward
+
+GRAD_NAMES = ("dX", "dW_u", "dW_v", "dW_z", "dgamma", "dbeta", "dW_o")
+
+
+def backward_workspace_size(B, n, d, e, s, chunk, causal, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().flashgau_backward_workspace_size(B, n, d, e, s, chunk, int(bool(causal)), dtype,
+                                               ctypes.byref(out))
+    if rc != OK:
+        raise FlashGauError(rc, "flashgau_backward_workspace_size")
+    return out.value
+
+
+def backward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base, B, n, d, e, s,
+                 dtype, dX, dW_u, dW_v, dW_z, dgamma, dbeta, dW_o, workspace, workspace_bytes,
+                 stream) -> int:
+    """Direct call of flash_gau_backward with integer addresses; returns the library's code."""
+    return lib().flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, int(bool(causal)),
+                                    float(rope_base), B, n, d, e, s, dtype, dX, dW_u, dW_v, dW_z,
+                                    dgamma, dbeta, dW_o, workspace, workspace_bytes, stream)
+
+
+def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base=0.0,
+                       workspace=None, stream=None, out=None):
+    """Gradients of Σ O ⊙ dO for O = flash_gau_forward(X, ..., chunk, causal, rope_base) on the
+    GPU. Arguments as flash_gau_forward, plus dO [B, n, d] of X's dtype. Returns a dict with dX
+    [B, n, d], dW_u, dW_v [d, e], dW_z [d, s], dW_o [e, d] (X's dtype) and dgamma, dbeta [4, s]
+    (float32). ``out`` may hold preallocated tensors under those names; ``workspace`` (uint8) is
+    allocated when not given."""
+    import torch
+    B, n, d = X.shape
+    e = W_u.shape[1]
+    s = W_z.shape[1]
+    dt = _dtype_code(X.dtype)
+    for name, t, shape in (("W_u", W_u, (d, e)), ("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)),
+                           ("W_o", W_o, (e, d)), ("dO", dO, (B, n, d))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if t.dtype != X.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from X dtype {X.dtype}")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if tuple(t.shape) != (4, s) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [4, {s}]")
+    tensors = (X, W_u, W_v, W_z, gamma, beta, W_o, dO)
+    dev = X.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous (row-major)")
+    shapes = dict(dX=((B, n, d), X.dtype), dW_u=((d, e), X.dtype), dW_v=((d, e), X.dtype),
+                  dW_z=((d, s), X.dtype), dgamma=((4, s), torch.float32),
+                  dbeta=((4, s), torch.float32), dW_o=((e, d), X.dtype))
+    grads = dict(out or {})
+    for k, (shape, tdt) in shapes.items():
+        if k not in grads:
+            grads[k] = torch.empty(shape, dtype=tdt, device=dev)
+    nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = backward_raw(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n, d, e,
+                      s, dt, *(grads[k].data_ptr() for k in GRAD_NAMES), workspace.data_ptr(),
+                      workspace.numel(), stream)
+    if rc != OK:
+        raise FlashGauError(rc, "flash_gau_backward")
+    return grads

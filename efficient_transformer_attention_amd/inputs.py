@@ -95,6 +95,13 @@ def make_inputs(B, n, d, e, s, chunk, causal, dtype, seed=0, gamma_std=0.02, bet
         W_o=round_to(W_o, dtype), chunk=int(chunk), causal=bool(causal), dtype=dtype)
 
 
+def make_output_grad(B, n, d, dtype, seed=0, std=1.0) -> np.ndarray:
+    """The gradient dO [B, n, d] arriving at the layer's output for a backward pass: N(0, std²),
+    drawn from ``numpy.random.default_rng(seed + 1000)`` and rounded to the storage dtype."""
+    rng = np.random.default_rng(seed + 1000)
+    return round_to(rng.standard_normal((B, n, d)) * std, dtype)
+
+
 def workload_inputs(name: str, seed: int = 0, **kw) -> LayerInputs:
     B, n, d, e, s, chunk, causal, dtype = WORKLOADS[name]
     return make_inputs(B, n, d, e, s, chunk, causal, dtype, seed=seed, **kw)

@@ -255,6 +255,42 @@ int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes
                           flashgau_dtype dtype, void* o, void* state, size_t state_bytes,
                           void* hip_stream);
 
+/* ------------------------------------------------------------------------------ backward
+ * Gradients of one FLASH layer for training. The FLASH page motivates the chunked form by its
+ * parallel training ("Mixed Chunk": the causal global term stays a prefix sum over chunks) but
+ * prints no gradient; these are the chain rule of the forward above for the scalar loss
+ * L = Σ O ⊙ dO, with the forward's readings (local relu²(·/c), global /n, SiLU on Z, the causal
+ * state of chunk g summing chunks h < g, so its gradient sums over the chunks after h).
+ * The call recomputes the forward's intermediates itself (nothing has to be kept from a forward
+ * call), accumulates every product in fp32 and rounds intermediates and results to dtype. */
+
+/* Bytes of device workspace flash_gau_backward needs (host-only; same validation as
+ * flash_gau_forward; 0 for an empty problem). Returns FLASHGAU_OK or an error code. */
+int flashgau_backward_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                                     int64_t chunk, int causal, flashgau_dtype dtype,
+                                     size_t* out_bytes);
+
+/* Gradients of L = Σ O ⊙ dO, O = the forward (flash_gau_forward, or flash_gau_forward_rope when
+ * rope_base > 0) of the same inputs:
+ *   X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal: as for flash_gau_forward
+ *   dO       [B, n, d]   dtype, device: the gradient arriving at the layer's output
+ *   rope_base: 0 for no position encoding, > 0 as flash_gau_forward_rope (s even)
+ *   dX       [B, n, d]   dtype, device
+ *   dW_u, dW_v [d, e], dW_z [d, s], dW_o [e, d]   dtype, device
+ *   dgamma, dbeta [4, s] fp32, device (rows Q_quad, K_quad, Q_lin, K_lin)
+ *   workspace, workspace_bytes: at least flashgau_backward_workspace_size() bytes (its first
+ *            flashgau_workspace_size() bytes hold the forward's intermediates, laid out as the
+ *            forward's FLASHGAU_WS_* regions)
+ * Every output is fully overwritten (with B == 0 or n == 0 the weight gradients are zeros).
+ * Tensor pointers 16-byte aligned, gamma/beta/dgamma/dbeta 4-byte aligned. The outputs and the
+ * workspace must not overlap one another or any input. Returns FLASHGAU_OK or an error code. */
+int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                       const float* gamma, const float* beta, const void* W_o, const void* dO,
+                       int64_t chunk, int causal, float rope_base, int64_t B, int64_t n, int64_t d,
+                       int64_t e, int64_t s, flashgau_dtype dtype, void* dX, void* dW_u,
+                       void* dW_v, void* dW_z, float* dgamma, float* dbeta, void* dW_o,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Static, human-readable text for a return code ("unknown error" for other values). */
 const char* flashgau_strerror(int code);
 

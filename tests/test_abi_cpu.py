@@ -278,3 +278,76 @@ def test_forward_rope_base_validated(base):
                              base_ptr + (4 << 30), base_ptr + (5 << 30), base_ptr + (6 << 30), c, 1, base,
                              B, n, d, e, s, fg.BF16, base_ptr + (7 << 30), base_ptr + (8 << 30), ws, None)
     assert rc == fg.ERR_BAD_SHAPE
+
+
+# ----------------------------------------------------------------------------------- backward
+
+def test_backward_workspace_holds_the_forward_layout_first():
+    for args in ((1, 128, 64, 128, 128, 64, True, fg.BF16), (2, 216, 200, 136, 24, 72, False, fg.F32),
+                 (8, 4096, 768, 1536, 128, 256, True, fg.BF16)):
+        fwd = fg.workspace_size(*args)
+        bwd = fg.backward_workspace_size(*args)
+        assert bwd > fwd
+        assert bwd % 256 == 0
+    assert fg.backward_workspace_size(0, 128, 64, 128, 128, 64, True, fg.BF16) == 0
+
+
+@pytest.mark.parametrize("shape,code", [
+    ((1, 100, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),   # chunk does not divide n
+    ((1, 128, 60, 128, 128, 64), fg.ERR_UNSUPPORTED),  # d not a multiple of 8
+    ((1, 128, 64, 128, 128, 0), fg.ERR_BAD_SHAPE),     # chunk 0
+    ((-1, 128, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),
+])
+def test_backward_shape_validation(shape, code):
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.backward_workspace_size(*shape, True, fg.BF16)
+    assert ei.value.code == code
+
+
+def _bcall(**over):
+    B, n, d, e, s, c = (SHAPE[k] for k in ("B", "n", "d", "e", "s", "chunk"))
+    ws = fg.backward_workspace_size(B, n, d, e, s, c, True, fg.BF16)
+    base = 1 << 40
+    names = ("X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "dO", "dX", "dW_u", "dW_v", "dW_z",
+             "dgamma", "dbeta", "dW_o", "workspace")
+    ptrs = {k: base + (i << 30) for i, k in enumerate(names)}
+    ptrs["workspace_bytes"] = ws
+    ptrs["rope_base"] = 0.0
+    ptrs.update(over)
+    return fg.backward_raw(*(ptrs[k] for k in names[:8]), c, 1, ptrs["rope_base"], B, n, d, e, s,
+                           fg.BF16, *(ptrs[k] for k in names[8:15]), ptrs["workspace"],
+                           ptrs["workspace_bytes"], None)
+
+
+@pytest.mark.parametrize("which", ["X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "dO", "dX",
+                                   "dW_u", "dW_v", "dW_z", "dgamma", "dbeta", "dW_o", "workspace"])
+def test_backward_null_pointer_rejected(which):
+    assert _bcall(**{which: None}) == fg.ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("which,delta", [("X", 8), ("dO", 2), ("dX", 4), ("dW_o", 8),
+                                         ("dgamma", 2), ("workspace", 8)])
+def test_backward_misaligned_pointer_rejected(which, delta):
+    names = ("X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "dO", "dX", "dW_u", "dW_v", "dW_z",
+             "dgamma", "dbeta", "dW_o", "workspace")
+    assert _bcall(**{which: (1 << 40) + (names.index(which) << 30) + delta}) == fg.ERR_MISALIGNED
+
+
+def test_backward_small_workspace_rejected():
+    assert _bcall(workspace_bytes=4096) == fg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("over", [
+    dict(dX=1 << 40),                                   # dX is X
+    dict(dW_u=(1 << 40) + (10 << 30)),                   # dW_u is dW_v
+    dict(workspace=(1 << 40) + (7 << 30)),               # workspace is dO
+    dict(dgamma=(1 << 40) + (15 << 30) + 4096),          # dgamma inside the workspace
+    dict(dbeta=(1 << 40) + (12 << 30)),                  # dbeta is dgamma
+])
+def test_backward_aliasing_rejected(over):
+    assert _bcall(**over) == fg.ERR_ALIASING
+
+
+@pytest.mark.parametrize("base", [-1.0, float("nan"), float("inf")])
+def test_backward_rope_base_validated(base):
+    assert _bcall(rope_base=base) == fg.ERR_BAD_SHAPE
