@@ -17,7 +17,9 @@ For a causal workload the line also carries a "decode" object: the same batch an
 decoded one token per sequence per step (flash_gau_decode_step), timed over one whole chunk of
 positions (c .. 2c-1, the last step folding the chunk into the state) after chunk 0 has filled the
 state untimed, with its HBM roofline (algorithmic bytes per step, see decode_bytes) and the
-oracle's decode step timed on the host. Two more objects time the same layer with the rotary
+oracle's decode step timed on the host. The "backward" object times flash_gau_backward on the same
+batch (2 x the forward's algorithmic FLOPs), with the oracle's backward on one sequence as its CPU
+baseline and parity check. Two more objects time the same layer with the rotary
 embedding (flash_gau_forward_rope) and compare FLASH-Quad (chunk = n: one quadratic chunk, no
 global term) with FLASH (the workload's chunk) on longer causal sequences of the same width.
 """
@@ -87,17 +89,26 @@ def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
 
 
 PROFILE_BYTES = os.path.join(ROOT, "profiles", "flash_layer_c3_hbm_bytes.txt")
-LIB_SOURCE = os.path.join(ROOT, "efficient_transformer_attention_amd", "csrc", "flashgau.hip")
+# the forward's sources, hashed in this order
+LIB_SOURCES = tuple(os.path.join(ROOT, "efficient_transformer_attention_amd", "csrc", f)
+                    for f in ("flashgau.hip", "kernels.h", "common.h"))
+
+
+def forward_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in LIB_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
     """Per-launch HBM-side bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of `kernel` from the
     committed rocprofv3 summary, or None when the summary is for another workload or the library
     source has changed since the counters were taken."""
-    import hashlib
     if workload != "c3_causal_bf16_n4096" or not os.path.exists(PROFILE_BYTES):
         return None
-    sha = hashlib.sha256(open(LIB_SOURCE, "rb").read()).hexdigest()
+    sha = forward_source_sha()
     text = open(PROFILE_BYTES).read()
     if f"library source sha256: {sha}" not in text:
         return None
@@ -161,6 +172,65 @@ def cpu_baseline(inp, seconds):
                      f"fp64 NumPy oracle, median of {len(times)} runs ({med:.2f} s each); "
                      f"host has {os.cpu_count()} logical CPUs"}
     return rec, ref
+
+
+def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10):
+    """Times flash_gau_backward on the whole batch (dO drawn by inputs.make_output_grad) and the
+    fp64 oracle's backward on sequence 0; checks the GPU gradients of a call whose dO is zero on
+    every other sequence against that oracle run. Algorithmic work: every contraction of the
+    forward has two gradient contractions of its size, so 2 x the forward's algorithmic FLOPs
+    (the recomputed forward intermediates are not counted)."""
+    import oracle
+    from efficient_transformer_attention_amd import inputs as gen
+    B, n, d = inp.X.shape
+    e, s, c, causal = inp.W_u.shape[1], inp.W_z.shape[1], inp.chunk, inp.causal
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    args = [up(inp.X), up(inp.W_u), up(inp.W_v), up(inp.W_z), up(inp.gamma, torch.float32),
+            up(inp.beta, torch.float32), up(inp.W_o)]
+    dO_np = gen.make_output_grad(B, n, d, dtype)
+    dO = up(dO_np)
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+    ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8,
+                     device=dev)
+    out = fg.flash_gau_backward(*args, dO, c, causal, workspace=ws)
+    for _ in range(2):
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 2.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
+    rec = {"workload": f"backward of the same layer and batch", "steps": steps,
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
+           "alg_gflop": round(flops / 1e9, 2),
+           "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK["bf16"], 4) if dtype == "bf16" else None}
+    if cpu_seconds > 0:
+        dO_np[1:] = 0.0
+        g = fg.flash_gau_backward(*args, up(dO_np), c, causal, workspace=ws, out=out)
+        torch.cuda.synchronize(dev)
+        got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in g.items()}
+        times, ref = [], None
+        t_start = time.perf_counter()
+        while not times or time.perf_counter() - t_start < cpu_seconds:
+            t1 = time.perf_counter()
+            ref = oracle.flash_backward(inp.X[:1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta,
+                                        inp.W_o, dO_np[:1], c, causal)
+            times.append(time.perf_counter() - t1)
+        med = statistics.median(times)
+        rec["cpu_baseline"] = {"value": n / med, "unit": "tokens/s", "kind": "oracle",
+                               "sample": f"backward of sequence 0 ({n} tokens), fp64 NumPy oracle, "
+                                         f"median of {len(times)} runs ({med:.2f} s each)"}
+        rec["max_rel_err_seq0"] = {
+            k: float(np.abs((got[k][:1] if k == "dX" else got[k]) - ref[k]).max() / np.abs(ref[k]).max())
+            for k in fg.GRAD_NAMES}
+    return rec
 
 
 def decode_bytes(B, d, e, s, c, esz, i):
@@ -327,6 +397,10 @@ def main():
                     help="skip the causal decoding measurement")
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the causal decoding measurement and print its JSON object")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the backward-pass measurement (no CPU baseline), one JSON line")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rotary-embedding and FLASH-Quad (chunk = n) timings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -365,6 +439,10 @@ def main():
     def up(a, t=tdt):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
 
+    if args.backward_only:
+        print(json.dumps({"workload": name, "backward": backward_measure(
+            inp, dtype, torch, fg, dev, 0.0, steps=args.steps)}), flush=True)
+        return
     if args.decode_only:
         if not causal:
             print("--decode-only needs a causal workload", file=sys.stderr)
@@ -456,6 +534,12 @@ def main():
     if causal and not args.no_decode:
         decode = decode_measure(inp, dtype, torch, fg, dev, min(args.cpu_seconds, 5.0))
 
+    backward = None
+    if not args.no_backward:
+        print("[bench] backward pass", file=sys.stderr, flush=True)
+        backward = backward_measure(inp, dtype, torch, fg, dev, min(args.cpu_seconds, 10.0))
+        backward["train_step_tokens_per_s"] = round(B * n / ((ms_step + backward["ms_per_step"]) * 1e-3), 1)
+
     rope = quad = None
     if not args.no_extras:
         print("[bench] rotary embedding and FLASH-Quad timings", file=sys.stderr, flush=True)
@@ -495,6 +579,7 @@ def main():
         "cpu_baseline": cpu,
         "max_rel_err_seq0": max_rel_err,
         "decode": decode,
+        "backward": backward,
         "rope": rope,
         "flash_vs_flash_quad": quad,
     }
