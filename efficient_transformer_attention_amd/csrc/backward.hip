@@ -616,7 +616,7 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
 }
 
 // ------------------------------------------------------------------------------ dz
-constexpr int kZRows = 128;  // token rows per dz workgroup (a multiple of 8)
+constexpr int kZRows = 32;  // token rows per dz workgroup (a multiple of 8)
 
 template <class E>
 struct DZArgs {
@@ -664,7 +664,8 @@ __global__ __launch_bounds__(256) void dz_kernel(DZArgs<E> p) {
     const int nheads = p.lin ? 4 : 2;
     const int row_end = min(p.M, int(blockIdx.x + 1) * kZRows);
     for (int rb = int(blockIdx.x) * kZRows + 8 * rg; rb < row_end; rb += 8 * RG) {
-      T z0[8], z1[8];
+      alignas(16) T z0[8];
+      alignas(16) T z1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int row = rb + k;
@@ -710,12 +711,13 @@ __global__ __launch_bounds__(256) void dz_kernel(DZArgs<E> p) {
         z1[k] = from_f32<E>(d1);
       }
       const int64_t bg = rb / p.c, t = rb % p.c;  // 8 rows inside one chunk (c % 8 == 0)
-      T* o0 = p.dHzt + (bg * p.s + f0) * p.c + t;
+      T* o0 = p.dHzt + (bg * p.s + f0) * p.c + t;  // 16-byte aligned: t and c are multiples of 8
       T* o1 = o0 + p.c;
+      constexpr int kVec = 16 / int(sizeof(T));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        o0[k] = z0[k];
-        o1[k] = z1[k];
+      for (int v = 0; v < 8 / kVec; ++v) {
+        *reinterpret_cast<u32x4*>(o0 + v * kVec) = *reinterpret_cast<const u32x4*>(z0 + v * kVec);
+        *reinterpret_cast<u32x4*>(o1 + v * kVec) = *reinterpret_cast<const u32x4*>(z1 + v * kVec);
       }
     }
   }
@@ -897,20 +899,28 @@ __global__ __launch_bounds__(256) void wreduce_kernel(RArgs<E> p, int64_t total4
   store4(J.out + i4 * 4, s[0], s[1], s[2], s[3]);
 }
 
-// dγ, dβ [4, s] each from the dz partials [nzb, 8, s]: 64 outputs per workgroup, 16 lanes per
-// output each summing every 16th partial, then a fixed-order sum of the 16.
+// dγ, dβ [4, s] each from the dz partials [nzb, 8, s]: 16 outputs per workgroup, 64 lanes per
+// output each summing every 64th partial (four loads in flight), then a fixed-order sum of the 64.
 __global__ __launch_bounds__(1024) void gbreduce_kernel(const float* gbpart, int nzb, int s,
                                                        float* dgamma, float* dbeta) {
-  __shared__ float red[16][64];
-  const int o = threadIdx.x & 63, l = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + o;  // output index in [0, 8 s)
+  __shared__ float red[64][16 + 1];
+  const int o = threadIdx.x & 15, l = threadIdx.x >> 4;
+  const int j = blockIdx.x * 16 + o;  // output index in [0, 8 s)
+  const int64_t stride = int64_t(8) * s;
   float v = 0.0f;
-  if (j < 8 * s)
-    for (int b = l; b < nzb; b += 16) v += gbpart[int64_t(b) * 8 * s + j];
+  if (j < 8 * s) {
+    int b = l;
+    for (; b + 192 < nzb; b += 256) {
+      const float x0 = gbpart[int64_t(b) * stride + j], x1 = gbpart[int64_t(b + 64) * stride + j];
+      const float x2 = gbpart[int64_t(b + 128) * stride + j], x3 = gbpart[int64_t(b + 192) * stride + j];
+      v += (x0 + x1) + (x2 + x3);
+    }
+    for (; b < nzb; b += 64) v += gbpart[int64_t(b) * stride + j];
+  }
   red[l][o] = v;
   __syncthreads();
   if (l == 0 && j < 8 * s) {
-    for (int k = 1; k < 16; ++k) v += red[k][o];
+    for (int k = 1; k < 64; ++k) v += red[k][o];
     if (j < 4 * s)
       dgamma[j] = v;
     else
@@ -1190,7 +1200,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     a.splits = int(bp.splits);
     hipLaunchKernelGGL(wreduce_kernel<E>, dim3(unsigned(cdiv(first, 256))), dim3(256), 0, stream, a,
                        first);
-    hipLaunchKernelGGL(gbreduce_kernel, dim3(unsigned(cdiv(8 * s, 64))), dim3(1024), 0, stream,
+    hipLaunchKernelGGL(gbreduce_kernel, dim3(unsigned(cdiv(8 * s, 16))), dim3(1024), 0, stream,
                        Rf(BR_GBPART), int(bp.nzb), s, dgamma, dbeta);
   }
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
