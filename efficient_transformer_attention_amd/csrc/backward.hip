@@ -5,11 +5,12 @@
 // page motivates the chunked form by its parallel training and prints no gradient, so the steps
 // below are the chain rule of the forward's steps, in reverse order, for the loss Σ O ⊙ dO:
 //
-//   recompute  pack, proj (also the pre-activations and V token-major), per-chunk scores P and the
+//   recompute  pack, proj (the gate's columns too; the pre-activations and V token-major), per-chunk scores P and the
 //              exclusive prefix states S_g / n (the forward's own kernels)
-//   mixb       per (chunk, value-column tile, token tile) three GEMMs into three accumulators:
-//              H_uᵀ = W_uᵀXᵀ, V̂ᵀ = [V_gᵀ | S_gᵀ][P_g | Q_lin,g]ᵀ and dYᵀ = W_o dOᵀ; epilogue
-//              Y = U ⊙ V̂ (for dW_o), dV̂ = dY ⊙ U, dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
+//   mixb       per (chunk, value-column tile, token tile) two GEMMs into two accumulators:
+//              V̂ᵀ = [V_gᵀ | S_gᵀ][P_g | Q_lin,g]ᵀ and dYᵀ = W_o dOᵀ; epilogue, with H_u = X W_u
+//              from the recomputing projection: Y = U ⊙ V̂ (for dW_o), dV̂ = dY ⊙ U,
+//              dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
 //   xpose      token-contiguous copies of X, dO and the heads (the weight gradients and the
 //              per-chunk contractions over tokens read K-contiguous rows)
 //   dscores    per chunk dW = dV̂ Vᵀ and A = Q_quad K_quadᵀ again: Pᵀ and dA = dW ⊙ 2 relu(A/c) / c
@@ -75,8 +76,7 @@ struct MixBArgs {
   const T* St;   // causal [nbg, e, s], non-causal [B, e, s] (already / n)
   const T* P;    // [nbg, c, c]: P[i][j], query i, key j
   const T* Ql;   // [M, s]
-  const T* X;    // [M, d]
-  const T* WuT;  // [e, d]
+  const T* Hu;   // [M, e]: X W_u before SiLU (the recomputing projection's)
   const T* Wo;   // [e, d], the input layout
   const T* dO;   // [M, d]
   T* Yt;         // [nbg, e, c]
@@ -107,19 +107,6 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
   const int64_t slot = p.causal ? bg : bg / p.G;
   const int nkd = ksteps<E>(p.d);
 
-  G gu;  // H_uᵀ
-  gu.zero();
-  {
-    const Src a = make_src(p.WuT, m0, p.d, E::kSize, p.e - m0, BT, p.d);
-    const Src b = make_src(p.X, tok0 + n0, p.d, E::kSize, p.c - n0, BT, p.d);
-    gu.run(lds, nkd,
-           [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-             sa = a;
-             sb = b;
-             ka = kb = t * kStageBytes;
-           },
-           NoPre(), wave, wm, wn, lane);
-  }
   G gd;  // dYᵀ
   gd.zero();
   {
@@ -161,9 +148,17 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
           wave, wm, wn, lane);
   }
 
+  // H_u of the lane's four value columns r.. of token column cl (tile-local), zeros off the edge
+  auto load_hu = [&](int r, int cl, float* hu) {
+    const int j = m0 + r, i = n0 + cl;
+    if (j < p.e && i < p.c) {
+      load4f(p.Hu + (tok0 + i) * p.e + j, hu);
+    } else {
+      hu[0] = hu[1] = hu[2] = hu[3] = 0.0f;
+    }
+  };
   // what: 0 Y = U ⊙ V̂, 1 dV̂ = dY ⊙ U, 2 dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
-  auto value = [&](int what, int fi, int fj, int k, float vh) -> float {
-    const float hu = gu.acc[fi][fj][k], dy = gd.acc[fi][fj][k];
+  auto value = [&](int what, float hu, float dy, float vh) -> float {
     if (what == 0) return silu(hu) * vh;
     if (what == 1) return dy * silu(hu);
     return dy * vh * silu_grad(hu);
@@ -174,9 +169,11 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
   for (int w = 0; w < 3; ++w) {
     g.template stage_cols<T>(
         lds, wave, wm, wn, lane,
-        [&](int fi, int fj, int, int, const f32x4& v, T* out) {
+        [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
+          float hu[4];
+          load_hu(r, cl, hu);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w, fi, fj, k, v[k]));
+          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w, hu[k], gd.acc[fi][fj][k], v[k]));
         },
         [&](int r, int cl, const u32x4& chunk) {
           const int j = m0 + r, i = n0 + cl;
@@ -190,9 +187,11 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
   for (int w = 0; w < 2; ++w) {
     g.template stage_rows<T>(
         lds, wave, wm, wn, lane,
-        [&](int fi, int fj, int, int, const f32x4& v, T* out) {
+        [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
+          float hu[4];
+          load_hu(r, cl, hu);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w + 1, fi, fj, k, v[k]));
+          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w + 1, hu[k], gd.acc[fi][fj][k], v[k]));
         },
         [&](int cl, int r, const u32x4& chunk) {
           const int j = m0 + r, i = n0 + cl;
@@ -937,7 +936,7 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t words) {
 
 // ------------------------------------------------------------------------------ host plan
 enum BRegion {
-  BR_HR, BR_VR, BR_XT, BR_DOT, BR_QQT, BR_KQT, BR_QLT, BR_KLR, BR_SR, BR_YT, BR_DVHT, BR_DVHR,
+  BR_HU, BR_HR, BR_VR, BR_XT, BR_DOT, BR_QQT, BR_KQT, BR_QLT, BR_KLR, BR_SR, BR_YT, BR_DVHT, BR_DVHR,
   BR_DHUT, BR_DHUR, BR_PT, BR_DAR, BR_DAT, BR_DTT, BR_DCARRY, BR_DTR, BR_DQQ, BR_DKQ, BR_DQL,
   BR_DKL, BR_DHVR, BR_DHVT, BR_DHZR, BR_DHZT, BR_WPART, BR_GBPART, BR_COUNT
 };
@@ -984,6 +983,7 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
   int64_t t0;
   if (!mul_ok(M, e + s, &cnt[BR_HR])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(M, e, &cnt[BR_VR])) return FLASHGAU_ERR_BAD_SHAPE;
+  cnt[BR_HU] = cnt[BR_VR];
   if (!mul_ok(M, d, &cnt[BR_XT])) return FLASHGAU_ERR_BAD_SHAPE;
   cnt[BR_DOT] = cnt[BR_XT];
   if (!mul_ok(M, s, &cnt[BR_QQT])) return FLASHGAU_ERR_BAD_SHAPE;
@@ -1062,9 +1062,9 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   // ---- recompute the forward's intermediates
   launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   {
-    ProjArgs<E> a{Xp, WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
-                  int(pl.n), rope, log2_base, R(BR_HR), R(BR_VR)};
-    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(e + s, S::kProjBN);
+    ProjArgs<E> a{Xp, WcatT, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
+                  int(pl.n), rope, log2_base, R(BR_HR), R(BR_VR), R(BR_HU)};
+    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
     hipLaunchKernelGGL(
         (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, true>),
         dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
@@ -1088,7 +1088,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
 
   // ---- gate, output projection and V̂
   {
-    MixBArgs<E> a{Vt, St, P, Ql, Xp, WcatT, reinterpret_cast<const T*>(W_o), dOp, R(BR_YT),
+    MixBArgs<E> a{Vt, St, P, Ql, R(BR_HU), reinterpret_cast<const T*>(W_o), dOp, R(BR_YT),
                   R(BR_DVHT), R(BR_DVHR), R(BR_DHUT), R(BR_DHUR), d, nbg, G, c, e, s, causal,
                   int(lin)};
     const int64_t nb = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
