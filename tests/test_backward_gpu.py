@@ -105,3 +105,64 @@ def test_backward_of_an_empty_batch_zeroes_the_weight_gradients():
     torch.cuda.synchronize()
     for k in ("dW_u", "dW_v", "dW_z", "dW_o", "dgamma", "dbeta"):
         assert float(g[k].float().abs().max()) == 0.0, k
+
+
+@pytest.mark.parametrize("name", ["c2_causal_bf16_n1024", "c3_causal_bf16_n4096"])
+def test_backward_full_size_through_sequence_zero(name):
+    # The full batch runs in the launch configuration of the benchmark; dO is zero on every
+    # sequence but the first, so each weight gradient is sequence 0's contribution alone and the
+    # oracle needs only that sequence. The other sequences' dX must be exactly zero.
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
+    print(f"[gpu case] backward full size {name}", flush=True)
+    inp = gen.workload_inputs(name, seed=0)
+    dO = gen.make_output_grad(B, n, d, dtype, seed=0)
+    dO[1:] = 0.0
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    grads = fg.flash_gau_backward(*args, _dev(dO, dtype), c, causal)
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    ref = oracle.flash_backward(inp.X[:1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o,
+                                dO[:1], c, causal)
+    assert np.abs(got["dX"][1:]).max() == 0.0
+    errs = {k: _rel(got[k][:1] if k == "dX" else got[k], ref[k]) for k in fg.GRAD_NAMES}
+    print("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k in fg.GRAD_NAMES:
+        assert errs[k] <= TOL[dtype], (k, errs[k])
+
+
+def test_forward_and_backward_replayed_from_a_hip_graph_match_eager():
+    # One forward and one backward captured into a HIP graph (torch.cuda.CUDAGraph) on a side
+    # stream; every replay must reproduce the eager outputs bitwise. Neither path records a memset.
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype = 2, 256, 64, 128, 32, 64, True, "bf16"
+    print("[gpu case] forward + backward graph replay", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=8, gamma_std=0.3, beta_std=0.1)
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    dO = _dev(gen.make_output_grad(B, n, d, dtype, seed=8), dtype)
+    dt = fg.BF16
+    fws = torch.empty((fg.workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8, device="cuda")
+    bws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8,
+                      device="cuda")
+    O_eager = fg.flash_gau_forward(*args, c, causal, workspace=fws).clone()
+    g_eager = {k: v.clone() for k, v in fg.flash_gau_backward(*args, dO, c, causal, workspace=bws).items()}
+    torch.cuda.synchronize()
+    O = torch.empty_like(O_eager)
+    grads = {k: torch.empty_like(v) for k, v in g_eager.items()}
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=stream):
+        fg.flash_gau_forward(*args, c, causal, out=O, workspace=fws, stream=stream.cuda_stream)
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=bws, stream=stream.cuda_stream, out=grads)
+    for rep in range(3):
+        O.zero_()
+        for v in grads.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O, O_eager), rep
+        for k in fg.GRAD_NAMES:
+            assert torch.equal(grads[k], g_eager[k]), (rep, k)
