@@ -5,15 +5,12 @@
 // page motivates the chunked form by its parallel training and prints no gradient, so the steps
 // below are the chain rule of the forward's steps, in reverse order, for the loss Σ O ⊙ dO:
 //
-//   recompute  pack, proj (the gate's columns too; the pre-activations and V token-major), per-chunk scores P and the
-//              exclusive prefix states S_g / n (the forward's own kernels)
+//   recompute  pack, proj (the gate's columns too, and the pre-activations), per-chunk scores P
+//              and the exclusive prefix states S_g / n (the forward's own kernels)
 //   mixb       per (chunk, value-column tile, token tile) two GEMMs into two accumulators:
-//              V̂ᵀ = [V_gᵀ | S_gᵀ][P_g | Q_lin,g]ᵀ and dYᵀ = W_o dOᵀ; epilogue, with H_u = X W_u
-//              from the recomputing projection: Y = U ⊙ V̂ (for dW_o), dV̂ = dY ⊙ U,
-//              dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
-//   xpose      token-contiguous copies of X, dO and the heads (the weight gradients and the
-//              per-chunk contractions over tokens read K-contiguous rows)
-//   dscores    per chunk dW = dV̂ Vᵀ and A = Q_quad K_quadᵀ again: Pᵀ and dA = dW ⊙ 2 relu(A/c) / c
+//              V̂ᵀ = [V_gᵀ | S_gᵀ][P_g | Q_lin,g]ᵀ and dYᵀ = W_o dOᵀ; epilogue, with H_u = X W_u from
+//              the projection: Y = U ⊙ V̂ (for dW_o), dV̂ = dY ⊙ U, dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
+//   dscores    per chunk dW = dV̂ Vᵀ and A = Q_quad K_quadᵀ again: dA = dW ⊙ 2 relu(A/c) / c
 //              (masked); dQ_lin = dV̂ (S_g/n)ᵀ; and, in the same launch, the state gradients
 //              dS_g = Q_lin,gᵀ dV̂_g / n summed over the LATER chunks (the forward's states and
 //              carry kernels walking the chunks last to first)
@@ -21,11 +18,14 @@
 //   dv         dVᵀ = [dV̂ᵀ | dTᵀ][Pᵀ | K_lin]ᵀ per chunk, times SiLU'(H_v)
 //   dz         the rotary transpose, dZ = Σ γ_h dhead_h, dH_z, and partial sums for dγ, dβ
 //   dx         dX = dH_u W_uᵀ + dH_v W_vᵀ + dH_z W_zᵀ (the input weights as stored)
-//   wgrad      dW = Xᵀ dH and dW_o = Yᵀ dO, split over chunk ranges into fp32 partials
+//   wgrad      dW = Xᵀ dH and dW_o = Yᵀ dO, split over token ranges into fp32 partials
 //   reduce     partial sums → dW_u, dW_v, dW_z, dW_o, dγ, dβ
 //
-// Every GEMM is the forward's TileGemm (K-contiguous operands straight into LDS, MFMA). Tiles are
-// 128 x 128 with 8 waves for bf16 and 64 x 64 with 4 waves for fp32.
+// Every GEMM is the forward's TileGemm. A contraction over tokens (a chunk's, or all of them)
+// reads its token-major operands as MN-major tiles (K rows of M-contiguous elements, fragments
+// through the transposing LDS reads), so every intermediate is stored once, token-major, and
+// nothing is transposed in memory. Tiles are 128 x 128 with 8 waves for bf16 and 64 x 64 with
+// 4 waves for fp32 (256-byte rows either way, as the MN-major tiles need).
 
 #include "kernels.h"
 
@@ -43,13 +43,21 @@ template <> struct BShapes<F32> {
 static_assert(BShapes<BF16>::BT == Shapes<BF16>::kScoresBT && BShapes<F32>::BT == Shapes<F32>::kScoresBT,
               "backward tiles must match the scores tiles");
 
-template <class E>
+constexpr int KK = kLayoutK, MN = kLayoutMN;
+
+template <class E, int AL = KK, int BL = KK>
 using BGemm = TileGemm<E, BShapes<E>::BT, BShapes<E>::BT, BShapes<E>::WM, BShapes<E>::WN,
-                       BShapes<E>::NS>;
+                       BShapes<E>::NS, false, 1, AL, BL>;
 
 template <class E>
 __device__ __forceinline__ int ksteps(int elems) {
   return (elems * E::kSize + kStageBytes - 1) / kStageBytes;
+}
+
+// K advance per tile of an operand: bytes along the row (K-major) or K rows (MN-major).
+template <class G, bool IS_A>
+constexpr int kadv() {
+  return (IS_A ? G::kAL : G::kBL) == KK ? kStageBytes : G::KS;
 }
 
 // Four consecutive elements as floats (8-byte aligned for bf16, 16-byte for fp32).
@@ -68,6 +76,34 @@ __device__ __forceinline__ void load4f(const float* p, float* o) {
   o[3] = v[3];
 }
 
+// One tile of C = A Bᵀ over nk K-tiles from the offsets ka0, kb0 (bytes or rows, by layout),
+// stored fp32 row-major at out (pitch ldo), rows < rows and columns < cols only.
+template <class G>
+__device__ __forceinline__ void gemm_to_f32(u32x4* lds, const Src& a, int ka0, const Src& b, int kb0,
+                                            int nk, float* out, int64_t ldo, int rows, int cols) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave / G::kWN, wn = wave % G::kWN;
+  G g;
+  g.zero();
+  g.run(lds, nk,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          sa = a;
+          sb = b;
+          ka = ka0 + t * kadv<G, true>();
+          kb = kb0 + t * kadv<G, false>();
+        },
+        NoPre(), wave, wm, wn, lane);
+  g.template stage_cols<float>(
+      lds, wave, wm, wn, lane,
+      [&](int, int, int, int, const f32x4& v, float* o) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = v[k];
+      },
+      [&](int r, int cl, const u32x4& chunk) {
+        if (r < rows && cl < cols) *reinterpret_cast<u32x4*>(out + r * ldo + cl) = chunk;
+      });
+}
+
 // ------------------------------------------------------------------------------ mixb
 template <class E>
 struct MixBArgs {
@@ -79,10 +115,8 @@ struct MixBArgs {
   const T* Hu;   // [M, e]: X W_u before SiLU (the recomputing projection's)
   const T* Wo;   // [e, d], the input layout
   const T* dO;   // [M, d]
-  T* Yt;         // [nbg, e, c]
-  T* dVht;       // [nbg, e, c]
+  T* Yr;         // [M, e]
   T* dVhr;       // [M, e]
-  T* dHut;       // [nbg, e, c]
   T* dHur;       // [M, e]
   int d, nbg, G, c, e, s, causal, lin;
 };
@@ -105,14 +139,13 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
   balanced_wave<WM, WN>(wave, wm, wn);
   const int64_t tok0 = int64_t(bg) * p.c;
   const int64_t slot = p.causal ? bg : bg / p.G;
-  const int nkd = ksteps<E>(p.d);
 
   G gd;  // dYᵀ
   gd.zero();
   {
     const Src a = make_src(p.Wo, m0, p.d, E::kSize, p.e - m0, BT, p.d);
     const Src b = make_src(p.dO, tok0 + n0, p.d, E::kSize, p.c - n0, BT, p.d);
-    gd.run(lds, nkd,
+    gd.run(lds, ksteps<E>(p.d),
            [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
              sa = a;
              sb = b;
@@ -157,146 +190,53 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
       hu[0] = hu[1] = hu[2] = hu[3] = 0.0f;
     }
   };
-  // what: 0 Y = U ⊙ V̂, 1 dV̂ = dY ⊙ U, 2 dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
-  auto value = [&](int what, float hu, float dy, float vh) -> float {
-    if (what == 0) return silu(hu) * vh;
-    if (what == 1) return dy * silu(hu);
-    return dy * vh * silu_grad(hu);
-  };
-  // token-contiguous (chunk-transposed) copies: Y, dV̂, dH_u
-  T* const tdst[3] = {p.Yt, p.dVht, p.dHut};
+  // what: 0 Y = U ⊙ V̂, 1 dV̂ = dY ⊙ U, 2 dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u); all token-major
+  T* const dst[3] = {p.Yr, p.dVhr, p.dHur};
 #pragma unroll
   for (int w = 0; w < 3; ++w) {
-    g.template stage_cols<T>(
-        lds, wave, wm, wn, lane,
-        [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
-          float hu[4];
-          load_hu(r, cl, hu);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w, hu[k], gd.acc[fi][fj][k], v[k]));
-        },
-        [&](int r, int cl, const u32x4& chunk) {
-          const int j = m0 + r, i = n0 + cl;
-          if (j < p.e && i < p.c)
-            *reinterpret_cast<u32x4*>(tdst[w] + (int64_t(bg) * p.e + j) * p.c + i) = chunk;
-        });
-  }
-  // token-major copies: dV̂, dH_u
-  T* const rdst[2] = {p.dVhr, p.dHur};
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
     g.template stage_rows<T>(
         lds, wave, wm, wn, lane,
         [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
           float hu[4];
           load_hu(r, cl, hu);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w + 1, hu[k], gd.acc[fi][fj][k], v[k]));
+          for (int k = 0; k < 4; ++k) {
+            const float dy = gd.acc[fi][fj][k];
+            const float x = w == 0 ? silu(hu[k]) * v[k]
+                            : w == 1 ? dy * silu(hu[k])
+                                     : dy * v[k] * silu_grad(hu[k]);
+            out[k] = from_f32<E>(x);
+          }
         },
         [&](int cl, int r, const u32x4& chunk) {
           const int j = m0 + r, i = n0 + cl;
-          if (j < p.e && i < p.c) *reinterpret_cast<u32x4*>(rdst[w] + (tok0 + i) * p.e + j) = chunk;
+          if (j < p.e && i < p.c) *reinterpret_cast<u32x4*>(dst[w] + (tok0 + i) * p.e + j) = chunk;
         });
   }
 }
-
-// ------------------------------------------------------------------------------ xpose
-// Batched transposes src[b] [R, C] -> dst[b] [C, R] in 64 x 64 tiles (as the weight packing).
-template <class E>
-struct XJob {
-  const typename E::T* src;
-  typename E::T* dst;
-  int64_t sbs, dbs;  // batch strides, elements
-  int R, C, tiles_c, tiles_per, first;
-};
-constexpr int kMaxXJobs = 8;
-template <class E>
-struct XArgs {
-  XJob<E> job[kMaxXJobs];
-  int njobs;
-};
-
-template <class E>
-__global__ __launch_bounds__(256) void xpose_kernel(XArgs<E> args) {
-  using T = typename E::T;
-  constexpr int kPer16 = 16 / E::kSize;
-  constexpr int kVecPerRow = 64 / kPer16;
-  __shared__ T tile[64][64 + 1];
-  const int bid = blockIdx.x;
-  // job selection by unrolled selects (a dynamic index would copy the arguments to scratch)
-  XJob<E> J = args.job[0];
-#pragma unroll
-  for (int i = 1; i < kMaxXJobs; ++i)
-    if (i < args.njobs && bid >= args.job[i].first) J = args.job[i];
-  int t = bid - J.first;
-  const int b = t / J.tiles_per;
-  t -= b * J.tiles_per;
-  const int r0 = (t / J.tiles_c) * 64, c0 = (t % J.tiles_c) * 64;
-  const T* src = J.src + b * J.sbs;
-  T* dst = J.dst + b * J.dbs;
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
-    const int rr = idx / kVecPerRow, cv = (idx % kVecPerRow) * kPer16;
-    if (r0 + rr < J.R && c0 + cv < J.C) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + int64_t(r0 + rr) * J.C + c0 + cv);
-      const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-      for (int k = 0; k < kPer16; ++k) tile[rr][cv + k] = e[k];
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
-    const int cc = idx / kVecPerRow, rv = (idx % kVecPerRow) * kPer16;
-    if (c0 + cc < J.C && r0 + rv < J.R) {
-      u32x4 v;
-      T* e = reinterpret_cast<T*>(&v);
-#pragma unroll
-      for (int k = 0; k < kPer16; ++k) e[k] = tile[rv + k][cc];
-      *reinterpret_cast<u32x4*>(dst + int64_t(c0 + cc) * J.R + r0 + rv) = v;
-    }
-  }
-}
-
-template <class E>
-struct XList {
-  XArgs<E> a{};
-  int tiles = 0;
-  void add(const typename E::T* src, typename E::T* dst, int batch, int R, int C) {
-    const int tr = int(cdiv(R, 64)), tc = int(cdiv(C, 64));
-    XJob<E>& j = a.job[a.njobs++];
-    j = {src, dst, int64_t(R) * C, int64_t(R) * C, R, C, tc, tr * tc, tiles};
-    tiles += batch * tr * tc;
-  }
-  void launch(hipStream_t stream) {
-    if (tiles == 0) return;
-    for (int i = a.njobs; i < kMaxXJobs; ++i) a.job[i] = a.job[0];
-    hipLaunchKernelGGL(xpose_kernel<E>, dim3(unsigned(tiles)), dim3(256), 0, stream, a);
-  }
-};
 
 // ------------------------------------------------------------------------------ dscores
 template <class E>
 struct DScoresArgs {
   using T = typename E::T;
   const T* dVhr;  // [M, e]
-  const T* Vr;    // [M, e]
+  const T* Vt;    // [nbg, e, c]
   const T* Qq;    // [M, s]
   const T* Kq;    // [M, s]
-  const T* Sr;    // [slots, s, e] (already / n)
-  T* Pt;          // [nbg, c, c]: Pᵀ[j][i]
+  const T* St;    // [slots, e, s] (already / n)
   T* dAr;         // [nbg, c, c]: dA[i][j]
-  T* dAt;         // [nbg, c, c]: dA[j][i]
   float* dQl;     // [M, s]
   int nbg, G, c, s, e, causal;
   float inv_c;
 };
 
-// Tile (i-tile, j-tile) of one chunk: dW = dV̂ Vᵀ (over e) and A = Q_quad K_quadᵀ (over s);
-// Pᵀ = relu(A/c)² and dA = dW ⊙ 2 relu(A/c) / c, zero above the diagonal when causal. Causal
-// launches only the tiles on or below the diagonal; the consumers read no other.
+// Tile (i-tile, j-tile) of one chunk: dW = dV̂ Vᵀ (over e; V read from V_gᵀ as an MN-major
+// operand) and A = Q_quad K_quadᵀ (over s); dA = dW ⊙ 2 relu(A/c) / c, zero above the diagonal
+// when causal. Causal launches only the tiles on or below the diagonal; the consumers read no other.
 template <class E>
 __device__ __forceinline__ void dp_block(const DScoresArgs<E>& p, u32x4* lds, int bid) {
-  using G = BGemm<E>;
+  using GA = BGemm<E>;
+  using GP = BGemm<E, KK, MN>;
   using T = typename E::T;
   constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
   const int ntc = (p.c + BT - 1) / BT;
@@ -319,7 +259,7 @@ __device__ __forceinline__ void dp_block(const DScoresArgs<E>& p, u32x4* lds, in
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tok0 = int64_t(bg) * p.c;
 
-  G ga;
+  GA ga;
   ga.zero();
   {
     const Src a = make_src(p.Qq, tok0 + i0, p.s, E::kSize, p.c - i0, BT, p.s);
@@ -332,87 +272,38 @@ __device__ __forceinline__ void dp_block(const DScoresArgs<E>& p, u32x4* lds, in
            },
            NoPre(), wave, wm, wn, lane);
   }
-  G gp;
+  GP gp;
   gp.zero();
   {
     const Src a = make_src(p.dVhr, tok0 + i0, p.e, E::kSize, p.c - i0, BT, p.e);
-    const Src b = make_src(p.Vr, tok0 + j0, p.e, E::kSize, p.c - j0, BT, p.e);
+    const Src b = make_src_mn(p.Vt, int64_t(bg) * p.e, p.c, E::kSize, p.e, j0, p.c - j0);
     gp.run(lds, ksteps<E>(p.e),
            [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
              sa = a;
              sb = b;
-             ka = kb = t * kStageBytes;
+             ka = t * kStageBytes;
+             kb = t * GP::KS;
            },
            NoPre(), wave, wm, wn, lane);
-  }
-  // what: 0 Pᵀ, 1 dA
-  auto value = [&](int what, int fi, int fj, int k, int r, int cl) -> float {
-    const int i = i0 + r + k, j = j0 + cl;
-    if (p.causal && j > i) return 0.0f;
-    const float x = fmaxf(ga.acc[fi][fj][k] * p.inv_c, 0.0f);
-    return what == 0 ? x * x : gp.acc[fi][fj][k] * 2.0f * x * p.inv_c;
-  };
-  T* const base_t[2] = {p.Pt + tok0 * p.c, p.dAt + tok0 * p.c};
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    gp.template stage_rows<T>(
-        lds, wave, wm, wn, lane,
-        [&](int fi, int fj, int r, int cl, const f32x4&, T* out) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(w, fi, fj, k, r, cl));
-        },
-        [&](int cl, int r, const u32x4& chunk) {
-          const int i = i0 + r, j = j0 + cl;
-          if (i < p.c && j < p.c) *reinterpret_cast<u32x4*>(base_t[w] + int64_t(j) * p.c + i) = chunk;
-        });
   }
   gp.template stage_cols<T>(
       lds, wave, wm, wn, lane,
       [&](int fi, int fj, int r, int cl, const f32x4&, T* out) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(value(1, fi, fj, k, r, cl));
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + r + k, j = j0 + cl;
+          const float x = fmaxf(ga.acc[fi][fj][k] * p.inv_c, 0.0f);
+          out[k] = from_f32<E>((p.causal && j > i) ? 0.0f : gp.acc[fi][fj][k] * 2.0f * x * p.inv_c);
+        }
       },
       [&](int r, int cl, const u32x4& chunk) {
         const int i = i0 + r, j = j0 + cl;
-        if (i < p.c && j < p.c)
-          *reinterpret_cast<u32x4*>(p.dAr + (tok0 + i) * p.c + j) = chunk;
+        if (i < p.c && j < p.c) *reinterpret_cast<u32x4*>(p.dAr + (tok0 + i) * p.c + j) = chunk;
       });
 }
 
-// A tile of rows (tokens of a chunk) x columns (s features) of a product over e, stored fp32
-// row-major [M, s]: dQ_lin = dV̂ (S_g/n)ᵀ, and (in dheads) dK_lin = V dTᵀ.
-template <class E>
-__device__ __forceinline__ void rows_by_s_block(const typename E::T* A, const typename E::T* Bm,
-                                                int64_t a_row0, int64_t b_row0, int a_rows,
-                                                int b_rows, int K, float* out, int64_t out_row0,
-                                                int f0, int s, u32x4* lds) {
-  using G = BGemm<E>;
-  constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave / WN, wn = wave % WN;
-  G g;
-  g.zero();
-  const Src a = make_src(A, a_row0, K, E::kSize, a_rows, BT, K);
-  const Src b = make_src(Bm, b_row0, K, E::kSize, b_rows, BT, K);
-  g.run(lds, ksteps<E>(K),
-        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-          sa = a;
-          sb = b;
-          ka = kb = t * kStageBytes;
-        },
-        NoPre(), wave, wm, wn, lane);
-  g.template stage_cols<float>(
-      lds, wave, wm, wn, lane,
-      [&](int, int, int, int, const f32x4& v, float* o) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = v[k];
-      },
-      [&](int r, int cl, const u32x4& chunk) {
-        if (r < a_rows && cl < b_rows)
-          *reinterpret_cast<u32x4*>(out + (out_row0 + r) * s + f0 + cl) = chunk;
-      });
-}
-
+// dQ_lin = dV̂ (S_g/n)ᵀ per (chunk, token tile, feature tile); S/n read from its [e, s] layout as
+// an MN-major operand.
 template <class E>
 __device__ __forceinline__ void dql_block(const DScoresArgs<E>& p, u32x4* lds, int bid) {
   constexpr int BT = BShapes<E>::BT;
@@ -420,31 +311,30 @@ __device__ __forceinline__ void dql_block(const DScoresArgs<E>& p, u32x4* lds, i
   const int lid = xcd_remap(bid, p.nbg * ntc * nts);
   const int bg = lid / (ntc * nts);
   const int rem = lid % (ntc * nts);
-  const int it = rem / nts, rt = rem % nts;
+  const int i0 = (rem / nts) * BT, f0 = (rem % nts) * BT;
   const int64_t slot = p.causal ? bg : bg / p.G;
-  const int64_t tok0 = int64_t(bg) * p.c + it * BT;
-  rows_by_s_block<E>(p.dVhr, p.Sr, tok0, slot * p.s + rt * BT, p.c - it * BT, p.s - rt * BT, p.e,
-                     p.dQl, tok0, rt * BT, p.s, lds);
+  const int64_t row0 = int64_t(bg) * p.c + i0;
+  const Src a = make_src(p.dVhr, row0, p.e, E::kSize, p.c - i0, BT, p.e);
+  const Src b = make_src_mn(p.St, slot * p.e, p.s, E::kSize, p.e, f0, p.s - f0);
+  gemm_to_f32<BGemm<E, KK, MN>>(lds, a, 0, b, 0, ksteps<E>(p.e), p.dQl + row0 * p.s + f0, p.s,
+                                p.c - i0, p.s - f0);
 }
 
 // One launch, three roles by workgroup index: [0, n_dp) score-gradient tiles, [n_dp, n_dp +
 // n_dql) dQ_lin tiles, then the state-gradient tiles (the forward's summaries walking the chunks
-// last to first: Q_lin,gᵀ dV̂_g / n summed over the later chunks).
+// last to first, reading Q_lin and dV̂ token-major: Q_lin,gᵀ dV̂_g / n summed over the later chunks).
 template <class E>
 __global__ __launch_bounds__(BGemm<E>::kThreads) void dscores_states_kernel(
     DScoresArgs<E> p, int n_dp, int n_dql, StatesArgs<E> tp, int states_on) {
-  using S = Shapes<E>;
-  using GT = TileGemm<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN, S::kStatesNS>;
-  static_assert(GT::kThreads == BGemm<E>::kThreads, "all roles run with the same workgroup size");
-  __shared__ u32x4 lds[BGemm<E>::kLds > GT::kLds ? BGemm<E>::kLds : GT::kLds];
+  constexpr int BT = BShapes<E>::BT, WM = BShapes<E>::WM, WN = BShapes<E>::WN, NS = BShapes<E>::NS;
+  __shared__ u32x4 lds[BGemm<E>::kLds];
   const int bid = blockIdx.x;
   if (bid < n_dp) {
     dp_block<E>(p, lds, bid);
   } else if (bid < n_dp + n_dql) {
     dql_block<E>(p, lds, bid - n_dp);
   } else if (states_on) {
-    states_block<E, S::kStatesBM, S::kStatesBN, S::kStatesWM, S::kStatesWN, S::kStatesNS>(
-        tp, lds, bid - n_dp - n_dql);
+    states_block<E, BT, BT, WM, WN, NS, MN>(tp, lds, bid - n_dp - n_dql);
   }
 }
 
@@ -453,25 +343,24 @@ template <class E>
 struct DHeadsArgs {
   using T = typename E::T;
   const T* dAr;  // [nbg, c, c]
-  const T* dAt;  // [nbg, c, c]
-  const T* Kqt;  // [nbg, s, c]
-  const T* Qqt;  // [nbg, s, c]
-  const T* Vr;   // [M, e]
-  const T* dTr;  // [slots, s, e] (already / n)
+  const T* Kq;   // [M, s]
+  const T* Qq;   // [M, s]
+  const T* Vt;   // [nbg, e, c]
+  const T* dTt;  // [slots, e, s] (already / n)
   float* dQq;    // [M, s]
   float* dKq;    // [M, s]
   float* dKl;    // [M, s]
   int nbg, G, c, s, e, causal;
 };
 
-// Role 0: dQ_quad = dA K_quad (rows i, K over keys j up to the tile's diagonal when causal).
-// Role 1: dK_quad = dAᵀ Q_quad (rows j, K over queries i from the tile's diagonal when causal).
-// Role 2: dK_lin = V dTᵀ (rows j, K over e).
+// Per (chunk, token tile, feature tile), three roles:
+//   0: dQ_quad = dA K_quad over the keys (up to the tile's diagonal when causal); K_quad MN-major;
+//   1: dK_quad = dAᵀ Q_quad over the queries (from the tile's diagonal); dA and Q_quad MN-major;
+//   2: dK_lin = V dTᵀ over e; V from V_gᵀ and dT/n from its [e, s] layout, both MN-major.
 template <class E>
 __global__ __launch_bounds__(BGemm<E>::kThreads) void dheads_kernel(DHeadsArgs<E> p, int roles) {
-  using G = BGemm<E>;
-  constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
-  __shared__ u32x4 lds[G::kLds];
+  constexpr int BT = BShapes<E>::BT;
+  __shared__ u32x4 lds[BGemm<E>::kLds];
   const int ntc = (p.c + BT - 1) / BT, nts = (p.s + BT - 1) / BT;
   const int per_role = p.nbg * ntc * nts;
   const int role = blockIdx.x / per_role;
@@ -479,69 +368,53 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dheads_kernel(DHeadsArgs<E
   const int lid = xcd_remap(blockIdx.x - role * per_role, per_role);
   const int bg = lid / (ntc * nts);
   const int rem = lid % (ntc * nts);
-  const int rt0 = rem / nts, st = rem % nts;
-  const int r0 = rt0 * BT, f0 = st * BT;  // row tile (tokens of the chunk), feature tile
+  const int r0 = (rem / nts) * BT, f0 = (rem % nts) * BT;  // token tile of the chunk, feature tile
   const int64_t tok0 = int64_t(bg) * p.c;
-  if (role == 2) {
+  const int rows = p.c - r0, cols = p.s - f0;
+  if (role == 0) {
+    const int kend = p.causal ? min(p.c, r0 + BT) : p.c;
+    const Src a = make_src(p.dAr, tok0 + r0, p.c, E::kSize, rows, BT, p.c);
+    const Src b = make_src_mn(p.Kq, tok0, p.s, E::kSize, p.c, f0, cols);
+    gemm_to_f32<BGemm<E, KK, MN>>(lds, a, 0, b, 0, ksteps<E>(kend), p.dQq + (tok0 + r0) * p.s + f0,
+                                  p.s, rows, cols);
+  } else if (role == 1) {
+    const int kbeg = p.causal ? r0 : 0;
+    const Src a = make_src_mn(p.dAr, tok0, p.c, E::kSize, p.c, r0, rows);
+    const Src b = make_src_mn(p.Qq, tok0, p.s, E::kSize, p.c, f0, cols);
+    gemm_to_f32<BGemm<E, MN, MN>>(lds, a, kbeg, b, kbeg, ksteps<E>(p.c - kbeg),
+                                  p.dKq + (tok0 + r0) * p.s + f0, p.s, rows, cols);
+  } else {
     const int64_t slot = p.causal ? bg : bg / p.G;
-    rows_by_s_block<E>(p.Vr, p.dTr, tok0 + r0, slot * p.s + f0, p.c - r0, p.s - f0, p.e, p.dKl,
-                       tok0 + r0, f0, p.s, lds);
-    return;
+    const Src a = make_src_mn(p.Vt, int64_t(bg) * p.e, p.c, E::kSize, p.e, r0, rows);
+    const Src b = make_src_mn(p.dTt, slot * p.e, p.s, E::kSize, p.e, f0, cols);
+    gemm_to_f32<BGemm<E, MN, MN>>(lds, a, 0, b, 0, ksteps<E>(p.e), p.dKl + (tok0 + r0) * p.s + f0,
+                                  p.s, rows, cols);
   }
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave / WN, wn = wave % WN;
-  // role 0 reads keys [0, min(c, r0 + BT)), role 1 queries [r0, c) when causal
-  const int kbeg = (p.causal && role == 1) ? r0 : 0;
-  const int kend = (p.causal && role == 0) ? min(p.c, r0 + BT) : p.c;
-  const typename E::T* A = role == 0 ? p.dAr : p.dAt;
-  const typename E::T* Bm = role == 0 ? p.Kqt : p.Qqt;
-  G g;
-  g.zero();
-  const Src a = make_src(A, tok0 + r0, p.c, E::kSize, p.c - r0, BT, p.c);
-  const Src b = make_src(Bm, int64_t(bg) * p.s + f0, p.c, E::kSize, p.s - f0, BT, p.c);
-  const int kb0 = kbeg * E::kSize;
-  g.run(lds, ksteps<E>(kend - kbeg),
-        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-          sa = a;
-          sb = b;
-          ka = kb = kb0 + t * kStageBytes;
-        },
-        NoPre(), wave, wm, wn, lane);
-  float* out = role == 0 ? p.dQq : p.dKq;
-  g.template stage_cols<float>(
-      lds, wave, wm, wn, lane,
-      [&](int, int, int, int, const f32x4& v, float* o) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = v[k];
-      },
-      [&](int r, int cl, const u32x4& chunk) {
-        const int i = r0 + r, f = f0 + cl;
-        if (i < p.c && f < p.s) *reinterpret_cast<u32x4*>(out + (tok0 + i) * p.s + f) = chunk;
-      });
 }
 
 // ------------------------------------------------------------------------------ dv
 template <class E>
 struct DVArgs {
   using T = typename E::T;
-  const T* dVht;  // [nbg, e, c]
-  const T* Pt;    // [nbg, c, c]: Pᵀ[j][i]
+  const T* dVhr;  // [M, e]
+  const T* P;     // [nbg, c, c]: P[i][j]
   const T* dTt;   // [slots, e, s] (already / n)
-  const T* Klr;   // [M, s]
+  const T* Klt;   // [nbg, s, c]
   const T* Hr;    // [M, e+s] pre-activations
   T* dHvr;        // [M, e]
-  T* dHvt;        // [nbg, e, c]
   int nbg, G, c, s, e, causal, lin;
 };
 
-// Tile (value columns, keys j of a chunk): dVᵀ = dV̂ᵀ Pᵀᵀ over the queries i >= j (causal: from the
-// tile's diagonal on) plus dTᵀ K_linᵀ over s; times SiLU'(H_v).
+// Tile (value columns, keys j of a chunk): dVᵀ = dV̂ᵀ P over the queries i >= j (causal: from the
+// tile's diagonal on; dV̂ and P MN-major), then + dTᵀ K_linᵀ over s (K_lin MN-major from its
+// chunk-transposed copy), times SiLU'(H_v).
 template <class E>
 __global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
-  using G = BGemm<E>;
+  using G0 = BGemm<E, MN, MN>;
+  using G1 = BGemm<E, KK, MN>;
   using T = typename E::T;
   constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
-  __shared__ u32x4 lds[G::kLds];
+  __shared__ u32x4 lds[G0::kLds];
   const int nte = (p.e + BT - 1) / BT, ntc = (p.c + BT - 1) / BT;
   const int lid = xcd_remap(blockIdx.x, p.nbg * nte * ntc);
   const int bg = lid / (nte * ntc);
@@ -553,37 +426,45 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
   const int64_t tok0 = int64_t(bg) * p.c;
   const int64_t slot = p.causal ? bg : bg / p.G;
   const int kbeg = p.causal ? n0 : 0;
-  const int nk0 = ksteps<E>(p.c - kbeg);
-  const int nk1 = p.lin ? ksteps<E>(p.s) : 0;
-  const Src a0 = make_src(p.dVht, int64_t(bg) * p.e + m0, p.c, E::kSize, p.e - m0, BT, p.c);
-  const Src b0 = make_src(p.Pt, tok0 + n0, p.c, E::kSize, p.c - n0, BT, p.c);
-  const Src a1 = make_src(p.dTt, slot * p.e + m0, p.s, E::kSize, p.e - m0, BT, p.s);
-  const Src b1 = make_src(p.Klr, tok0 + n0, p.s, E::kSize, p.c - n0, BT, p.s);
-  const int kb0 = kbeg * E::kSize;
-  G g;
-  g.zero();
-  g.run(lds, nk0 + nk1,
-        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
-          if (t < nk0) {
-            sa = a0;
-            sb = b0;
-            ka = kb = kb0 + t * kStageBytes;
-          } else {
-            sa = a1;
-            sb = b1;
-            ka = kb = (t - nk0) * kStageBytes;
-          }
-        },
-        NoPre(), wave, wm, wn, lane);
+  G0 g0;
+  g0.zero();
+  {
+    const Src a = make_src_mn(p.dVhr, tok0, p.e, E::kSize, p.c, m0, p.e - m0);
+    const Src b = make_src_mn(p.P, tok0, p.c, E::kSize, p.c, n0, p.c - n0);
+    g0.run(lds, ksteps<E>(p.c - kbeg),
+           [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+             sa = a;
+             sb = b;
+             ka = kb = kbeg + t * G0::KS;
+           },
+           NoPre(), wave, wm, wn, lane);
+  }
+  G1 g;
+#pragma unroll
+  for (int i = 0; i < G1::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G1::TN; ++j) g.acc[i][j] = g0.acc[i][j];
+  if (p.lin) {
+    const Src a = make_src(p.dTt, slot * p.e + m0, p.s, E::kSize, p.e - m0, BT, p.s);
+    const Src b = make_src_mn(p.Klt, int64_t(bg) * p.s, p.c, E::kSize, p.s, n0, p.c - n0);
+    g.run(lds, ksteps<E>(p.s),
+          [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+            sa = a;
+            sb = b;
+            ka = t * kStageBytes;
+            kb = t * G1::KS;
+          },
+          NoPre(), wave, wm, wn, lane);
+  }
   // dH_v = dV ⊙ SiLU'(H_v), in place
   const int ncols = p.e + p.s;
   const int lr = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < G::TM; ++i)
+  for (int i = 0; i < G1::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int col = m0 + wm * G::WTM + i * 16 + q * 4;  // first of four value columns
-      const int key = n0 + wn * G::WTN + j * 16 + lr;
+    for (int j = 0; j < G1::TN; ++j) {
+      const int col = m0 + wm * G1::WTM + i * 16 + q * 4;  // first of four value columns
+      const int key = n0 + wn * G1::WTN + j * 16 + lr;
       if (col < p.e && key < p.c) {
         float h[4];
         load4f(p.Hr + (tok0 + key) * ncols + col, h);
@@ -601,21 +482,10 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
         const int j = m0 + r, key = n0 + cl;
         if (j < p.e && key < p.c) *reinterpret_cast<u32x4*>(p.dHvr + (tok0 + key) * p.e + j) = chunk;
       });
-  g.template stage_cols<T>(
-      lds, wave, wm, wn, lane,
-      [&](int, int, int, int, const f32x4& v, T* out) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
-      },
-      [&](int r, int cl, const u32x4& chunk) {
-        const int j = m0 + r, key = n0 + cl;
-        if (j < p.e && key < p.c)
-          *reinterpret_cast<u32x4*>(p.dHvt + (int64_t(bg) * p.e + j) * p.c + key) = chunk;
-      });
 }
 
 // ------------------------------------------------------------------------------ dz
-constexpr int kZRows = 32;  // token rows per dz workgroup (a multiple of 8)
+constexpr int kZRows = 32;  // token rows per dz workgroup
 
 template <class E>
 struct DZArgs {
@@ -627,15 +497,13 @@ struct DZArgs {
   const T* Hr;          // [M, e+s]; Z's pre-activations in columns e..
   const float* gamma;   // [4, s]
   T* dHzr;              // [M, s]
-  T* dHzt;              // [nbg, s, c]
   float* gbpart;        // [nzb, 8, s]: rows 0..3 dγ, 4..7 dβ partial sums of workgroup row block
   int M, n, c, e, s, lin, rope;
   double log2_base;
 };
 
 // One thread per feature pair (2f, 2f+1) and group of rows; the rotary transpose turns a pair
-// back by −m·θ. Rows go in runs of 8 tokens of one chunk so that dH_z's chunk-transposed copy
-// leaves as 8-element runs.
+// back by −m·θ.
 template <class E>
 __global__ __launch_bounds__(256) void dz_kernel(DZArgs<E> p) {
   using T = typename E::T;
@@ -662,62 +530,44 @@ __global__ __launch_bounds__(256) void dz_kernel(DZArgs<E> p) {
     const float* src[4] = {p.dQq, p.dKq, p.dQl, p.dKl};
     const int nheads = p.lin ? 4 : 2;
     const int row_end = min(p.M, int(blockIdx.x + 1) * kZRows);
-    for (int rb = int(blockIdx.x) * kZRows + 8 * rg; rb < row_end; rb += 8 * RG) {
-      alignas(16) T z0[8];
-      alignas(16) T z1[8];
+    for (int row = int(blockIdx.x) * kZRows + rg; row < row_end; row += RG) {
+      float g[4][2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int row = rb + k;
-        float g[4][2];
+      for (int h = 0; h < 4; ++h) {
+        if (h < nheads) {
+          const f32x2 v = *reinterpret_cast<const f32x2*>(src[h] + int64_t(row) * p.s + f0);
+          g[h][0] = v[0];
+          g[h][1] = v[1];
+        } else {
+          g[h][0] = g[h][1] = 0.0f;
+        }
+      }
+      if (p.rope) {
+        float cs, sn;
+        rope_angle(row % p.n, rope_theta(f0, p.s, p.log2_base), &cs, &sn);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          if (h < nheads) {
-            const f32x2 v = *reinterpret_cast<const f32x2*>(src[h] + int64_t(row) * p.s + f0);
-            g[h][0] = v[0];
-            g[h][1] = v[1];
-          } else {
-            g[h][0] = g[h][1] = 0.0f;
-          }
+          const float x0 = g[h][0], x1 = g[h][1];
+          g[h][0] = rope_apply(x0, x1, f0, cs, -sn);
+          g[h][1] = rope_apply(x1, x0, f0 + 1, cs, -sn);
         }
-        if (p.rope) {
-          float cs, sn;
-          rope_angle(row % p.n, rope_theta(f0, p.s, p.log2_base), &cs, &sn);
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float x0 = g[h][0], x1 = g[h][1];
-            g[h][0] = rope_apply(x0, x1, f0, cs, -sn);
-            g[h][1] = rope_apply(x1, x0, f0 + 1, cs, -sn);
-          }
-        }
-        const T* hz = p.Hr + int64_t(row) * ncols + p.e + f0;
-        const float hz0 = to_f32(hz[0]), hz1 = to_f32(hz[1]);
-        const float zz[2] = {silu(hz0), silu(hz1)};
-        float dz0 = 0.0f, dz1 = 0.0f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          dz0 = fmaf(gm[h][0], g[h][0], dz0);
-          dz1 = fmaf(gm[h][1], g[h][1], dz1);
-          acc[h * 2] = fmaf(zz[0], g[h][0], acc[h * 2]);
-          acc[h * 2 + 1] = fmaf(zz[1], g[h][1], acc[h * 2 + 1]);
-          acc[8 + h * 2] += g[h][0];
-          acc[8 + h * 2 + 1] += g[h][1];
-        }
-        const float d0 = dz0 * silu_grad(hz0), d1 = dz1 * silu_grad(hz1);
-        T* o = p.dHzr + int64_t(row) * p.s + f0;
-        o[0] = from_f32<E>(d0);
-        o[1] = from_f32<E>(d1);
-        z0[k] = from_f32<E>(d0);
-        z1[k] = from_f32<E>(d1);
       }
-      const int64_t bg = rb / p.c, t = rb % p.c;  // 8 rows inside one chunk (c % 8 == 0)
-      T* o0 = p.dHzt + (bg * p.s + f0) * p.c + t;  // 16-byte aligned: t and c are multiples of 8
-      T* o1 = o0 + p.c;
-      constexpr int kVec = 16 / int(sizeof(T));
+      const T* hz = p.Hr + int64_t(row) * ncols + p.e + f0;
+      const float hz0 = to_f32(hz[0]), hz1 = to_f32(hz[1]);
+      const float zz[2] = {silu(hz0), silu(hz1)};
+      float dz0 = 0.0f, dz1 = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 8 / kVec; ++v) {
-        *reinterpret_cast<u32x4*>(o0 + v * kVec) = *reinterpret_cast<const u32x4*>(z0 + v * kVec);
-        *reinterpret_cast<u32x4*>(o1 + v * kVec) = *reinterpret_cast<const u32x4*>(z1 + v * kVec);
+      for (int h = 0; h < 4; ++h) {
+        dz0 = fmaf(gm[h][0], g[h][0], dz0);
+        dz1 = fmaf(gm[h][1], g[h][1], dz1);
+        acc[h * 2] = fmaf(zz[0], g[h][0], acc[h * 2]);
+        acc[h * 2 + 1] = fmaf(zz[1], g[h][1], acc[h * 2 + 1]);
+        acc[8 + h * 2] += g[h][0];
+        acc[8 + h * 2 + 1] += g[h][1];
       }
+      T* o = p.dHzr + int64_t(row) * p.s + f0;
+      o[0] = from_f32<E>(dz0 * silu_grad(hz0));
+      o[1] = from_f32<E>(dz1 * silu_grad(hz1));
     }
   }
 #pragma unroll
@@ -804,25 +654,25 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dx_kernel(DXArgs<E> p) {
 }
 
 // ------------------------------------------------------------------------------ wgrad
-// out[q] [Fa, Fb] = Σ over the tokens of chunks [q cps, (q+1) cps) of A[chunk] [Fa, c] ·
-// B[chunk] [Fb, c]ᵀ: operands chunk-transposed (token-contiguous), fp32 partial per split q.
+// out[q] [Fa, Fb] = Σ over the tokens [q tps, (q+1) tps) of A[token] [Fa] ⊗ B[token] [Fb]: both
+// operands token-major, read as MN-major tiles; fp32 partial per split q.
 template <class E>
 struct WJob {
-  const typename E::T* A;
-  const typename E::T* B;
+  const typename E::T* A;  // [M, Fa]
+  const typename E::T* B;  // [M, Fb]
   float* out;
   int Fa, Fb, tiles_m, tiles_n, first;
 };
 template <class E>
 struct WArgs {
   WJob<E> job[4];
-  int njobs, nbg, c, cps, splits;
+  int njobs, M, tps, splits;
 };
 
 template <class E>
 __global__ __launch_bounds__(BGemm<E>::kThreads) void wgrad_kernel(WArgs<E> p, int total) {
-  using G = BGemm<E>;
-  constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
+  using G = BGemm<E, MN, MN>;
+  constexpr int BT = BShapes<E>::BT;
   __shared__ u32x4 lds[G::kLds];
   const int lid = xcd_remap(blockIdx.x, total);
   WJob<E> J = p.job[0];
@@ -835,33 +685,12 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void wgrad_kernel(WArgs<E> p, i
   t -= q * per_split;
   const int nt = t / J.tiles_m, mt = t % J.tiles_m;
   const int m0 = mt * BT, n0 = nt * BT;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave / WN, wn = wave % WN;
-  const int cbeg = q * p.cps;
-  const int nch = min(p.nbg, cbeg + p.cps) - cbeg;
-  const int nkc = ksteps<E>(p.c);
-  G g;
-  g.zero();
-  g.run(lds, nch * nkc,
-        [&](int tt, Src& sa, int& ka, Src& sb, int& kb) {
-          const int64_t chunk = cbeg + tt / nkc;
-          sa = make_src(J.A, chunk * J.Fa + m0, p.c, E::kSize, J.Fa - m0, BT, p.c);
-          sb = make_src(J.B, chunk * J.Fb + n0, p.c, E::kSize, J.Fb - n0, BT, p.c);
-          ka = kb = (tt % nkc) * kStageBytes;
-        },
-        NoPre(), wave, wm, wn, lane);
-  float* out = J.out + int64_t(q) * J.Fa * J.Fb;
-  g.template stage_cols<float>(
-      lds, wave, wm, wn, lane,
-      [&](int, int, int, int, const f32x4& v, float* o) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = v[k];
-      },
-      [&](int r, int cl, const u32x4& chunk) {
-        const int row = m0 + r, col = n0 + cl;
-        if (row < J.Fa && col < J.Fb)
-          *reinterpret_cast<u32x4*>(out + int64_t(row) * J.Fb + col) = chunk;
-      });
+  const int tbeg = q * p.tps;
+  const int ntok = min(p.M, tbeg + p.tps) - tbeg;
+  const Src a = make_src_mn(J.A, tbeg, J.Fa, E::kSize, ntok, m0, J.Fa - m0);
+  const Src b = make_src_mn(J.B, tbeg, J.Fb, E::kSize, ntok, n0, J.Fb - n0);
+  gemm_to_f32<G>(lds, a, 0, b, 0, ksteps<E>(ntok), J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0,
+                 J.Fb, J.Fa - m0, J.Fb - n0);
 }
 
 // ------------------------------------------------------------------------------ reduce
@@ -936,15 +765,14 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t words) {
 
 // ------------------------------------------------------------------------------ host plan
 enum BRegion {
-  BR_HU, BR_HR, BR_VR, BR_XT, BR_DOT, BR_QQT, BR_KQT, BR_QLT, BR_KLR, BR_SR, BR_YT, BR_DVHT, BR_DVHR,
-  BR_DHUT, BR_DHUR, BR_PT, BR_DAR, BR_DAT, BR_DTT, BR_DCARRY, BR_DTR, BR_DQQ, BR_DKQ, BR_DQL,
-  BR_DKL, BR_DHVR, BR_DHVT, BR_DHZR, BR_DHZT, BR_WPART, BR_GBPART, BR_COUNT
+  BR_HU, BR_HR, BR_YR, BR_DVHR, BR_DHUR, BR_DAR, BR_DTT, BR_DCARRY, BR_DQQ, BR_DKQ, BR_DQL, BR_DKL,
+  BR_DHVR, BR_DHZR, BR_WPART, BR_GBPART, BR_COUNT
 };
 
 struct BPlan {
   Plan f;                 // the forward's regions come first in the workspace
   int64_t slots;          // state slots: chunks (causal) or sequences
-  int64_t splits, cps;    // weight gradients: chunk-range splits, chunks per split
+  int64_t splits, tps;    // weight gradients: token-range splits, tokens per split
   int64_t wcount[4];      // elements of dW_u, dW_v, dW_z, dW_o
   int64_t nzb;            // dz row blocks
   int64_t bt;             // backward tile
@@ -973,31 +801,25 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
   bp->slots = causal ? nbg : B;
   const int64_t tiles_per_split = 2 * cdiv(d, bt) * cdiv(e, bt) + cdiv(d, bt) * cdiv(s, bt) +
                                   cdiv(e, bt) * cdiv(d, bt);
-  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(nbg, cdiv(kWgradTargetBlocks, tiles_per_split)));
-  bp->cps = cdiv(nbg, splits);
-  bp->splits = cdiv(nbg, bp->cps);
+  // token ranges of whole stage lengths (a multiple of the chunk, so also of 8)
+  const int64_t ks = kStageBytes / f.esz;
+  const int64_t splits0 = std::max<int64_t>(1, std::min<int64_t>(cdiv(M, ks), cdiv(kWgradTargetBlocks, tiles_per_split)));
+  bp->tps = cdiv(cdiv(M, splits0), ks) * ks;
+  bp->splits = cdiv(M, bp->tps);
   bp->nzb = cdiv(M, kZRows);
   const int64_t esz = f.esz;
   int64_t cnt[BR_COUNT], sz[BR_COUNT];
   for (int i = 0; i < BR_COUNT; ++i) sz[i] = esz;
   int64_t t0;
+  if (!mul_ok(M, e, &cnt[BR_HU])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(M, e + s, &cnt[BR_HR])) return FLASHGAU_ERR_BAD_SHAPE;
-  if (!mul_ok(M, e, &cnt[BR_VR])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_HU] = cnt[BR_VR];
-  if (!mul_ok(M, d, &cnt[BR_XT])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_DOT] = cnt[BR_XT];
-  if (!mul_ok(M, s, &cnt[BR_QQT])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_KQT] = cnt[BR_QLT] = cnt[BR_KLR] = cnt[BR_QQT];
-  if (!mul_ok(bp->slots, s, &t0) || !mul_ok(t0, e, &cnt[BR_SR])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_YT] = cnt[BR_DVHT] = cnt[BR_DVHR] = cnt[BR_DHUT] = cnt[BR_DHUR] = cnt[BR_VR];
-  if (!mul_ok(M, chunk, &cnt[BR_PT])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_DAR] = cnt[BR_DAT] = cnt[BR_PT];
-  cnt[BR_DTT] = cnt[BR_DTR] = cnt[BR_SR];
+  cnt[BR_YR] = cnt[BR_DVHR] = cnt[BR_DHUR] = cnt[BR_DHVR] = cnt[BR_HU];
+  if (!mul_ok(M, chunk, &cnt[BR_DAR])) return FLASHGAU_ERR_BAD_SHAPE;
+  if (!mul_ok(bp->slots, s, &t0) || !mul_ok(t0, e, &cnt[BR_DTT])) return FLASHGAU_ERR_BAD_SHAPE;
   if (!mul_ok(B * f.ng, e, &t0) || !mul_ok(t0, s, &cnt[BR_DCARRY])) return FLASHGAU_ERR_BAD_SHAPE;
-  cnt[BR_DQQ] = cnt[BR_DKQ] = cnt[BR_DQL] = cnt[BR_DKL] = cnt[BR_QQT];
+  if (!mul_ok(M, s, &cnt[BR_DQQ])) return FLASHGAU_ERR_BAD_SHAPE;
+  cnt[BR_DKQ] = cnt[BR_DQL] = cnt[BR_DKL] = cnt[BR_DHZR] = cnt[BR_DQQ];
   sz[BR_DQQ] = sz[BR_DKQ] = sz[BR_DQL] = sz[BR_DKL] = 4;
-  cnt[BR_DHVR] = cnt[BR_DHVT] = cnt[BR_VR];
-  cnt[BR_DHZR] = cnt[BR_DHZT] = cnt[BR_QQT];
   const int64_t wtot = bp->wcount[0] + bp->wcount[1] + bp->wcount[2] + bp->wcount[3];
   if (!mul_ok(bp->splits, wtot, &cnt[BR_WPART])) return FLASHGAU_ERR_BAD_SHAPE;
   sz[BR_WPART] = 4;
@@ -1012,22 +834,22 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
     if (__builtin_add_overflow(off, padded, &off)) return FLASHGAU_ERR_BAD_SHAPE;
   }
   bp->total = off;
-  // grid sizes
+  // grid sizes, and the byte ranges the MN-major operands address (32-bit buffer descriptors)
   const int64_t ntc = cdiv(chunk, bt), nts = cdiv(s, bt), nte = cdiv(e, bt);
-  const int64_t xtiles = 2 * nbg * cdiv(chunk, 64) * cdiv(d, 64) + 4 * nbg * cdiv(chunk, 64) * cdiv(s, 64) +
-                         bp->slots * cdiv(e, 64) * cdiv(s, 64);
   const int64_t grids[] = {
-      nbg * nte * ntc,                                                           // mixb, dv
-      xtiles,                                                                    // xpose
-      nbg * ntc * ntc + nbg * ntc * nts + B * f.ng * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN),
-      3 * nbg * ntc * nts,                                                       // dheads
-      cdiv(d, bt) * cdiv(M, bt),                                                 // dx
-      bp->splits * tiles_per_split,                                              // wgrad
-      cdiv(wtot / 4, 256),                                                       // reduce
-      bp->nzb * cdiv(s / 2, 256),                                                // dz
+      nbg * nte * ntc,                                                        // mixb, dv
+      nbg * ntc * ntc + nbg * ntc * nts + B * f.ng * cdiv(s, bt) * cdiv(e, bt),  // dscores_states
+      3 * nbg * ntc * nts,                                                    // dheads
+      cdiv(d, bt) * cdiv(M, bt),                                              // dx
+      bp->splits * tiles_per_split,                                           // wgrad
+      cdiv(wtot / 4, 256),                                                    // reduce
+      bp->nzb * cdiv(s / 2, 256),                                             // dz
   };
   for (int64_t g : grids)
     if (g > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
+  const int64_t widest = std::max<int64_t>({d, e + s, chunk});
+  if (bp->tps * widest * esz > int64_t(0xFFFFFFFF) || e * chunk * esz > int64_t(0xFFFFFFFF))
+    return FLASHGAU_ERR_BAD_SHAPE;
   return FLASHGAU_OK;
 }
 
@@ -1063,7 +885,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   {
     ProjArgs<E> a{Xp, WcatT, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
-                  int(pl.n), rope, log2_base, R(BR_HR), R(BR_VR), R(BR_HU)};
+                  int(pl.n), rope, log2_base, R(BR_HR), R(BR_HU)};
     const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
     hipLaunchKernelGGL(
         (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, true>),
@@ -1088,34 +910,21 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
 
   // ---- gate, output projection and V̂
   {
-    MixBArgs<E> a{Vt, St, P, Ql, R(BR_HU), reinterpret_cast<const T*>(W_o), dOp, R(BR_YT),
-                  R(BR_DVHT), R(BR_DVHR), R(BR_DHUT), R(BR_DHUR), d, nbg, G, c, e, s, causal,
-                  int(lin)};
+    MixBArgs<E> a{Vt, St, P, Ql, R(BR_HU), reinterpret_cast<const T*>(W_o), dOp, R(BR_YR),
+                  R(BR_DVHR), R(BR_DHUR), d, nbg, G, c, e, s, causal, int(lin)};
     const int64_t nb = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
     hipLaunchKernelGGL(mixb_kernel<E>, dim3(unsigned(nb)), dim3(kThreads), 0, stream, a);
   }
-  // ---- token-contiguous copies
+  // ---- score gradients, dQ_lin, state gradients (token-major Q_lin and dV̂, chunks last to first)
   {
-    XList<E> xl;
-    xl.add(Xp, R(BR_XT), nbg, c, d);
-    xl.add(dOp, R(BR_DOT), nbg, c, d);
-    xl.add(Qq, R(BR_QQT), nbg, c, s);
-    xl.add(Kq, R(BR_KQT), nbg, c, s);
-    xl.add(Ql, R(BR_QLT), nbg, c, s);
-    xl.add(Klt, R(BR_KLR), nbg, s, c);
-    if (lin) xl.add(St, R(BR_SR), int(bp.slots), e, s);
-    xl.launch(stream);
-  }
-  // ---- score gradients, dQ_lin, state gradients
-  {
-    DScoresArgs<E> a{R(BR_DVHR), R(BR_VR), Qq, Kq, R(BR_SR), R(BR_PT), R(BR_DAR), R(BR_DAT),
-                     Rf(BR_DQL), nbg, G, c, s, e, causal, 1.0f / float(c)};
+    DScoresArgs<E> a{R(BR_DVHR), Vt, Qq, Kq, St, R(BR_DAR), Rf(BR_DQL), nbg, G, c, s, e, causal,
+                     1.0f / float(c)};
     const int64_t ntc = cdiv(c, bt), nts = cdiv(s, bt);
     const int64_t n_dp = pl.nbg * (causal ? ntc * (ntc + 1) / 2 : ntc * ntc);
     const int64_t n_dql = lin ? pl.nbg * ntc * nts : 0;
-    StatesArgs<E> ta{R(BR_QLT), R(BR_DVHT), R(BR_DTT), R(BR_DCARRY), B, G, s, e, c, causal,
-                     int(pl.ng), int(pl.gs), inv_n, 1};
-    const int64_t ntb = lin ? pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN) : 0;
+    StatesArgs<E> ta{Ql, R(BR_DVHR), R(BR_DTT), R(BR_DCARRY), B, G, s, e, c, causal, int(pl.ng),
+                     int(pl.gs), inv_n, 1};
+    const int64_t ntb = lin ? pl.B * pl.ng * cdiv(s, bt) * cdiv(e, bt) : 0;
     hipLaunchKernelGGL(dscores_states_kernel<E>, dim3(unsigned(n_dp + n_dql + ntb)), dim3(kThreads),
                        0, stream, a, int(n_dp), int(n_dql), ta, int(lin));
   }
@@ -1124,15 +933,10 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     hipLaunchKernelGGL(carry_kernel<E>, dim3(unsigned(cdiv(pl.B * e * s / 8, 256))), dim3(256), 0,
                        stream, a);
   }
-  if (lin) {
-    XList<E> xl;
-    xl.add(R(BR_DTT), R(BR_DTR), int(bp.slots), e, s);
-    xl.launch(stream);
-  }
   // ---- head gradients
   {
-    DHeadsArgs<E> a{R(BR_DAR), R(BR_DAT), R(BR_KQT), R(BR_QQT), R(BR_VR), R(BR_DTR), Rf(BR_DQQ),
-                    Rf(BR_DKQ), Rf(BR_DKL), nbg, G, c, s, e, causal};
+    DHeadsArgs<E> a{R(BR_DAR), Kq, Qq, Vt, R(BR_DTT), Rf(BR_DQQ), Rf(BR_DKQ), Rf(BR_DKL), nbg, G, c,
+                    s, e, causal};
     const int roles = lin ? 3 : 2;
     const int64_t per_role = pl.nbg * cdiv(c, bt) * cdiv(s, bt);
     hipLaunchKernelGGL(dheads_kernel<E>, dim3(unsigned(roles * per_role)), dim3(kThreads), 0, stream,
@@ -1140,15 +944,15 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   }
   // ---- value gradients
   {
-    DVArgs<E> a{R(BR_DVHT), R(BR_PT), R(BR_DTT), R(BR_KLR), R(BR_HR), R(BR_DHVR), R(BR_DHVT), nbg, G,
-                c, s, e, causal, int(lin)};
+    DVArgs<E> a{R(BR_DVHR), P, R(BR_DTT), Klt, R(BR_HR), R(BR_DHVR), nbg, G, c, s, e, causal,
+                int(lin)};
     const int64_t nb = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
     hipLaunchKernelGGL(dv_kernel<E>, dim3(unsigned(nb)), dim3(kThreads), 0, stream, a);
   }
   // ---- rotary transpose, dZ, dH_z, dγ/dβ partials
   {
     DZArgs<E> a{Rf(BR_DQQ), Rf(BR_DKQ), Rf(BR_DQL), Rf(BR_DKL), R(BR_HR), gamma, R(BR_DHZR),
-                R(BR_DHZT), Rf(BR_GBPART), M, int(pl.n), c, e, s, int(lin), rope, log2_base};
+                Rf(BR_GBPART), M, int(pl.n), c, e, s, int(lin), rope, log2_base};
     hipLaunchKernelGGL(dz_kernel<E>, dim3(unsigned(bp.nzb), unsigned(cdiv(s / 2, 256))), dim3(256), 0,
                        stream, a);
   }
@@ -1170,8 +974,8 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
       o += bp.splits * bp.wcount[i];
     }
     WArgs<E> a{};
-    const T* As[4] = {R(BR_XT), R(BR_XT), R(BR_XT), R(BR_YT)};
-    const T* Bs[4] = {R(BR_DHUT), R(BR_DHVT), R(BR_DHZT), R(BR_DOT)};
+    const T* As[4] = {Xp, Xp, Xp, R(BR_YR)};
+    const T* Bs[4] = {R(BR_DHUR), R(BR_DHVR), R(BR_DHZR), dOp};
     const int Fa[4] = {d, d, d, e};
     const int Fb[4] = {e, e, s, d};
     int total = 0;
@@ -1181,9 +985,8 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
       total += int(bp.splits) * tm * tn;
     }
     a.njobs = 4;
-    a.nbg = nbg;
-    a.c = c;
-    a.cps = int(bp.cps);
+    a.M = M;
+    a.tps = int(bp.tps);
     a.splits = int(bp.splits);
     hipLaunchKernelGGL(wgrad_kernel<E>, dim3(unsigned(total)), dim3(kThreads), 0, stream, a, total);
   }

@@ -23,7 +23,18 @@ namespace {
 // tile; with NS = 2 (tiles too large for three stages) the loads of tile t+2 are issued after
 // tile t has been consumed, two barriers per tile. PRIO raises the wave priority while it issues
 // matrix instructions; iglp_opt(1) asks the scheduler to interleave the LDS reads with them.
-template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false, int IGLP = 1>
+//
+// Operand layouts (AL for A, BL for B): kLayoutK (the default) stores each of the tile's rows with
+// its K elements contiguous; kLayoutMN stores the operand as K rows of M-contiguous elements (a
+// token-major tensor read with K = tokens, say). An MN tile is KS K-rows of BM elements, 256 bytes
+// each; it travels into LDS as straight 1 KB copies whose source chunks are permuted (below), and
+// its fragments are read with the transposing LDS reads of CDNA4 (ds_read_b64_tr_b16: in every
+// 16-lane group, lane i's k-th element comes from lane i/4 + 4k at column offset i % 4), four
+// 4-byte reads per fragment for fp32.
+constexpr int kLayoutK = 0, kLayoutMN = 1;
+
+template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false, int IGLP = 1,
+          int AL = kLayoutK, int BL = kLayoutK>
 struct TileGemm {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kWaves = WM * WN;
@@ -38,6 +49,17 @@ struct TileGemm {
   static_assert((BM + BN) % (8 * kWaves) == 0, "tile rows must spread evenly over the waves");
   static_assert(NS == 2 || NS == 3, "two or three LDS stages");
   static_assert(BM % 8 == 0, "A rows end on an 8-row boundary");
+  static constexpr int KS = kStageBytes / E::kSize;  // K elements per stage
+  static constexpr int kWM = WM, kWN = WN, kAL = AL, kBL = BL;
+  static_assert(AL == kLayoutK || BM * E::kSize == 256, "an MN-major A tile is 256 bytes wide");
+  static_assert(BL == kLayoutK || BN * E::kSize == 256, "an MN-major B tile is 256 bytes wide");
+
+  // Chunk swizzle of an MN tile's K row p (even, so the two chunks of a 16-element fragment row
+  // stay adjacent): the 8 K rows one transposing read serves per half-wave (p = 8g + r, r < 4,
+  // g < 2) land in 8 distinct 32-byte bank windows.
+  __device__ __forceinline__ static int mn_swizzle(int p) {
+    return 2 * ((p & 3) | (((p >> 3) & 1) << 2));
+  }
 
   f32x4 acc[TM][TN];
 
@@ -48,9 +70,13 @@ struct TileGemm {
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Copies K-tile (a at byte ka, b at byte kb) into LDS stage `stage`. Wave w copies rows
-  // [8 (w IPW + j), +8) of the stage (A rows first, then B rows); lane l fetches row + l/8, logical
-  // chunk (l % 8) ^ (l / 8), which lands at physical chunk l % 8: the XOR-swizzled layout.
+  // Copies K-tile (a at ka, b at kb) into LDS stage `stage`. Each copy instruction fills one 1 KB
+  // slab of the stage (A's slabs first, then B's). K-major operand: ka is the byte offset along K;
+  // slab s holds rows [8s, 8s+8), lane l fetches row + l/8, logical chunk (l % 8) ^ (l / 8), which
+  // lands at physical chunk l % 8: the XOR-swizzled layout. MN-major operand: ka is the first K
+  // row; slab s holds K rows [4s, 4s+4), lane l fetches K row 4s + l/16, logical chunk
+  // (l % 16) ^ mn_swizzle(row), landing at physical chunk l % 16; src.kbytes bounds the valid
+  // M bytes of a row, and rows past the descriptor's range read as zeros.
   __device__ __forceinline__ static void issue(u32x4* lds, int stage, const Src& a, int ka,
                                                const Src& b, int kb, int wave, int lane) {
     const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds)) + uint32_t(stage * kStage) * 16;
@@ -60,10 +86,55 @@ struct TileGemm {
       const int rg = wave * IPW + j;  // wave-uniform
       const bool is_a = rg * 8 < BM;
       const Src& src = is_a ? a : b;
-      const int row = (is_a ? rg * 8 : rg * 8 - BM) + (lane >> 3);
-      const int koff = (is_a ? ka : kb) + lchunk * 16;
-      const uint32_t voff = koff < src.kbytes ? uint32_t(row) * src.ld + uint32_t(koff) : kOutOfRange;
+      const int slab = is_a ? rg : rg - BM / 8;
+      uint32_t voff;
+      if ((is_a ? AL : BL) == kLayoutMN) {
+        const int row = slab * 4 + (lane >> 4);
+        const int col = ((lane & 15) ^ mn_swizzle(row)) * 16;
+        voff = col < src.kbytes ? uint32_t((is_a ? ka : kb) + row) * src.ld + uint32_t(col) : kOutOfRange;
+      } else {
+        const int row = slab * 8 + (lane >> 3);
+        const int koff = (is_a ? ka : kb) + lchunk * 16;
+        voff = koff < src.kbytes ? uint32_t(row) * src.ld + uint32_t(koff) : kOutOfRange;
+      }
       lds_dma16(src.rsrc, voff, base + uint32_t(rg) * 1024u);
+    }
+  }
+
+  // The lane's 16-byte fragment of rows [16 blk, 16 blk + 16) of an operand region R (K-major or
+  // MN-major), sub-step ks of the stage: row lane % 16, K elements of lane group lane / 16.
+  template <int L>
+  __device__ __forceinline__ static u32x4 frag(const u32x4* R, int blk, int ks, int lane) {
+    const int lr = lane & 15, q = lane >> 4;
+    if constexpr (L == kLayoutK) {
+      return R[(blk * 16 + lr) * kRowChunks + ((ks * 4 + q) ^ (lr & 7))];
+    } else if constexpr (sizeof(typename E::T) == 2) {
+      // K rows 32 ks + 8 q + lr/4 (+4), 8 bytes at column 16 blk + 4 (lr % 4)
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      const char* base = reinterpret_cast<const char*>(R);
+      const int cb = blk * 32 + 8 * (lr & 3);  // byte within the 256-byte K row
+      const int p0 = 32 * ks + 8 * q + (lr >> 2);
+      const int p1 = p0 + 4;
+      const char* a0 = base + p0 * 256 + ((((cb >> 4) ^ mn_swizzle(p0)) << 4) | (cb & 15));
+      const char* a1 = base + p1 * 256 + ((((cb >> 4) ^ mn_swizzle(p1)) << 4) | (cb & 15));
+      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(a0));
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(a1));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
+      return u32x4{w0[0], w0[1], w1[0], w1[1]};
+    } else {
+      // fp32: the four K rows 16 ks + 4 q + c of column 16 blk + lr
+      const char* base = reinterpret_cast<const char*>(R);
+      const int cb = blk * 64 + 4 * lr;
+      u32x4 r;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = 16 * ks + 4 * q + c;
+        r[c] = *reinterpret_cast<const uint32_t*>(base + p * 256 +
+                                                  ((((cb >> 4) ^ mn_swizzle(p)) << 4) | (cb & 15)));
+      }
+      return r;
     }
   }
 
@@ -79,18 +150,15 @@ struct TileGemm {
   __device__ __forceinline__ void compute(const u32x4* stage, int wm, int wn, int lane) {
     const u32x4* As = stage;
     const u32x4* Bs = stage + BM * kRowChunks;
-    const int lr = lane & 15;
-    const int q = lane >> 4;
     if (PRIO) __builtin_amdgcn_s_setprio(1);
     if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
 #pragma unroll
     for (int ks = 0; ks < kRowChunks / 4; ++ks) {
-      const int ch = (ks * 4 + q) ^ (lr & 7);  // rows below differ from lr by multiples of 16
       u32x4 a[TM], b[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = As[(wm * WTM + i * 16 + lr) * kRowChunks + ch];
+      for (int i = 0; i < TM; ++i) a[i] = frag<AL>(As, wm * TM + i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = Bs[(wn * WTN + j * 16 + lr) * kRowChunks + ch];
+      for (int j = 0; j < TN; ++j) b[j] = frag<BL>(Bs, wn * TN + j, ks, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -164,6 +232,10 @@ struct TileGemm {
     constexpr int kCpr = WTM * int(sizeof(T)) / 16;  // 16-byte chunks per staged row
     constexpr int kRegionBytes = WTM * WTN * int(sizeof(T));
     static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "staged row must be 2^k chunks");
+    // The 16 columns one write instruction covers start kCpr*16 bytes apart; kPer of them share a
+    // 256-byte bank period, so the chunk swizzle takes col / kPer: the 16 rows' chunks then fall in
+    // distinct banks.
+    constexpr int kPer = kCpr >= 16 ? 1 : 16 / kCpr;
     static_assert(WM * WN * kRegionBytes <= kLds * 16, "staging regions exceed the LDS tiles");
     char* region = reinterpret_cast<char*>(lds) + wave * kRegionBytes;
     const int lr = lane & 15;
@@ -177,7 +249,7 @@ struct TileGemm {
         T v[4];
         conv(i, j, wm * WTM + row, wn * WTN + col, acc[i][j], v);
         const int byte = row * int(sizeof(T));
-        char* dst = region + col * (kCpr * 16) + (((byte >> 4) ^ (col & (kCpr - 1))) << 4) + (byte & 15);
+        char* dst = region + col * (kCpr * 16) + (((byte >> 4) ^ ((col / kPer) & (kCpr - 1))) << 4) + (byte & 15);
         if constexpr (sizeof(T) == 2) {
           u32x2 w;
           w[0] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
@@ -192,7 +264,7 @@ struct TileGemm {
       const int idx = lane + k * 64;
       const int col = idx / kCpr, ch = idx % kCpr;
       const u32x4 chunk = *reinterpret_cast<const u32x4*>(
-          region + col * (kCpr * 16) + ((ch ^ (col & (kCpr - 1))) << 4));
+          region + col * (kCpr * 16) + ((ch ^ ((col / kPer) & (kCpr - 1))) << 4));
       emit(wn * WTN + col, wm * WTM + ch * (16 / int(sizeof(T))), chunk);
     }
   }
@@ -247,6 +319,16 @@ struct TileGemm {
       for (int j = 0; j < TN; ++j) f(wm * WTM + i * 16 + q * 4, wn * WTN + j * 16 + lr, acc[i][j]);
   }
 };
+
+// An MN-major operand of a TileGemm: K rows [row0, row0 + k_rows) of a row-major tensor with
+// row pitch ld_elems, columns [m0, m0 + m_valid) valid (a tile reads 256 bytes of each row from
+// column m0; columns past m_valid and rows past k_rows read as zeros). m_valid·esz must be a
+// multiple of 16 (every dimension here is a multiple of 8).
+__device__ __forceinline__ Src make_src_mn(const void* base, int64_t row0, int64_t ld_elems, int esz,
+                                           int k_rows, int64_t m0, int m_valid) {
+  return make_src(reinterpret_cast<const char*>(base) + m0 * esz, row0, ld_elems, esz, k_rows,
+                  k_rows, m_valid);
+}
 
 struct NoPre {
   __device__ __forceinline__ void operator()(int) const {}
@@ -342,9 +424,8 @@ struct ProjArgs {
   int rope;          // rotate the four heads (rotary position embedding)
   double log2_base;  // log2 of the rotary base
   // Written only by the EXTRA instantiation (the backward pass recomputes the projection, the
-  // gate's columns included, and also needs the pre-activations and V in token-major order):
+  // gate's columns included, and also needs the pre-activations):
   typename E::T* Hr;  // [M, e+s]: X W_v | X W_z before SiLU
-  typename E::T* Vr;  // [M, e]: V = SiLU(X W_v)
   typename E::T* Hu;  // [M, e]: X W_u before SiLU
 };
 
@@ -467,16 +548,6 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
                                  if (row < p.M)
                                    *reinterpret_cast<u32x4*>(p.Hr + int64_t(row) * hcols + col) = chunk;
                                });
-      g.template stage_cols<T>(lds, wave, wm, wn, lane,
-                               [&](int, int, int, int, const f32x4& v, T* out) {
-#pragma unroll
-                                 for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
-                               },
-                               [&](int r, int cl, const u32x4& chunk) {
-                                 const int row = m0 + r, col = n0 + cl - cu;
-                                 if (row < p.M)
-                                   *reinterpret_cast<u32x4*>(p.Vr + int64_t(row) * e + col) = chunk;
-                               });
     }
     return;
   }
@@ -503,10 +574,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
     const int col = gcol - cu;  // V column, or e + head feature
     if constexpr (EXTRA) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p.Hr[int64_t(row + k) * hcols + col] = from_f32<E>(v[k]);
-        if (col < e) p.Vr[int64_t(row + k) * e + col] = from_f32<E>(y[k]);
-      }
+      for (int k = 0; k < 4; ++k) p.Hr[int64_t(row + k) * hcols + col] = from_f32<E>(v[k]);
     }
     if (col < e) {
       store4(p.Vt + (bg * e + col) * c + t, y[0], y[1], y[2], y[3]);
@@ -634,9 +702,11 @@ struct StatesArgs {
   int rev;
 };
 
-template <class E, int BM, int BN, int WM, int WN, int NS>
+// L = kLayoutMN reads K_lin and V token-major ([tokens, s] and [tokens, e] behind the Klt and Vt
+// pointers) instead of chunk-transposed.
+template <class E, int BM, int BN, int WM, int WN, int NS, int L = kLayoutK>
 __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds, int bid) {
-  using G = TileGemm<E, BM, BN, WM, WN, NS>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS, false, 1, L, L>;
   const int nts = (p.s + BM - 1) / BM;
   const int nte = (p.e + BN - 1) / BN;
   const int lid = xcd_remap(bid, p.B * p.ng * nts * nte);
@@ -676,9 +746,15 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
   g.run(lds, nchunks * nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
           const int64_t chunk = phys(t / nk);
-          sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, BM, p.c);
-          sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, BN, p.c);
-          ka = kb = (t % nk) * kStageBytes;
+          if constexpr (L == kLayoutK) {
+            sa = make_src(p.Klt, chunk * p.s + m0, p.c, E::kSize, p.s - m0, BM, p.c);
+            sb = make_src(p.Vt, chunk * p.e + n0, p.c, E::kSize, p.e - n0, BN, p.c);
+            ka = kb = (t % nk) * kStageBytes;
+          } else {
+            sa = make_src_mn(p.Klt, chunk * p.c, p.s, E::kSize, p.c, m0, p.s - m0);
+            sb = make_src_mn(p.Vt, chunk * p.c, p.e, E::kSize, p.c, n0, p.e - n0);
+            ka = kb = (t % nk) * G::KS;
+          }
         },
         [&](int t) {
           // exclusive prefix inside the group: chunk g reads the group's chunks before it. With
