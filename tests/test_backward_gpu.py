@@ -31,6 +31,10 @@ CASES = {
     "groups_noncausal_bf16": (8, 256, 64, 1536, 16, 8, False, "bf16", None),
     "rope_causal_f32": (1, 256, 64, 128, 32, 64, True, "f32", 100.0),
     "rope_causal_bf16": (2, 256, 128, 256, 64, 128, True, "bf16", 10000.0),
+    "rope_noncausal_f32": (2, 192, 48, 72, 16, 64, False, "f32", 50.0),
+    "chunk_eq_n_noncausal_f32": (2, 128, 32, 64, 24, 128, False, "f32", None),
+    "chunk_eq_n_noncausal_bf16": (2, 256, 64, 128, 32, 256, False, "bf16", None),
+    "wide_s_groups_causal_bf16": (4, 512, 64, 256, 256, 32, True, "bf16", None),
 }
 
 
