@@ -178,6 +178,7 @@ constexpr int kAttnCols = 128;   // value columns per workgroup
 constexpr int kAttnGroups = kAttnCols / 8;  // groups of 8 consecutive columns
 constexpr int kAttnThreads = 1024;
 constexpr int kAttnSlots = kAttnThreads / kAttnGroups;  // row slots (64)
+constexpr int kPreV = 2, kPreS = 2;  // cache and state rows per slot loaded before the key weights
 
 // 8 consecutive elements as fp32 (16 bytes for bf16, two 16-byte loads for fp32).
 __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
@@ -209,6 +210,35 @@ __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const int col0 = blockIdx.x * kAttnCols;
+  // slot `sl` takes cache and state rows sl, sl + kAttnSlots, ...; group `cg` owns 8 consecutive
+  // value columns. The first kPreV cache rows and kPreS state rows of the slot are loaded here,
+  // before the key weights: they do not depend on them, so their latency overlaps that phase.
+  const int cg = tid % kAttnGroups, sl = tid / kAttnGroups;
+  const int col = col0 + cg * 8;
+  const bool col_ok = col < p.e;  // e % 8 == 0: the 8 columns are all valid or all past the end
+  const typename E::T* vb = p.Vc + int64_t(b) * p.c * p.e + col;
+  const float* sb = p.S + int64_t(b) * p.s * p.e + col;
+  float pv[kPreV][8], ps[kPreS][8];
+#pragma unroll
+  for (int r = 0; r < kPreV; ++r) {
+    const int j = sl + r * kAttnSlots;
+    if (col_ok && j <= p.i) {
+      load8(vb + int64_t(j) * p.e, pv[r]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) pv[r][m] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kPreS; ++r) {
+    const int k = sl + r * kAttnSlots;
+    if (col_ok && k < p.s) {
+      load8(sb + int64_t(k) * p.e, ps[r]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ps[r][m] = 0.f;
+    }
+  }
   for (int k = tid; k < p.s; k += kAttnThreads) {
     qq[k] = to_f32(p.Qq[int64_t(b) * p.s + k]);
     ql[k] = to_f32(p.Ql[int64_t(b) * p.s + k]) * p.inv_n;
@@ -240,24 +270,34 @@ __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p
   }
   __syncthreads();
 
-  // Σ_j w_j v_j over the cache rows and Σ_k (q_lin,k / n) S_k over the state rows; slot `sl`
-  // takes rows sl, sl + kAttnSlots, ...; group `cg` owns 8 consecutive value columns.
-  const int cg = tid % kAttnGroups, sl = tid / kAttnGroups;
-  const int col = col0 + cg * 8;
+  // Σ_j w_j v_j over the cache rows and Σ_k (q_lin,k / n) S_k over the state rows: the prefetched
+  // rows first, then the rest.
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (col < p.e) {  // e % 8 == 0: the 8 columns are all valid or all past the end
-    const typename E::T* vb = p.Vc + int64_t(b) * p.c * p.e + col;
+  if (col_ok) {
+#pragma unroll
+    for (int r = 0; r < kPreV; ++r) {
+      const int j = sl + r * kAttnSlots;
+      const float wj = j <= p.i ? w[j] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = fmaf(wj, pv[r][m], acc[m]);
+    }
+#pragma unroll
+    for (int r = 0; r < kPreS; ++r) {
+      const int k = sl + r * kAttnSlots;
+      const float qk = k < p.s ? ql[k] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = fmaf(qk, ps[r][m], acc[m]);
+    }
 #pragma unroll 4
-    for (int j = sl; j <= p.i; j += kAttnSlots) {
+    for (int j = sl + kPreV * kAttnSlots; j <= p.i; j += kAttnSlots) {
       float v[8];
       load8(vb + int64_t(j) * p.e, v);
       const float wj = w[j];
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc[m] = fmaf(wj, v[m], acc[m]);
     }
-    const float* sb = p.S + int64_t(b) * p.s * p.e + col;
 #pragma unroll 4
-    for (int k = sl; k < p.s; k += kAttnSlots) {
+    for (int k = sl + kPreS * kAttnSlots; k < p.s; k += kAttnSlots) {
       float v[8];
       load8(sb + int64_t(k) * p.e, v);
       const float qk = ql[k];
