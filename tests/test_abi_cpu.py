@@ -351,3 +351,12 @@ def test_backward_aliasing_rejected(over):
 @pytest.mark.parametrize("base", [-1.0, float("nan"), float("inf")])
 def test_backward_rope_base_validated(base):
     assert _bcall(rope_base=base) == fg.ERR_BAD_SHAPE
+
+
+def test_backward_rejects_shapes_beyond_its_descriptor_ranges():
+    # a chunk's value block read as one operand (e x chunk elements) must stay under 4 GiB
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.backward_workspace_size(1, 32768, 64, 65536, 128, 32768, True, fg.BF16)
+    assert ei.value.code == fg.ERR_BAD_SHAPE
+    # the same widths with a short chunk are fine
+    assert fg.backward_workspace_size(1, 1024, 64, 1024, 128, 256, True, fg.BF16) > 0
