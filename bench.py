@@ -498,6 +498,27 @@ def main():
             stage_ms[st].append(events.ms(h[i], h[i + 1]))
         gpu_ms.append(events.ms(h[0], h[nst]))
     events.close()
+
+    # Step-time distribution, from a separate pass of the same number of steps, each bracketed by
+    # two events on the stream (between steps only, never between kernels); `value` does not use it.
+    sev = HipEvents(2 * args.steps)
+    for k in range(args.steps):
+        events_rec = sev.handles[2 * k:2 * k + 2]
+        sev.hip.hipEventRecord(ctypes.c_void_p(events_rec[0]), ctypes.c_void_p(stream))
+        step()
+        sev.hip.hipEventRecord(ctypes.c_void_p(events_rec[1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    per_step = sorted(sev.ms(sev.handles[2 * k], sev.handles[2 * k + 1]) for k in range(args.steps))
+    sev.close()
+
+    def quantile(q):
+        return per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
+    step_q = {"p10": round(quantile(0.1), 4), "p50": round(quantile(0.5), 4),
+              "p90": round(quantile(0.9), 4)}
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "compute_units": props.multi_processor_count,
+              "gcn_arch": getattr(props, "gcnArchName", None),
+              "max_sclk_mhz": round(getattr(props, "clock_rate", 0) / 1000.0) or None}
     stage_avg = {st: statistics.mean(v) for st, v in stage_ms.items()}
 
     flops = alg_flops(B, n, d, e, s, c, causal)
@@ -574,6 +595,8 @@ def main():
         if dtype == "bf16" else None,
         "alg_gflop": round(total_flops / 1e9, 2),
         "gpu_ms_per_instrumented_step": round(statistics.mean(gpu_ms), 4),
+        "step_ms_quantiles": step_q,
+        "device": device,
         "roofline": roofline,
         "stages": stages,
         "cpu_baseline": cpu,
