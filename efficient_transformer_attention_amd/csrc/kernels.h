@@ -763,10 +763,24 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
           if (write_local && t % nk == 0) write_state(g, p.St + phys(t / nk) * es);
         },
         wave, wm, wn, lane);
+  // The final tile leaves through LDS (the stages are idle now) as 16-byte runs along s.
+  auto write_final = [&](typename E::T* dst) {
+    using T = typename E::T;
+    g.template stage_rows<T>(
+        lds, wave, wm, wn, lane,
+        [&](int, int, int, int, const f32x4& v, T* out) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k] * p.inv_n);
+        },
+        [&](int cl, int r, const u32x4& chunk) {
+          const int i = m0 + r, j = n0 + cl;
+          if (i < p.s && j < p.e) *reinterpret_cast<u32x4*>(dst + int64_t(j) * p.s + i) = chunk;
+        });
+  };
   if (!p.causal && p.ng == 1)
-    write_state(g, p.St + int64_t(b) * es);
+    write_final(p.St + int64_t(b) * es);
   else if (!p.causal || grp < p.ng - 1)  // the last group's total is never read when causal
-    write_state(g, p.Carry + (int64_t(b) * p.ng + grp) * es);
+    write_final(p.Carry + (int64_t(b) * p.ng + grp) * es);
 }
 
 // ------------------------------------------------------------------------------ scores + states
