@@ -19,7 +19,8 @@ positions (c .. 2c-1, the last step folding the chunk into the state) after chun
 state untimed, with its HBM roofline (algorithmic bytes per step, see decode_bytes) and the
 oracle's decode step timed on the host. The "backward" object times flash_gau_backward on the same
 batch (2 x the forward's algorithmic FLOPs), with the oracle's backward on one sequence as its CPU
-baseline and parity check. Two more objects time the same layer with the rotary
+baseline and parity check, and (saved_activations) a training step that keeps the forward's
+intermediates: flash_gau_forward_train, then flash_gau_backward_saved. Two more objects time the same layer with the rotary
 embedding (flash_gau_forward_rope) and compare FLASH-Quad (chunk = n: one quadratic chunk, no
 global term) with FLASH (the workload's chunk) on longer causal sequences of the same width.
 """
@@ -206,11 +207,35 @@ def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10):
     torch.cuda.synchronize(dev)
     ms = (time.perf_counter() - t0) * 1e3 / steps
     flops = 2.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
+    # a training step without the backward's recompute: forward_train, then backward_saved
+    O = torch.empty_like(args[0])
+    for _ in range(2):
+        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
+    torch.cuda.synchronize(dev)
+    t_f = t_b = 0.0
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(steps):
+        e0.record()
+        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+        e1.record()
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
+        e2.record()
+        torch.cuda.synchronize(dev)
+        t_f += e0.elapsed_time(e1)
+        t_b += e1.elapsed_time(e2)
+    t_f, t_b = t_f / steps, t_b / steps
+    training = {"forward_train_ms": round(t_f, 4), "backward_saved_ms": round(t_b, 4),
+                "train_step_tokens_per_s": round(B * n / ((t_f + t_b) * 1e-3), 1),
+                "frac_bf16_peak": round(3.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
+                                        / ((t_f + t_b) * 1e-3) / 1e12 / PEAK["bf16"], 4)
+                if dtype == "bf16" else None}
     rec = {"workload": f"backward of the same layer and batch", "steps": steps,
            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
            "alg_gflop": round(flops / 1e9, 2),
            "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-           "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK["bf16"], 4) if dtype == "bf16" else None}
+           "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK["bf16"], 4) if dtype == "bf16" else None,
+           "saved_activations": training}
     if cpu_seconds > 0:
         dO_np[1:] = 0.0
         g = fg.flash_gau_backward(*args, up(dO_np), c, causal, workspace=ws, out=out)

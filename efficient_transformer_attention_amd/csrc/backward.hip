@@ -60,22 +60,6 @@ constexpr int kadv() {
   return (IS_A ? G::kAL : G::kBL) == KK ? kStageBytes : G::KS;
 }
 
-// Four consecutive elements as floats (8-byte aligned for bf16, 16-byte for fp32).
-__device__ __forceinline__ void load4f(const uint16_t* p, float* o) {
-  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-  o[0] = __uint_as_float(v[0] << 16);
-  o[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-  o[2] = __uint_as_float(v[1] << 16);
-  o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-}
-__device__ __forceinline__ void load4f(const float* p, float* o) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  o[0] = v[0];
-  o[1] = v[1];
-  o[2] = v[2];
-  o[3] = v[3];
-}
-
 // One tile of C = A Bᵀ over nk K-tiles from the offsets ka0, kb0 (bytes or rows, by layout),
 // stored fp32 row-major at out (pitch ldo), rows < rows and columns < cols only.
 template <class G>
@@ -854,34 +838,29 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
 }
 
 // ------------------------------------------------------------------------------ launches
+// The forward's intermediates as the backward reads them: pack, the projection over all three
+// weights (also storing H_u and H_v | H_z), scores and prefix states. `flash_gau_backward` runs this
+// first; `flash_gau_forward_train` runs it as part of a forward and leaves it in the workspace.
 template <class E>
-int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
-                    const void* W_z, const float* gamma, const float* beta, const void* W_o,
-                    const void* dO, int causal, float rope_base, void* dX, void* dW_u, void* dW_v,
-                    void* dW_z, float* dgamma, float* dbeta, void* dW_o, char* ws,
-                    hipStream_t stream) {
+void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
+                      const void* W_z, const float* gamma, const float* beta, const void* W_o,
+                      int causal, float rope_base, char* ws, hipStream_t stream) {
   using T = typename E::T;
   using S = Shapes<E>;
-  constexpr int kThreads = BGemm<E>::kThreads;
   const Plan& pl = bp.f;
   auto W = [&](int r) { return reinterpret_cast<T*>(ws + pl.off[r]); };
   auto R = [&](int r) { return reinterpret_cast<T*>(ws + bp.off[r]); };
-  auto Rf = [&](int r) { return reinterpret_cast<float*>(ws + bp.off[r]); };
   T *WcatT = W(FLASHGAU_WS_WCAT_T), *WoT = W(FLASHGAU_WS_WO_T), *Vt = W(FLASHGAU_WS_VT);
   T *Qq = W(FLASHGAU_WS_QQ), *Kq = W(FLASHGAU_WS_KQ), *Ql = W(FLASHGAU_WS_QL);
   T *Klt = W(FLASHGAU_WS_KLT), *P = W(FLASHGAU_WS_P), *St = W(FLASHGAU_WS_ST);
   T* Carry = W(FLASHGAU_WS_CARRY);
   const T* Xp = reinterpret_cast<const T*>(X);
-  const T* dOp = reinterpret_cast<const T*>(dO);
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
   const int nbg = int(pl.nbg), G = int(pl.G), B = int(pl.B);
-  const int bt = int(bp.bt);
   const bool lin = !(causal && pl.G == 1);
   const int rope = rope_base > 0.0f ? 1 : 0;
   const double log2_base = rope ? log2(double(rope_base)) : 0.0;
   const float inv_n = float(1.0 / double(pl.n));
-
-  // ---- recompute the forward's intermediates
   launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   {
     ProjArgs<E> a{Xp, WcatT, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
@@ -907,6 +886,66 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     hipLaunchKernelGGL(carry_kernel<E>, dim3(unsigned(cdiv(pl.B * e * s / 8, 256))), dim3(256), 0,
                        stream, a);
   }
+}
+
+// A forward that keeps what the backward needs: the recompute stages, then the forward's mix
+// (its gate read from the stored H_u instead of its own GEMM) and output projection.
+template <class E>
+int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
+                         const void* W_z, const float* gamma, const float* beta, const void* W_o,
+                         int causal, float rope_base, void* O, char* ws, hipStream_t stream) {
+  using T = typename E::T;
+  using S = Shapes<E>;
+  const Plan& pl = bp.f;
+  auto W = [&](int r) { return reinterpret_cast<T*>(ws + pl.off[r]); };
+  auto R = [&](int r) { return reinterpret_cast<T*>(ws + bp.off[r]); };
+  const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
+  const bool lin = !(causal && pl.G == 1);
+  launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream);
+  {
+    MixArgs<E> a{W(FLASHGAU_WS_VT), W(FLASHGAU_WS_ST), W(FLASHGAU_WS_P), W(FLASHGAU_WS_QL),
+                 reinterpret_cast<const T*>(X), W(FLASHGAU_WS_WCAT_T), W(FLASHGAU_WS_Y), d,
+                 int(pl.nbg), int(pl.G), c, e, s, causal, int(lin), R(BR_HU)};
+    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
+    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS, true>),
+                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+  }
+  {
+    OutArgs<E> a{W(FLASHGAU_WS_WO_T), W(FLASHGAU_WS_Y), reinterpret_cast<T*>(O), M, d, e};
+    const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
+    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
+                                    S::kOutPrio>),
+                       dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
+}
+
+template <class E>
+int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
+                    const void* W_z, const float* gamma, const float* beta, const void* W_o,
+                    const void* dO, int causal, float rope_base, void* dX, void* dW_u, void* dW_v,
+                    void* dW_z, float* dgamma, float* dbeta, void* dW_o, char* ws,
+                    hipStream_t stream, bool recompute) {
+  using T = typename E::T;
+  constexpr int kThreads = BGemm<E>::kThreads;
+  const Plan& pl = bp.f;
+  auto R = [&](int r) { return reinterpret_cast<T*>(ws + bp.off[r]); };
+  auto Rf = [&](int r) { return reinterpret_cast<float*>(ws + bp.off[r]); };
+  auto W = [&](int r) { return reinterpret_cast<T*>(ws + pl.off[r]); };
+  T *Vt = W(FLASHGAU_WS_VT), *Qq = W(FLASHGAU_WS_QQ), *Kq = W(FLASHGAU_WS_KQ);
+  T *Ql = W(FLASHGAU_WS_QL), *Klt = W(FLASHGAU_WS_KLT), *P = W(FLASHGAU_WS_P), *St = W(FLASHGAU_WS_ST);
+  const T* Xp = reinterpret_cast<const T*>(X);
+  const T* dOp = reinterpret_cast<const T*>(dO);
+  const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
+  const int nbg = int(pl.nbg), G = int(pl.G), B = int(pl.B);
+  const int bt = int(bp.bt);
+  const bool lin = !(causal && pl.G == 1);
+  const int rope = rope_base > 0.0f ? 1 : 0;
+  const double log2_base = rope ? log2(double(rope_base)) : 0.0;
+  const float inv_n = float(1.0 / double(pl.n));
+
+  if (recompute)
+    launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream);
 
   // ---- gate, output projection and V̂
   {
@@ -1009,6 +1048,82 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
 }
 
+// Host-side checks shared by the entry points that take the backward workspace: outs[i] holds
+// nout[i] bytes (0: not used by this call) and must be aligned to amask[i] + 1 bytes.
+int check_call(const BPlan& bp, const void* X, const void* W_u, const void* W_v, const void* W_z,
+               const float* gamma, const float* beta, const void* W_o, const void* dO,
+               float rope_base, void* const* outs, const size_t* nout, const uint32_t* amask,
+               int nouts, void* workspace, size_t workspace_bytes) {
+  if (!(rope_base >= 0.0f) || !std::isfinite(rope_base)) return FLASHGAU_ERR_BAD_SHAPE;
+  for (int i = 0; i < nouts; ++i)
+    if (nout[i] && !outs[i]) return FLASHGAU_ERR_NULL_PTR;
+  for (int i = 0; i < nouts; ++i)
+    if (nout[i] && (reinterpret_cast<uintptr_t>(outs[i]) & amask[i])) return FLASHGAU_ERR_MISALIGNED;
+  for (int i = 0; i < nouts; ++i)
+    for (int j = i + 1; j < nouts; ++j)
+      if (overlaps(outs[i], nout[i], outs[j], nout[j])) return FLASHGAU_ERR_ALIASING;
+  if (bp.f.M == 0) return FLASHGAU_OK;
+  if (!X || !W_u || !W_v || !W_z || !gamma || !beta || !W_o || !workspace) return FLASHGAU_ERR_NULL_PTR;
+  if (misaligned(X) || misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o) ||
+      (dO && misaligned(dO)) || misaligned(workspace) ||
+      (reinterpret_cast<uintptr_t>(gamma) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return FLASHGAU_ERR_MISALIGNED;
+  if (workspace_bytes < bp.total) return FLASHGAU_ERR_WORKSPACE;
+  const size_t es = size_t(bp.f.esz);
+  const size_t nX = size_t(bp.f.M) * size_t(bp.f.d) * es;
+  const size_t nWu = size_t(bp.f.d) * size_t(bp.f.e) * es, nWz = size_t(bp.f.d) * size_t(bp.f.s) * es;
+  const size_t nGB = size_t(4) * size_t(bp.f.s) * sizeof(float);
+  const void* ins[] = {X, W_u, W_v, W_z, W_o, gamma, beta, dO};
+  const size_t nin[] = {nX, nWu, nWu, nWz, nWu, nGB, nGB, dO ? nX : 0};
+  for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < nouts; ++j)
+      if (overlaps(outs[j], nout[j], ins[i], nin[i])) return FLASHGAU_ERR_ALIASING;
+    if (overlaps(workspace, bp.total, ins[i], nin[i])) return FLASHGAU_ERR_ALIASING;
+  }
+  for (int j = 0; j < nouts; ++j)
+    if (overlaps(outs[j], nout[j], workspace, bp.total)) return FLASHGAU_ERR_ALIASING;
+  return FLASHGAU_OK;
+}
+
+int backward_impl(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                  const float* gamma, const float* beta, const void* W_o, const void* dO,
+                  int64_t chunk, int causal, float rope_base, int64_t B, int64_t n, int64_t d,
+                  int64_t e, int64_t s, flashgau_dtype dtype, void* dX, void* dW_u, void* dW_v,
+                  void* dW_z, float* dgamma, float* dbeta, void* dW_o, void* workspace,
+                  size_t workspace_bytes, void* hip_stream, bool recompute) {
+  BPlan bp;
+  const int rc = make_bplan(B, n, d, e, s, chunk, causal, dtype, &bp);
+  if (rc != FLASHGAU_OK) return rc;
+  if (rope_base > 0.0f && (s & 1)) return FLASHGAU_ERR_BAD_SHAPE;
+  const size_t es = size_t(bp.f.esz);
+  const size_t nX = size_t(bp.f.M) * size_t(d) * es;
+  const size_t nWu = size_t(d) * size_t(e) * es, nWz = size_t(d) * size_t(s) * es;
+  const size_t nGB = size_t(4) * size_t(s) * sizeof(float);
+  void* outs[] = {dW_u, dW_v, dW_z, dW_o, dgamma, dbeta, dX};
+  const size_t nout[] = {nWu, nWu, nWz, nWu, nGB, nGB, nX};
+  const uint32_t amask[] = {15u, 15u, 15u, 15u, 3u, 3u, 15u};
+  if (bp.f.M > 0 && !dO) return FLASHGAU_ERR_NULL_PTR;
+  const int vc = check_call(bp, X, W_u, W_v, W_z, gamma, beta, W_o, dO, rope_base, outs, nout,
+                            amask, 7, workspace, workspace_bytes);
+  if (vc != FLASHGAU_OK) return vc;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  if (bp.f.M == 0) {
+    // no tokens: every weight gradient is zero
+    for (int i = 0; i < 6; ++i)
+      hipLaunchKernelGGL(zero_kernel, dim3(unsigned(std::min<size_t>(1024, (nout[i] / 4 + 255) / 256))),
+                         dim3(256), 0, stream, reinterpret_cast<uint32_t*>(outs[i]),
+                         int64_t(nout[i] / 4));
+    return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
+  }
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int cz = causal ? 1 : 0;
+  if (dtype == FLASHGAU_BF16)
+    return launch_backward<BF16>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, dO, cz, rope_base, dX, dW_u,
+                                 dW_v, dW_z, dgamma, dbeta, dW_o, ws, stream, recompute);
+  return launch_backward<F32>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, dO, cz, rope_base, dX, dW_u,
+                              dW_v, dW_z, dgamma, dbeta, dW_o, ws, stream, recompute);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1030,64 +1145,47 @@ int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const vo
                        int64_t e, int64_t s, flashgau_dtype dtype, void* dX, void* dW_u,
                        void* dW_v, void* dW_z, float* dgamma, float* dbeta, void* dW_o,
                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return backward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base, B, n, d, e,
+                       s, dtype, dX, dW_u, dW_v, dW_z, dgamma, dbeta, dW_o, workspace,
+                       workspace_bytes, hip_stream, true);
+}
+
+int flash_gau_backward_saved(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                             const float* gamma, const float* beta, const void* W_o,
+                             const void* dO, int64_t chunk, int causal, float rope_base, int64_t B,
+                             int64_t n, int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,
+                             void* dX, void* dW_u, void* dW_v, void* dW_z, float* dgamma,
+                             float* dbeta, void* dW_o, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+  return backward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base, B, n, d, e,
+                       s, dtype, dX, dW_u, dW_v, dW_z, dgamma, dbeta, dW_o, workspace,
+                       workspace_bytes, hip_stream, false);
+}
+
+int flash_gau_forward_train(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                            const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                            int causal, float rope_base, int64_t B, int64_t n, int64_t d, int64_t e,
+                            int64_t s, flashgau_dtype dtype, void* O, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
   BPlan bp;
   const int rc = make_bplan(B, n, d, e, s, chunk, causal, dtype, &bp);
   if (rc != FLASHGAU_OK) return rc;
-  if (!(rope_base >= 0.0f) || !std::isfinite(rope_base)) return FLASHGAU_ERR_BAD_SHAPE;
   if (rope_base > 0.0f && (s & 1)) return FLASHGAU_ERR_BAD_SHAPE;
-  if (!dW_u || !dW_v || !dW_z || !dgamma || !dbeta || !dW_o) return FLASHGAU_ERR_NULL_PTR;
-  const size_t es = size_t(bp.f.esz);
-  const size_t nX = size_t(bp.f.M) * size_t(d) * es;
-  const size_t nWu = size_t(d) * size_t(e) * es, nWz = size_t(d) * size_t(s) * es;
-  const size_t nGB = size_t(4) * size_t(s) * sizeof(float);
+  if (bp.f.M == 0) return FLASHGAU_OK;
+  void* outs[] = {O};
+  const size_t nout[] = {size_t(bp.f.M) * size_t(d) * size_t(bp.f.esz)};
+  const uint32_t amask[] = {15u};
+  const int vc = check_call(bp, X, W_u, W_v, W_z, gamma, beta, W_o, nullptr, rope_base, outs, nout,
+                            amask, 1, workspace, workspace_bytes);
+  if (vc != FLASHGAU_OK) return vc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  if (misaligned(dW_u) || misaligned(dW_v) || misaligned(dW_z) || misaligned(dW_o) ||
-      (reinterpret_cast<uintptr_t>(dgamma) & 3u) || (reinterpret_cast<uintptr_t>(dbeta) & 3u))
-    return FLASHGAU_ERR_MISALIGNED;
-  // the outputs must not overlap one another
-  {
-    void* outs[] = {dW_u, dW_v, dW_z, dW_o, dgamma, dbeta, dX};
-    const size_t nout[] = {nWu, nWu, nWz, nWu, nGB, nGB, nX};
-    const int cnt = bp.f.M > 0 ? 7 : 6;
-    for (int i = 0; i < cnt; ++i)
-      for (int j = i + 1; j < cnt; ++j)
-        if (overlaps(outs[i], nout[i], outs[j], nout[j])) return FLASHGAU_ERR_ALIASING;
-  }
-  if (bp.f.M == 0) {
-    // no tokens: every weight gradient is zero
-    void* outs[] = {dW_u, dW_v, dW_z, dW_o, dgamma, dbeta};
-    const size_t nout[] = {nWu, nWu, nWz, nWu, nGB, nGB};
-    for (int i = 0; i < 6; ++i)
-      hipLaunchKernelGGL(zero_kernel, dim3(unsigned(std::min<size_t>(1024, (nout[i] / 4 + 255) / 256))),
-                         dim3(256), 0, stream, reinterpret_cast<uint32_t*>(outs[i]),
-                         int64_t(nout[i] / 4));
-    return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
-  }
-  if (!X || !W_u || !W_v || !W_z || !gamma || !beta || !W_o || !dO || !dX || !workspace)
-    return FLASHGAU_ERR_NULL_PTR;
-  if (misaligned(X) || misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o) ||
-      misaligned(dO) || misaligned(dX) || misaligned(workspace) ||
-      (reinterpret_cast<uintptr_t>(gamma) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u))
-    return FLASHGAU_ERR_MISALIGNED;
-  if (workspace_bytes < bp.total) return FLASHGAU_ERR_WORKSPACE;
-  {
-    const void* ins[] = {X, W_u, W_v, W_z, W_o, gamma, beta, dO};
-    const size_t nin[] = {nX, nWu, nWu, nWz, nWu, nGB, nGB, nX};
-    void* outs[] = {dW_u, dW_v, dW_z, dW_o, dgamma, dbeta, dX, workspace};
-    const size_t nout[] = {nWu, nWu, nWz, nWu, nGB, nGB, nX, bp.total};
-    for (int i = 0; i < 8; ++i)
-      for (int j = 0; j < 8; ++j)
-        if (overlaps(outs[j], nout[j], ins[i], nin[i])) return FLASHGAU_ERR_ALIASING;
-    for (int j = 0; j < 7; ++j)
-      if (overlaps(outs[j], nout[j], workspace, bp.total)) return FLASHGAU_ERR_ALIASING;
-  }
   char* ws = reinterpret_cast<char*>(workspace);
   const int cz = causal ? 1 : 0;
   if (dtype == FLASHGAU_BF16)
-    return launch_backward<BF16>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, dO, cz, rope_base, dX, dW_u,
-                                 dW_v, dW_z, dgamma, dbeta, dW_o, ws, stream);
-  return launch_backward<F32>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, dO, cz, rope_base, dX, dW_u,
-                              dW_v, dW_z, dgamma, dbeta, dW_o, ws, stream);
+    return launch_train_forward<BF16>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, cz, rope_base, O, ws,
+                                      stream);
+  return launch_train_forward<F32>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, cz, rope_base, O, ws,
+                                   stream);
 }
 
 }  // extern "C"

@@ -50,6 +50,22 @@ __device__ __forceinline__ uint16_t from_f32<BF16>(float f) { return f32_to_bf16
 template <>
 __device__ __forceinline__ float from_f32<F32>(float f) { return f; }
 
+// Four consecutive elements as floats (8-byte aligned for bf16, 16-byte for fp32).
+__device__ __forceinline__ void load4f(const uint16_t* p, float* o) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  o[0] = __uint_as_float(v[0] << 16);
+  o[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+  o[2] = __uint_as_float(v[1] << 16);
+  o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4f(const float* p, float* o) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v[0];
+  o[1] = v[1];
+  o[2] = v[2];
+  o[3] = v[3];
+}
+
 // Store four consecutive elements (8-byte aligned for bf16, 16-byte aligned for fp32).
 __device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
   u32x2 v;

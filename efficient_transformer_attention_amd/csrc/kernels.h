@@ -907,9 +907,11 @@ struct MixArgs {
   int d;
   int nbg, G, c, e, s, causal;
   int lin;  // 0: no global term (causal with a single chunk: its prefix state is empty)
+  const typename E::T* Hu;   // HU instantiation: X W_u before SiLU, [B*G*c, e], stored by the
+                             // projection (the gate's GEMM is then not run here)
 };
 
-template <class E, int BM, int BN, int WM, int WN, int NS>
+template <class E, int BM, int BN, int WM, int WN, int NS, bool HU = false>
 __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
@@ -946,7 +948,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   // share a CU (one pipeline over all three K-ranges needs more and halves the occupancy).
   G gu;
   gu.zero();
-  {
+  if constexpr (!HU) {
     const Src au = make_src(p.WuT, m0, p.d, E::kSize, p.e - m0, BM, p.d);
     const Src bu = make_src(p.X, tok0 + n0, p.d, E::kSize, p.c - n0, BN, p.d);
     const int nku = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
@@ -981,9 +983,21 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   using T = typename E::T;
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
-      [&](int fi, int fj, int, int, const f32x4& v, T* out) {
+      [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
+        float hu[4];
+        if constexpr (HU) {
+          const int j = m0 + r, i = n0 + cl;
+          if (j < p.e && i < p.c) {
+            load4f(p.Hu + (tok0 + i) * p.e + j, hu);
+          } else {
+            hu[0] = hu[1] = hu[2] = hu[3] = 0.0f;
+          }
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(gu.acc[fi][fj][k]) * v[k]);
+          for (int k = 0; k < 4; ++k) hu[k] = gu.acc[fi][fj][k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(hu[k]) * v[k]);
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, i = n0 + cl;

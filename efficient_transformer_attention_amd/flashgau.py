@@ -37,7 +37,7 @@ EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_st
            "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
            "flash_gau_decode_step", "flashgau_backward_workspace_size", "flash_gau_backward",
-           "flashgau_strerror")
+           "flash_gau_forward_train", "flash_gau_backward_saved", "flashgau_strerror")
 
 # Kernels of one forward call, in launch order (FLASHGAU_NUM_STAGES in include/flashgau.h).
 STAGES = ("pack", "proj", "scores_states", "carry", "mix", "out")
@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_backward.argtypes = [vp] * 8 + [i64, ctypes.c_int, ctypes.c_float] + [i64] * 5 + \
         [ctypes.c_int] + [vp] * 7 + [vp, sz, vp]
     L.flash_gau_backward.restype = ctypes.c_int
+    L.flash_gau_backward_saved.argtypes = L.flash_gau_backward.argtypes
+    L.flash_gau_backward_saved.restype = ctypes.c_int
+    L.flash_gau_forward_train.argtypes = L.flash_gau_forward_rope.argtypes
+    L.flash_gau_forward_train.restype = ctypes.c_int
     L.flashgau_strerror.argtypes = [ctypes.c_int]
     L.flashgau_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -371,13 +375,57 @@ def backward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_bas
                                     dgamma, dbeta, dW_o, workspace, workspace_bytes, stream)
 
 
+def forward_train_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_base, B, n, d, e, s,
+                      dtype, O, workspace, workspace_bytes, stream) -> int:
+    """Direct call of flash_gau_forward_train with integer addresses; returns the library's code."""
+    return lib().flash_gau_forward_train(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
+                                         float(rope_base), B, n, d, e, s, dtype, O, workspace,
+                                         workspace_bytes, stream)
+
+
+def backward_saved_raw(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base, B, n, d, e,
+                       s, dtype, dX, dW_u, dW_v, dW_z, dgamma, dbeta, dW_o, workspace,
+                       workspace_bytes, stream) -> int:
+    """Direct call of flash_gau_backward_saved with integer addresses; returns the library's code."""
+    return lib().flash_gau_backward_saved(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk,
+                                          int(bool(causal)), float(rope_base), B, n, d, e, s, dtype,
+                                          dX, dW_u, dW_v, dW_z, dgamma, dbeta, dW_o, workspace,
+                                          workspace_bytes, stream)
+
+
+def flash_gau_forward_train(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, workspace,
+                            rope_base=0.0, out=None, stream=None):
+    """flash_gau_forward that also leaves in ``workspace`` (uint8, at least
+    backward_workspace_size() bytes) what flash_gau_backward_saved reads. Returns O."""
+    import torch
+    B, n, d = X.shape
+    e, s = W_u.shape[1], W_z.shape[1]
+    dt = _dtype_code(X.dtype)
+    nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    if out is None:
+        out = torch.empty((B, n, d), dtype=X.dtype, device=X.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device).cuda_stream
+    tensors = (X, W_u, W_v, W_z, gamma, beta, W_o)
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous (row-major)")
+    rc = forward_train_raw(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n,
+                           d, e, s, dt, out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    if rc != OK:
+        raise FlashGauError(rc, "flash_gau_forward_train")
+    return out
+
+
 def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, rope_base=0.0,
-                       workspace=None, stream=None, out=None):
+                       workspace=None, stream=None, out=None, saved=False):
     """Gradients of Σ O ⊙ dO for O = flash_gau_forward(X, ..., chunk, causal, rope_base) on the
     GPU. Arguments as flash_gau_forward, plus dO [B, n, d] of X's dtype. Returns a dict with dX
     [B, n, d], dW_u, dW_v [d, e], dW_z [d, s], dW_o [e, d] (X's dtype) and dgamma, dbeta [4, s]
     (float32). ``out`` may hold preallocated tensors under those names; ``workspace`` (uint8) is
-    allocated when not given."""
+    allocated when not given. ``saved=True`` calls flash_gau_backward_saved: ``workspace`` must then
+    be the one a flash_gau_forward_train of the same inputs filled."""
     import torch
     B, n, d = X.shape
     e = W_u.shape[1]
@@ -406,13 +454,16 @@ def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, ro
         if k not in grads:
             grads[k] = torch.empty(shape, dtype=tdt, device=dev)
     nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
+    if saved and workspace is None:
+        raise ValueError("saved=True needs the workspace of a flash_gau_forward_train call")
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = backward_raw(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n, d, e,
-                      s, dt, *(grads[k].data_ptr() for k in GRAD_NAMES), workspace.data_ptr(),
-                      workspace.numel(), stream)
+    call = backward_saved_raw if saved else backward_raw
+    rc = call(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n, d, e,
+              s, dt, *(grads[k].data_ptr() for k in GRAD_NAMES), workspace.data_ptr(),
+              workspace.numel(), stream)
     if rc != OK:
-        raise FlashGauError(rc, "flash_gau_backward")
+        raise FlashGauError(rc, "flash_gau_backward_saved" if saved else "flash_gau_backward")
     return grads

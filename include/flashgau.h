@@ -291,6 +291,30 @@ int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const vo
                        void* dW_v, void* dW_z, float* dgamma, float* dbeta, void* dW_o,
                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Training without the backward's recompute: flash_gau_forward_train computes O exactly as
+ * flash_gau_forward_rope / flash_gau_forward do (rope_base 0: none) and also leaves in the
+ * workspace (at least flashgau_backward_workspace_size() bytes) everything the backward reads of
+ * the forward: the projection over W_u | W_v | W_z with its pre-activations, the heads, the scores,
+ * the prefix states. Its mix stage reads the stored X W_u instead of running the gate's GEMM, so
+ * O may differ from flash_gau_forward's in the last bf16 bit (same tolerance to the exact result).
+ * flash_gau_backward_saved then returns the gradients flash_gau_backward would (bitwise the same),
+ * reading that workspace instead of recomputing it: it must follow a flash_gau_forward_train of
+ * the same inputs, shapes and rope_base on the same stream, with the workspace untouched between.
+ * Arguments, layouts, alignment and aliasing rules as flash_gau_forward / flash_gau_backward. */
+int flash_gau_forward_train(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                            const float* gamma, const float* beta, const void* W_o, int64_t chunk,
+                            int causal, float rope_base, int64_t B, int64_t n, int64_t d, int64_t e,
+                            int64_t s, flashgau_dtype dtype, void* O, void* workspace,
+                            size_t workspace_bytes, void* hip_stream);
+
+int flash_gau_backward_saved(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                             const float* gamma, const float* beta, const void* W_o,
+                             const void* dO, int64_t chunk, int causal, float rope_base, int64_t B,
+                             int64_t n, int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,
+                             void* dX, void* dW_u, void* dW_v, void* dW_z, float* dgamma,
+                             float* dbeta, void* dW_o, void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
 /* Static, human-readable text for a return code ("unknown error" for other values). */
 const char* flashgau_strerror(int code);
 

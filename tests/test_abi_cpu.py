@@ -360,3 +360,51 @@ def test_backward_rejects_shapes_beyond_its_descriptor_ranges():
     assert ei.value.code == fg.ERR_BAD_SHAPE
     # the same widths with a short chunk are fine
     assert fg.backward_workspace_size(1, 1024, 64, 1024, 128, 256, True, fg.BF16) > 0
+
+
+def _tcall(**over):
+    B, n, d, e, s, c = (SHAPE[k] for k in ("B", "n", "d", "e", "s", "chunk"))
+    ws = fg.backward_workspace_size(B, n, d, e, s, c, True, fg.BF16)
+    base = 1 << 40
+    names = ("X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "O", "workspace")
+    ptrs = {k: base + (i << 30) for i, k in enumerate(names)}
+    ptrs["workspace_bytes"] = ws
+    ptrs["rope_base"] = 0.0
+    ptrs.update(over)
+    return fg.forward_train_raw(*(ptrs[k] for k in names[:7]), c, 1, ptrs["rope_base"], B, n, d, e, s,
+                                fg.BF16, ptrs["O"], ptrs["workspace"], ptrs["workspace_bytes"], None)
+
+
+@pytest.mark.parametrize("which", ["X", "W_u", "W_v", "W_z", "gamma", "beta", "W_o", "O", "workspace"])
+def test_forward_train_null_pointer_rejected(which):
+    assert _tcall(**{which: None}) == fg.ERR_NULL_PTR
+
+
+def test_forward_train_needs_the_backward_workspace():
+    fwd = fg.workspace_size(1, 128, 64, 128, 128, 64, True, fg.BF16)
+    assert _tcall(workspace_bytes=fwd) == fg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(O=(1 << 40) + 4), fg.ERR_MISALIGNED),
+    (dict(O=1 << 40), fg.ERR_ALIASING),                       # O is X
+    (dict(workspace=(1 << 40) + (6 << 30)), fg.ERR_ALIASING),  # workspace is W_o
+    (dict(rope_base=-1.0), fg.ERR_BAD_SHAPE),
+])
+def test_forward_train_validation(over, code):
+    assert _tcall(**over) == code
+
+
+def test_backward_saved_validates_like_the_backward():
+    B, n, d, e, s, c = (SHAPE[k] for k in ("B", "n", "d", "e", "s", "chunk"))
+    ws = fg.backward_workspace_size(B, n, d, e, s, c, True, fg.BF16)
+    base = 1 << 40
+    ptrs = [base + (i << 30) for i in range(16)]
+    args = lambda p, wsb: (*p[:8], c, 1, 0.0, B, n, d, e, s, fg.BF16, *p[8:15], p[15], wsb, None)
+    assert fg.backward_saved_raw(*args(ptrs, 1024)) == fg.ERR_WORKSPACE
+    bad = list(ptrs)
+    bad[7] = None  # dO
+    assert fg.backward_saved_raw(*args(bad, ws)) == fg.ERR_NULL_PTR
+    bad = list(ptrs)
+    bad[8] = ptrs[0]  # dX is X
+    assert fg.backward_saved_raw(*args(bad, ws)) == fg.ERR_ALIASING

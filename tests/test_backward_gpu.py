@@ -170,3 +170,41 @@ def test_forward_and_backward_replayed_from_a_hip_graph_match_eager():
         assert torch.equal(O, O_eager), rep
         for k in fg.GRAD_NAMES:
             assert torch.equal(grads[k], g_eager[k]), (rep, k)
+
+
+# name: (B, n, d, e, s, chunk, causal, dtype, rope_base)
+TRAIN_CASES = {
+    "causal_bf16": (2, 512, 128, 256, 128, 256, True, "bf16", None),
+    "noncausal_ragged_bf16": (3, 216, 200, 136, 24, 72, False, "bf16", None),
+    "rope_causal_f32": (1, 256, 64, 128, 32, 64, True, "f32", 100.0),
+    "single_chunk_causal_f32": (2, 128, 32, 64, 24, 128, True, "f32", None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TRAIN_CASES))
+def test_train_forward_then_saved_backward(name):
+    # flash_gau_forward_train gives the forward's output (to the parity bar against the oracle) and
+    # leaves the intermediates; flash_gau_backward_saved on them returns exactly what
+    # flash_gau_backward (which recomputes them) returns.
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype, base = TRAIN_CASES[name]
+    print(f"[gpu case] train forward + saved backward {name}", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=6, gamma_std=0.3, beta_std=0.1)
+    dO = _dev(gen.make_output_grad(B, n, d, dtype, seed=6), dtype)
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+    ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8,
+                     device="cuda")
+    ws.fill_(255)
+    O = fg.flash_gau_forward_train(*args, c, causal, ws, rope_base=base or 0.0)
+    saved = fg.flash_gau_backward(*args, dO, c, causal, rope_base=base or 0.0, workspace=ws, saved=True)
+    full = fg.flash_gau_backward(*args, dO, c, causal, rope_base=base or 0.0)
+    torch.cuda.synchronize()
+    ref = oracle.flash_forward(inp.X, inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o, c, causal,
+                               rope_base=base)
+    err = _rel(O.float().cpu().numpy(), ref)
+    print(f"  O max rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    for k in fg.GRAD_NAMES:
+        assert torch.equal(saved[k], full[k]), k
