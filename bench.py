@@ -175,7 +175,7 @@ def cpu_baseline(inp, seconds):
     return rec, ref
 
 
-def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10):
+def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10, with_saved=True):
     """Times flash_gau_backward on the whole batch (dO drawn by inputs.make_output_grad) and the
     fp64 oracle's backward on sequence 0; checks the GPU gradients of a call whose dO is zero on
     every other sequence against that oracle run. Algorithmic work: every contraction of the
@@ -208,28 +208,30 @@ def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     flops = 2.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
     # a training step without the backward's recompute: forward_train, then backward_saved
-    O = torch.empty_like(args[0])
-    for _ in range(2):
-        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
-        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
-    torch.cuda.synchronize(dev)
-    t_f = t_b = 0.0
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    for _ in range(steps):
-        e0.record()
-        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
-        e1.record()
-        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
-        e2.record()
+    training = None
+    if with_saved:
+        O = torch.empty_like(args[0])
+        for _ in range(2):
+            fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+            fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
         torch.cuda.synchronize(dev)
-        t_f += e0.elapsed_time(e1)
-        t_b += e1.elapsed_time(e2)
-    t_f, t_b = t_f / steps, t_b / steps
-    training = {"forward_train_ms": round(t_f, 4), "backward_saved_ms": round(t_b, 4),
-                "train_step_tokens_per_s": round(B * n / ((t_f + t_b) * 1e-3), 1),
-                "frac_bf16_peak": round(3.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
-                                        / ((t_f + t_b) * 1e-3) / 1e12 / PEAK["bf16"], 4)
-                if dtype == "bf16" else None}
+        t_f = t_b = 0.0
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for _ in range(steps):
+            e0.record()
+            fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+            e1.record()
+            fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
+            e2.record()
+            torch.cuda.synchronize(dev)
+            t_f += e0.elapsed_time(e1)
+            t_b += e1.elapsed_time(e2)
+        t_f, t_b = t_f / steps, t_b / steps
+        step_flops = 3.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
+        training = {"forward_train_ms": round(t_f, 4), "backward_saved_ms": round(t_b, 4),
+                    "train_step_tokens_per_s": round(B * n / ((t_f + t_b) * 1e-3), 1),
+                    "frac_bf16_peak": round(step_flops / ((t_f + t_b) * 1e-3) / 1e12 / PEAK["bf16"], 4)
+                    if dtype == "bf16" else None}
     rec = {"workload": f"backward of the same layer and batch", "steps": steps,
            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
            "alg_gflop": round(flops / 1e9, 2),
@@ -425,7 +427,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement")
     ap.add_argument("--backward-only", action="store_true",
-                    help="only the backward-pass measurement (no CPU baseline), one JSON line")
+                    help="only flash_gau_backward's timing (no CPU baseline, no training pair), "
+                         "one JSON line")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rotary-embedding and FLASH-Quad (chunk = n) timings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -466,7 +469,7 @@ def main():
 
     if args.backward_only:
         print(json.dumps({"workload": name, "backward": backward_measure(
-            inp, dtype, torch, fg, dev, 0.0, steps=args.steps)}), flush=True)
+            inp, dtype, torch, fg, dev, 0.0, steps=args.steps, with_saved=False)}), flush=True)
         return
     if args.decode_only:
         if not causal:
