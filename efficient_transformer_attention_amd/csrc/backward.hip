@@ -14,11 +14,11 @@
 //              (masked); dQ_lin = dV̂ (S_g/n)ᵀ; and, in the same launch, the state gradients
 //              dS_g = Q_lin,gᵀ dV̂_g / n summed over the LATER chunks (the forward's states and
 //              carry kernels walking the chunks last to first)
-//   dheads     dQ_quad = dA K_quad, dK_quad = dAᵀ Q_quad, dK_lin = V dTᵀ
-//   dv         dVᵀ = [dV̂ᵀ | dTᵀ][Pᵀ | K_lin]ᵀ per chunk, times SiLU'(H_v)
+//   dheads_dv  one launch: dQ_quad = dA K_quad, dK_quad = dAᵀ Q_quad, dK_lin = V dTᵀ, and
+//              dVᵀ = [dV̂ᵀ | dTᵀ][Pᵀ | K_lin]ᵀ per chunk, times SiLU'(H_v)
 //   dz         the rotary transpose, dZ = Σ γ_h dhead_h, dH_z, and partial sums for dγ, dβ
-//   dx         dX = dH_u W_uᵀ + dH_v W_vᵀ + dH_z W_zᵀ (the input weights as stored)
-//   wgrad      dW = Xᵀ dH and dW_o = Yᵀ dO, split over token ranges into fp32 partials
+//   dx_wgrad   one launch: dX = dH_u W_uᵀ + dH_v W_vᵀ + dH_z W_zᵀ (the input weights as stored),
+//              and dW = Xᵀ dH, dW_o = Yᵀ dO split over token ranges into fp32 partials
 //   reduce     partial sums → dW_u, dW_v, dW_z, dW_o, dγ, dβ
 //
 // Every GEMM is the forward's TileGemm. A contraction over tokens (a chunk's, or all of them)
@@ -337,19 +337,14 @@ struct DHeadsArgs {
   int nbg, G, c, s, e, causal;
 };
 
-// Per (chunk, token tile, feature tile), three roles:
+// Per (chunk, token tile, feature tile), one of three roles:
 //   0: dQ_quad = dA K_quad over the keys (up to the tile's diagonal when causal); K_quad MN-major;
 //   1: dK_quad = dAᵀ Q_quad over the queries (from the tile's diagonal); dA and Q_quad MN-major;
 //   2: dK_lin = V dTᵀ over e; V from V_gᵀ and dT/n from its [e, s] layout, both MN-major.
 template <class E>
-__global__ __launch_bounds__(BGemm<E>::kThreads) void dheads_kernel(DHeadsArgs<E> p, int roles) {
+__device__ __forceinline__ void dheads_block(const DHeadsArgs<E>& p, u32x4* lds, int role, int lid) {
   constexpr int BT = BShapes<E>::BT;
-  __shared__ u32x4 lds[BGemm<E>::kLds];
   const int ntc = (p.c + BT - 1) / BT, nts = (p.s + BT - 1) / BT;
-  const int per_role = p.nbg * ntc * nts;
-  const int role = blockIdx.x / per_role;
-  if (role >= roles) return;
-  const int lid = xcd_remap(blockIdx.x - role * per_role, per_role);
   const int bg = lid / (ntc * nts);
   const int rem = lid % (ntc * nts);
   const int r0 = (rem / nts) * BT, f0 = (rem % nts) * BT;  // token tile of the chunk, feature tile
@@ -393,14 +388,12 @@ struct DVArgs {
 // tile's diagonal on; dV̂ and P MN-major), then + dTᵀ K_linᵀ over s (K_lin MN-major from its
 // chunk-transposed copy), times SiLU'(H_v).
 template <class E>
-__global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
+__device__ __forceinline__ void dv_block(const DVArgs<E>& p, u32x4* lds, int lid) {
   using G0 = BGemm<E, MN, MN>;
   using G1 = BGemm<E, KK, MN>;
   using T = typename E::T;
   constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
-  __shared__ u32x4 lds[G0::kLds];
   const int nte = (p.e + BT - 1) / BT, ntc = (p.c + BT - 1) / BT;
-  const int lid = xcd_remap(blockIdx.x, p.nbg * nte * ntc);
   const int bg = lid / (nte * ntc);
   const int rem = lid % (nte * ntc);
   const int nt = rem / nte, mt = rem % nte;
@@ -466,6 +459,29 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void dv_kernel(DVArgs<E> p) {
         const int j = m0 + r, key = n0 + cl;
         if (j < p.e && key < p.c) *reinterpret_cast<u32x4*>(p.dHvr + (tok0 + key) * p.e + j) = chunk;
       });
+}
+
+// One launch for the head and value gradients, which read only the score and state gradients:
+// the long dK_lin tiles (K = e) first, then the value tiles, then the short dQ_quad and dK_quad
+// tiles, so the short work fills in behind the long.
+template <class E>
+__global__ __launch_bounds__(BGemm<E>::kThreads) void dheads_dv_kernel(DHeadsArgs<E> h, DVArgs<E> v,
+                                                                       int n_lin, int n_dv,
+                                                                       int per_role) {
+  __shared__ u32x4 lds[BGemm<E>::kLds];
+  int bid = blockIdx.x;
+  if (bid < n_lin) {
+    dheads_block<E>(h, lds, 2, xcd_remap(bid, n_lin));
+    return;
+  }
+  bid -= n_lin;
+  if (bid < n_dv) {
+    dv_block<E>(v, lds, xcd_remap(bid, n_dv));
+    return;
+  }
+  bid -= n_dv;
+  const int role = bid / per_role;
+  if (role < 2) dheads_block<E>(h, lds, role, xcd_remap(bid - role * per_role, per_role));
 }
 
 // ------------------------------------------------------------------------------ dz
@@ -588,13 +604,11 @@ struct DXArgs {
 
 // dXᵀ tiles (input features x tokens) over the three K ranges e | e | s.
 template <class E>
-__global__ __launch_bounds__(BGemm<E>::kThreads) void dx_kernel(DXArgs<E> p) {
+__device__ __forceinline__ void dx_block(const DXArgs<E>& p, u32x4* lds, int lid) {
   using G = BGemm<E>;
   using T = typename E::T;
   constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
-  __shared__ u32x4 lds[G::kLds];
-  const int ntd = (p.d + BT - 1) / BT, ntt = (p.M + BT - 1) / BT;
-  const int lid = xcd_remap(blockIdx.x, ntd * ntt);
+  const int ntd = (p.d + BT - 1) / BT;
   const int nt = lid / ntd, mt = lid % ntd;
   const int m0 = mt * BT, n0 = nt * BT;  // m: input feature, n: token
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -654,11 +668,9 @@ struct WArgs {
 };
 
 template <class E>
-__global__ __launch_bounds__(BGemm<E>::kThreads) void wgrad_kernel(WArgs<E> p, int total) {
+__device__ __forceinline__ void wgrad_block(const WArgs<E>& p, u32x4* lds, int lid) {
   using G = BGemm<E, MN, MN>;
   constexpr int BT = BShapes<E>::BT;
-  __shared__ u32x4 lds[G::kLds];
-  const int lid = xcd_remap(blockIdx.x, total);
   WJob<E> J = p.job[0];
 #pragma unroll
   for (int i = 1; i < 4; ++i)
@@ -675,6 +687,19 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void wgrad_kernel(WArgs<E> p, i
   const Src b = make_src_mn(J.B, tbeg, J.Fb, E::kSize, ntok, n0, J.Fb - n0);
   gemm_to_f32<G>(lds, a, 0, b, 0, ksteps<E>(ntok), J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0,
                  J.Fb, J.Fa - m0, J.Fb - n0);
+}
+
+// One launch for the input and weight gradients, which read the same finished inputs: the
+// weight-gradient tiles first, then the dX tiles.
+template <class E>
+__global__ __launch_bounds__(BGemm<E>::kThreads) void dx_wgrad_kernel(DXArgs<E> x, WArgs<E> w,
+                                                                      int n_w, int n_dx) {
+  __shared__ u32x4 lds[BGemm<E>::kLds];
+  const int bid = blockIdx.x;
+  if (bid < n_w)
+    wgrad_block<E>(w, lds, xcd_remap(bid, n_w));
+  else
+    dx_block<E>(x, lds, xcd_remap(bid - n_w, n_dx));
 }
 
 // ------------------------------------------------------------------------------ reduce
@@ -821,11 +846,10 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
   // grid sizes, and the byte ranges the MN-major operands address (32-bit buffer descriptors)
   const int64_t ntc = cdiv(chunk, bt), nts = cdiv(s, bt), nte = cdiv(e, bt);
   const int64_t grids[] = {
-      nbg * nte * ntc,                                                        // mixb, dv
+      nbg * nte * ntc,                                                        // mixb
       nbg * ntc * ntc + nbg * ntc * nts + B * f.ng * cdiv(s, bt) * cdiv(e, bt),  // dscores_states
-      3 * nbg * ntc * nts,                                                    // dheads
-      cdiv(d, bt) * cdiv(M, bt),                                              // dx
-      bp->splits * tiles_per_split,                                           // wgrad
+      3 * nbg * ntc * nts + nbg * nte * ntc,                                  // dheads + dv
+      cdiv(d, bt) * cdiv(M, bt) + bp->splits * tiles_per_split,               // dx + wgrad
       cdiv(wtot / 4, 256),                                                    // reduce
       bp->nzb * cdiv(s / 2, 256),                                             // dz
   };
@@ -972,21 +996,17 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     hipLaunchKernelGGL(carry_kernel<E>, dim3(unsigned(cdiv(pl.B * e * s / 8, 256))), dim3(256), 0,
                        stream, a);
   }
-  // ---- head gradients
+  // ---- head and value gradients
   {
-    DHeadsArgs<E> a{R(BR_DAR), Kq, Qq, Vt, R(BR_DTT), Rf(BR_DQQ), Rf(BR_DKQ), Rf(BR_DKL), nbg, G, c,
+    DHeadsArgs<E> h{R(BR_DAR), Kq, Qq, Vt, R(BR_DTT), Rf(BR_DQQ), Rf(BR_DKQ), Rf(BR_DKL), nbg, G, c,
                     s, e, causal};
-    const int roles = lin ? 3 : 2;
-    const int64_t per_role = pl.nbg * cdiv(c, bt) * cdiv(s, bt);
-    hipLaunchKernelGGL(dheads_kernel<E>, dim3(unsigned(roles * per_role)), dim3(kThreads), 0, stream,
-                       a, roles);
-  }
-  // ---- value gradients
-  {
-    DVArgs<E> a{R(BR_DVHR), P, R(BR_DTT), Klt, R(BR_HR), R(BR_DHVR), nbg, G, c, s, e, causal,
+    DVArgs<E> v{R(BR_DVHR), P, R(BR_DTT), Klt, R(BR_HR), R(BR_DHVR), nbg, G, c, s, e, causal,
                 int(lin)};
-    const int64_t nb = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
-    hipLaunchKernelGGL(dv_kernel<E>, dim3(unsigned(nb)), dim3(kThreads), 0, stream, a);
+    const int64_t per_role = pl.nbg * cdiv(c, bt) * cdiv(s, bt);
+    const int64_t n_lin = lin ? per_role : 0;
+    const int64_t n_dv = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
+    hipLaunchKernelGGL(dheads_dv_kernel<E>, dim3(unsigned(n_lin + n_dv + 2 * per_role)),
+                       dim3(kThreads), 0, stream, h, v, int(n_lin), int(n_dv), int(per_role));
   }
   // ---- rotary transpose, dZ, dH_z, dγ/dβ partials
   {
@@ -995,15 +1015,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     hipLaunchKernelGGL(dz_kernel<E>, dim3(unsigned(bp.nzb), unsigned(cdiv(s / 2, 256))), dim3(256), 0,
                        stream, a);
   }
-  // ---- input gradient
-  {
-    DXArgs<E> a{reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
-                reinterpret_cast<const T*>(W_z), R(BR_DHUR), R(BR_DHVR), R(BR_DHZR),
-                reinterpret_cast<T*>(dX), M, d, e, s};
-    const int64_t nb = cdiv(d, bt) * cdiv(M, bt);
-    hipLaunchKernelGGL(dx_kernel<E>, dim3(unsigned(nb)), dim3(kThreads), 0, stream, a);
-  }
-  // ---- weight gradients
+  // ---- input and weight gradients
   float* wpart = Rf(BR_WPART);
   float* part[4];
   {
@@ -1027,7 +1039,12 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     a.M = M;
     a.tps = int(bp.tps);
     a.splits = int(bp.splits);
-    hipLaunchKernelGGL(wgrad_kernel<E>, dim3(unsigned(total)), dim3(kThreads), 0, stream, a, total);
+    DXArgs<E> x{reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
+                reinterpret_cast<const T*>(W_z), R(BR_DHUR), R(BR_DHVR), R(BR_DHZR),
+                reinterpret_cast<T*>(dX), M, d, e, s};
+    const int64_t n_dx = cdiv(d, bt) * cdiv(M, bt);
+    hipLaunchKernelGGL(dx_wgrad_kernel<E>, dim3(unsigned(total + n_dx)), dim3(kThreads), 0, stream,
+                       x, a, total, int(n_dx));
   }
   // ---- reductions
   {
