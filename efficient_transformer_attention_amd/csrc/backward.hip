@@ -165,15 +165,14 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
           wave, wm, wn, lane);
   }
 
-  // H_u of the lane's four value columns r.. of token column cl (tile-local), zeros off the edge
-  auto load_hu = [&](int r, int cl, float* hu) {
-    const int j = m0 + r, i = n0 + cl;
-    if (j < p.e && i < p.c) {
-      load4f(p.Hu + (tok0 + i) * p.e + j, hu);
-    } else {
-      hu[0] = hu[1] = hu[2] = hu[3] = 0.0f;
-    }
-  };
+  // H_u of the tile (token rows, value columns) goes once into the LDS half that the output
+  // staging leaves free; each of the three passes reads its four values from there.
+  static_assert(2 * BT * BT * E::kSize <= G::kLds * 16, "H_u tile and staging exceed the LDS");
+  char* const hub = reinterpret_cast<char*>(lds) + BT * BT * E::kSize;
+  lds_tile_load<T, BT, BT, G::kThreads>(hub, p.Hu + (tok0 + n0) * p.e + m0, p.e, p.c - n0,
+                                        p.e - m0);
+  __syncthreads();
+  auto load_hu = [&](int r, int cl, float* hu) { lds_tile_read4f<T, BT>(hub, cl, r, hu); };
   // what: 0 Y = U ⊙ V̂, 1 dV̂ = dY ⊙ U, 2 dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u); all token-major
   T* const dst[3] = {p.Yr, p.dVhr, p.dHur};
 #pragma unroll
@@ -433,21 +432,23 @@ __device__ __forceinline__ void dv_block(const DVArgs<E>& p, u32x4* lds, int lid
           },
           NoPre(), wave, wm, wn, lane);
   }
-  // dH_v = dV ⊙ SiLU'(H_v), in place
+  // dH_v = dV ⊙ SiLU'(H_v), in place; the H_v tile (key rows, value columns) comes through the
+  // LDS half that the output staging leaves free
+  static_assert(2 * BT * BT * E::kSize <= G0::kLds * 16, "H_v tile and staging exceed the LDS");
+  char* const hub = reinterpret_cast<char*>(lds) + BT * BT * E::kSize;
   const int ncols = p.e + p.s;
+  lds_tile_load<T, BT, BT, G0::kThreads>(hub, p.Hr + (tok0 + n0) * ncols + m0, ncols, p.c - n0,
+                                         p.e - m0);
+  __syncthreads();
   const int lr = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int i = 0; i < G1::TM; ++i)
 #pragma unroll
     for (int j = 0; j < G1::TN; ++j) {
-      const int col = m0 + wm * G1::WTM + i * 16 + q * 4;  // first of four value columns
-      const int key = n0 + wn * G1::WTN + j * 16 + lr;
-      if (col < p.e && key < p.c) {
-        float h[4];
-        load4f(p.Hr + (tok0 + key) * ncols + col, h);
+      float h[4];  // value columns r.. of key cl (tile-local)
+      lds_tile_read4f<T, BT>(hub, wn * G1::WTN + j * 16 + lr, wm * G1::WTM + i * 16 + q * 4, h);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) g.acc[i][j][k] *= silu_grad(h[k]);
-      }
+      for (int k = 0; k < 4; ++k) g.acc[i][j][k] *= silu_grad(h[k]);
     }
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,

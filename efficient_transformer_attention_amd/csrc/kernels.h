@@ -320,6 +320,38 @@ struct TileGemm {
   }
 };
 
+// An epilogue's elementwise operand tile in LDS: ROWS x COLS elements of a row-major tensor (row
+// pitch ld; rows past nrows and columns past ncols read as zeros) copied by THREADS threads with
+// 16-byte loads that cover whole rows, each row's chunks XOR-swizzled by the row so that the 16
+// rows a fragment read touches fall in distinct banks. Callers synchronise before reading it back
+// with lds_tile_read4f.
+template <class T, int ROWS, int COLS, int THREADS>
+__device__ __forceinline__ void lds_tile_load(char* dst, const T* src, int64_t ld, int nrows,
+                                              int ncols) {
+  constexpr int kCpr = COLS * int(sizeof(T)) / 16;  // 16-byte chunks per row
+  static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "a tile row must be 2^k chunks");
+  static_assert(ROWS * kCpr % THREADS == 0, "the chunks must spread evenly over the threads");
+#pragma unroll
+  for (int k = 0; k < ROWS * kCpr / THREADS; ++k) {
+    const int idx = int(threadIdx.x) + k * THREADS;
+    const int row = idx / kCpr, ch = idx % kCpr;
+    const int col = ch * (16 / int(sizeof(T)));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < nrows && col < ncols) v = *reinterpret_cast<const u32x4*>(src + int64_t(row) * ld + col);
+    *reinterpret_cast<u32x4*>(dst + row * (kCpr * 16) + ((ch ^ (row & (kCpr - 1))) << 4)) = v;
+  }
+}
+
+// Elements col..col+3 of row `row` of a tile stored by lds_tile_load, as floats (col % 4 == 0).
+template <class T, int COLS>
+__device__ __forceinline__ void lds_tile_read4f(const char* src, int row, int col, float* o) {
+  constexpr int kCpr = COLS * int(sizeof(T)) / 16;
+  const int byte = col * int(sizeof(T));
+  load4f(reinterpret_cast<const T*>(src + row * (kCpr * 16) +
+                                    (((byte >> 4) ^ (row & (kCpr - 1))) << 4) + (byte & 15)),
+         o);
+}
+
 // An MN-major operand of a TileGemm: K rows [row0, row0 + k_rows) of a row-major tensor with
 // row pitch ld_elems, columns [m0, m0 + m_valid) valid (a tile reads 256 bytes of each row from
 // column m0; columns past m_valid and rows past k_rows read as zeros). m_valid·esz must be a
@@ -979,19 +1011,22 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
         wave, wm, wn, lane);
 
   // Y = SiLU(X W_u) ⊙ (P V + Q_lin S / n), formed in fp32 from both accumulators, rounded once,
-  // and staged through LDS so that every token row of Y is written as full 16-byte runs.
+  // and staged through LDS so that every token row of Y is written as full 16-byte runs. A stored
+  // H_u tile first goes whole into the LDS half the staging leaves free.
   using T = typename E::T;
+  char* const hub = reinterpret_cast<char*>(lds) + BM * BN * E::kSize;
+  if constexpr (HU) {
+    static_assert(2 * BM * BN * E::kSize <= G::kLds * 16, "H_u tile and staging exceed the LDS");
+    lds_tile_load<T, BN, BM, G::kThreads>(hub, p.Hu + (tok0 + n0) * p.e + m0, p.e, p.c - n0,
+                                          p.e - m0);
+    __syncthreads();
+  }
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
       [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
         float hu[4];
         if constexpr (HU) {
-          const int j = m0 + r, i = n0 + cl;
-          if (j < p.e && i < p.c) {
-            load4f(p.Hu + (tok0 + i) * p.e + j, hu);
-          } else {
-            hu[0] = hu[1] = hu[2] = hu[3] = 0.0f;
-          }
+          lds_tile_read4f<T, BM>(hub, cl, r, hu);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) hu[k] = gu.acc[fi][fj][k];
