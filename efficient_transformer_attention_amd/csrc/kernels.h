@@ -876,29 +876,37 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-// One thread per 8 consecutive state elements of one sequence, walking the chunk groups in order.
+// The carry walk of 8 consecutive elements (offset j inside one [e, s] state) of sequence b, over
+// the chunk groups in order. Chunk and group totals are loaded kCarryBatch at a time ahead of
+// their sums, so that the loads' latencies overlap; the sums keep the walking order.
+constexpr int kCarryBatch = 8;
+
 template <class E>
-__global__ __launch_bounds__(256) void carry_kernel(CarryArgs<E> p) {
-  const int64_t per_seq = p.es / 8;
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= p.B * per_seq) return;
-  const int b = int(idx / per_seq);
-  const int64_t j = (idx % per_seq) * 8;
+__device__ __forceinline__ void carry_vec(const CarryArgs<E>& p, int b, int64_t j) {
   float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float v[8];
+  const typename E::T* tot = p.Carry + int64_t(b) * p.ng * p.es + j;
   auto chunk_at = [&](int g) -> int64_t { return int64_t(b) * p.G + (p.rev ? p.G - 1 - g : g); };
   if (p.causal && p.gs == 1) {
-    // one chunk per group: the states stage left only the chunk totals; write the exclusive
-    // prefix of every chunk directly
-    for (int g = 0; g < p.G; ++g) {
-      store8(p.St + chunk_at(g) * p.es + j, run);
-      if (g < p.G - 1) {
-        load8(p.Carry + (int64_t(b) * p.ng + g) * p.es + j, v);
+    // one chunk per group: the states stage left only the chunk totals (of chunks 0..G-2); write
+    // the exclusive prefix of every chunk directly
+    for (int g0 = 0; g0 < p.G; g0 += kCarryBatch) {
+      float v[kCarryBatch][8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) run[q] += v[q];
+      for (int q = 0; q < kCarryBatch; ++q)
+        if (g0 + q < p.G - 1) load8(tot + int64_t(g0 + q) * p.es, v[q]);
+#pragma unroll
+      for (int q = 0; q < kCarryBatch; ++q) {
+        if (g0 + q >= p.G) break;
+        store8(p.St + chunk_at(g0 + q) * p.es + j, run);
+        if (g0 + q < p.G - 1) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) run[k] += v[q][k];
+        }
       }
     }
   } else if (p.causal) {
+    // the states stage left each chunk's prefix inside its group; add the earlier groups' totals
+    float v[8];
     for (int k = 0; k < p.ng; ++k) {
       if (k > 0) {
         const int g1 = min(p.G, (k + 1) * p.gs);
@@ -911,19 +919,35 @@ __global__ __launch_bounds__(256) void carry_kernel(CarryArgs<E> p) {
         }
       }
       if (k < p.ng - 1) {
-        load8(p.Carry + (int64_t(b) * p.ng + k) * p.es + j, v);
+        load8(tot + int64_t(k) * p.es, v);
 #pragma unroll
         for (int q = 0; q < 8; ++q) run[q] += v[q];
       }
     }
   } else {
-    for (int k = 0; k < p.ng; ++k) {
-      load8(p.Carry + (int64_t(b) * p.ng + k) * p.es + j, v);
+    for (int k0 = 0; k0 < p.ng; k0 += kCarryBatch) {
+      float v[kCarryBatch][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) run[q] += v[q];
+      for (int q = 0; q < kCarryBatch; ++q)
+        if (k0 + q < p.ng) load8(tot + int64_t(k0 + q) * p.es, v[q]);
+#pragma unroll
+      for (int q = 0; q < kCarryBatch; ++q) {
+        if (k0 + q >= p.ng) break;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) run[k] += v[q][k];
+      }
     }
     store8(p.St + int64_t(b) * p.es + j, run);
   }
+}
+
+// One thread per 8 consecutive state elements of one sequence.
+template <class E>
+__global__ __launch_bounds__(256) void carry_kernel(CarryArgs<E> p) {
+  const int64_t per_seq = p.es / 8;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= p.B * per_seq) return;
+  carry_vec(p, int(idx / per_seq), (idx % per_seq) * 8);
 }
 
 // ------------------------------------------------------------------------------ mix
