@@ -50,6 +50,23 @@ def _expected_layout(B, n, d, e, s, c, causal, esz, ng):
     return offs, off
 
 
+@pytest.mark.parametrize("args,ng,gs", [
+    ((8, 256, 64, 1536, 16, 8, True, fg.BF16), 16, 2),       # two chunks per group
+    ((8, 256, 64, 1536, 16, 8, False, fg.BF16), 16, 2),
+    ((128, 64, 32, 2048, 128, 16, True, fg.BF16), 1, 4),     # one group per sequence
+    ((128, 64, 32, 2048, 128, 16, False, fg.BF16), 1, 4),
+    ((8, 4096, 768, 1536, 128, 256, True, fg.BF16), 16, 1),  # one chunk per group
+])
+def test_state_groups_cover_every_carry_branch(args, ng, gs):
+    """The GPU parity cases with these shapes reach each branch of the carry walk: the chunk
+    grouping is ceil(2048 / (B * state tiles)) groups, at most one per chunk."""
+    B, n, d, e, s, c, causal, dt = args
+    G = n // c
+    got = fg.state_groups(*args)
+    assert got == ng
+    assert -(-G // got) == gs
+
+
 @pytest.mark.parametrize("name,args", [
     ("c1", (1, 512, 256, 512, 128, 128, False, fg.F32)),
     ("c3", (8, 4096, 768, 1536, 128, 256, True, fg.BF16)),

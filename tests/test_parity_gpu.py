@@ -81,6 +81,13 @@ SMALL = {
     "tiny_noncausal_fp32": (1, 16, 8, 16, 8, 8, False, "f32"),
     "many_chunks_causal_bf16": (2, 1024, 64, 128, 128, 8, True, "bf16"),
     "wide_chunk_c512_causal_bf16": (1, 1536, 256, 512, 128, 512, True, "bf16"),
+    # the states stage's chunk grouping (flashgau_state_groups): two chunks per group, so the
+    # carry walk adds earlier groups' totals to in-group prefixes; and one group per sequence
+    # (B * state tiles >= 2048), where the states stage writes every state and no carry runs
+    "chunk_groups_causal_bf16": (8, 256, 64, 1536, 16, 8, True, "bf16"),
+    "chunk_groups_noncausal_bf16": (8, 256, 64, 1536, 16, 8, False, "bf16"),
+    "one_group_causal_bf16": (128, 64, 32, 2048, 128, 16, True, "bf16"),
+    "one_group_noncausal_bf16": (128, 64, 32, 2048, 128, 16, False, "bf16"),
 }
 
 
@@ -110,7 +117,9 @@ def test_parity_each_branch(name, branch):
 
 
 @pytest.mark.parametrize("name", ["c2_causal_bf16", "c2_noncausal_bf16", "ragged_causal_bf16",
-                                  "ragged_noncausal_fp32", "c1_noncausal_fp32"])
+                                  "ragged_noncausal_fp32", "c1_noncausal_fp32",
+                                  "chunk_groups_causal_bf16", "chunk_groups_noncausal_bf16",
+                                  "one_group_causal_bf16", "one_group_noncausal_bf16"])
 def test_stage_parity(name):
     B, n, d, e, s, c, causal, dtype = SMALL[name]
     _announce(f"{name} stages")
