@@ -416,7 +416,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None, help="name in inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
