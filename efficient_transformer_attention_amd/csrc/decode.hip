@@ -26,7 +26,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "common.h"
+#include "kernels.h"
 
 namespace {
 
@@ -174,32 +174,13 @@ struct DecAttnArgs {
   float inv_c, inv_n;
 };
 
-constexpr int kAttnCols = 128;   // value columns per workgroup
+constexpr int kAttnCols = 64;    // value columns per workgroup (e / 64 x B workgroups)
 constexpr int kAttnGroups = kAttnCols / 8;  // groups of 8 consecutive columns
-constexpr int kAttnThreads = 1024;
+constexpr int kAttnThreads = 512;
 constexpr int kAttnSlots = kAttnThreads / kAttnGroups;  // row slots (64)
 constexpr int kPreV = 2, kPreS = 2;  // cache and state rows per slot loaded before the key weights
 
-// 8 consecutive elements as fp32 (16 bytes for bf16, two 16-byte loads for fp32).
-__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[2 * k] = __uint_as_float(v[k] << 16);
-    o[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
-  }
-}
-__device__ __forceinline__ void load8(const float* p, float* o) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[k] = a[k];
-    o[4 + k] = b[k];
-  }
-}
-
-// grid (ceil(e / 128), B), 1024 threads, dynamic LDS (c + 2 s + 64·128) floats.
+// grid (ceil(e / 64), B), 512 threads, dynamic LDS (c + 2 s + 64·64) floats.
 template <class E>
 __global__ __launch_bounds__(kAttnThreads) void dec_attn_kernel(DecAttnArgs<E> p) {
   extern __shared__ float sh[];
@@ -352,51 +333,48 @@ struct DecFoldArgs {
   int B, e, s, c;
 };
 
-constexpr int kFoldRows = 32;    // state rows (K_lin dimensions) per workgroup
-constexpr int kFoldTokens = 64;  // chunk tokens staged in LDS at a time
+// S_b += K_lin,gᵀ V_g on the matrix cores: one (state rows) x (value columns) tile of one sequence
+// per workgroup, the contraction over the chunk's tokens reading the token-major cache rows as
+// MN-major operands (K rows of s or e contiguous elements); the epilogue adds the tile to the fp32
+// state in place.
+template <class E> struct FoldShape;
+template <> struct FoldShape<BF16> {
+  static constexpr int BT = 128, WM = 2, WN = 4, NS = 2;  // an MN tile row is 256 bytes
+};
+template <> struct FoldShape<F32> {
+  static constexpr int BT = 64, WM = 2, WN = 2, NS = 3;
+};
 
-// grid (ceil(e / 256), ceil(s / 32), B), 256 threads: thread = one value column, 32 state rows.
+// grid (ceil(s / BT), ceil(e / BT), B), 64 WM WN threads.
 template <class E>
-__global__ __launch_bounds__(256) void dec_fold_kernel(DecFoldArgs<E> p) {
-  __shared__ __align__(16) float kl[kFoldTokens][kFoldRows];
-  const int tid = threadIdx.x;
-  const int col = blockIdx.x * 256 + tid;
-  const int k0 = blockIdx.y * kFoldRows;
+__global__ __launch_bounds__(64 * FoldShape<E>::WM * FoldShape<E>::WN) void dec_fold_kernel(
+    DecFoldArgs<E> p) {
+  using FS = FoldShape<E>;
+  using G = TileGemm<E, FS::BT, FS::BT, FS::WM, FS::WN, FS::NS, false, 1, kLayoutMN, kLayoutMN>;
+  __shared__ u32x4 lds[G::kLds];
+  const int m0 = blockIdx.x * FS::BT;  // state row (K_lin dimension)
+  const int n0 = blockIdx.y * FS::BT;  // value column
   const int b = blockIdx.z;
-  float acc[kFoldRows];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave / FS::WN, wn = wave % FS::WN;
+  const Src a = make_src_mn(p.Klc, int64_t(b) * p.c, p.s, E::kSize, p.c, m0, p.s - m0);
+  const Src v = make_src_mn(p.Vc, int64_t(b) * p.c, p.e, E::kSize, p.c, n0, p.e - n0);
+  G g;
+  g.zero();
+  g.run(lds, (p.c + G::KS - 1) / G::KS,
+        [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
+          sa = a;
+          sb = v;
+          ka = kb = t * G::KS;
+        },
+        NoPre(), wave, wm, wn, lane);
+  float* S = p.S + int64_t(b) * p.s * p.e;
+  g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& acc) {
+    const int i = m0 + r, j = n0 + cl;  // rows i..i+3 of column j (s % 8 == 0)
+    if (i >= p.s || j >= p.e) return;
 #pragma unroll
-  for (int k = 0; k < kFoldRows; ++k) acc[k] = 0.f;
-  for (int j0 = 0; j0 < p.c; j0 += kFoldTokens) {
-    __syncthreads();  // the previous tile is consumed
-    {
-      const int jj = tid >> 2, kk = (tid & 3) * 8;  // 64 tokens x 4 groups of 8 rows
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (j0 + jj < p.c && k0 + kk < p.s) load8(p.Klc + (int64_t(b) * p.c + j0 + jj) * p.s + k0 + kk, v);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) kl[jj][kk + m] = v[m];
-    }
-    __syncthreads();
-    if (col < p.e) {
-      const int nt = min(kFoldTokens, p.c - j0);
-      const typename E::T* vb = p.Vc + (int64_t(b) * p.c + j0) * p.e + col;
-#pragma unroll 4
-      for (int jj = 0; jj < nt; ++jj) {
-        const float v = to_f32(vb[int64_t(jj) * p.e]);
-        const f32x4* row = reinterpret_cast<const f32x4*>(kl[jj]);  // broadcast reads, 16 B each
-#pragma unroll
-        for (int k4 = 0; k4 < kFoldRows / 4; ++k4) {
-          const f32x4 kv = row[k4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[4 * k4 + m] = fmaf(kv[m], v, acc[4 * k4 + m]);
-        }
-      }
-    }
-  }
-  if (col < p.e) {
-#pragma unroll
-    for (int k = 0; k < kFoldRows; ++k)
-      if (k0 + k < p.s) p.S[(int64_t(b) * p.s + k0 + k) * p.e + col] += acc[k];
-  }
+    for (int k = 0; k < 4; ++k) S[int64_t(i + k) * p.e + j] += acc[k];
+  });
 }
 
 // ------------------------------------------------------------------------------ clear
@@ -418,10 +396,10 @@ int make_decode_plan(int64_t B, int64_t d, int64_t e, int64_t s, int64_t chunk,
   if (dtype != FLASHGAU_F32 && dtype != FLASHGAU_BF16) return FLASHGAU_ERR_UNSUPPORTED;
   if (B < 0 || d < 1 || e < 1 || s < 1 || chunk < 1) return FLASHGAU_ERR_BAD_SHAPE;
   if (d % 8 || e % 8 || s % 8) return FLASHGAU_ERR_UNSUPPORTED;
-  // the attention kernel keeps the chunk's weights and both query heads in LDS next to its
-  // 32 KB of partial sums (64 KB in all)
-  static_assert(kAttnSlots * kAttnCols == 8192, "32 KB of partial sums");
-  if (chunk + 2 * s + kAttnSlots * kAttnCols > 16384) return FLASHGAU_ERR_UNSUPPORTED;
+  // the attention kernel keeps the chunk's weights and both query heads (chunk + 2 s floats, at
+  // most 32 KB) in LDS next to its partial sums (at most 32 KB)
+  static_assert(kAttnSlots * kAttnCols <= 8192, "at most 32 KB of partial sums");
+  if (chunk + 2 * s > 8192) return FLASHGAU_ERR_UNSUPPORTED;
   p->B = B, p->d = d, p->e = e, p->s = s, p->c = chunk;
   p->esz = dtype == FLASHGAU_BF16 ? 2 : 4;
   p->ncols = 2 * e + s;
@@ -488,9 +466,10 @@ int launch_decode(const DecodePlan& pl, const void* x, const char* packed, size_
   }
   if (i == c - 1) {
     DecFoldArgs<E> a{Klc, Vc, S, B, e, s, c};
+    using FS = FoldShape<E>;
     hipLaunchKernelGGL(dec_fold_kernel<E>,
-                       dim3(unsigned(cdiv(e, 256)), unsigned(cdiv(s, kFoldRows)), unsigned(B)),
-                       dim3(256), 0, stream, a);
+                       dim3(unsigned(cdiv(s, FS::BT)), unsigned(cdiv(e, FS::BT)), unsigned(B)),
+                       dim3(64 * FS::WM * FS::WN), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
 }

@@ -24,6 +24,8 @@ CASES = {
     "batch17_ktail_bf16": (17, 40, 88, 16, 4, 9, 16, "bf16", 0.3, 0.1),
     "chunk1_f32": (2, 32, 64, 8, 1, 5, 5, "f32", 0.3, 0.1),
     "wide_chunk_f32": (2, 48, 264, 40, 40, 43, 80, "f32", 0.3, 0.1),
+    # two K tiles of the matrix-core fold, the second ragged (72 = 64 + 8 tokens); two folds
+    "ragged_fold_bf16": (2, 48, 264, 40, 72, 150, 160, "bf16", 0.3, 0.1),
     "n4096_dims_bf16": (8, 768, 1536, 128, 256, 300, 4096, "bf16", 0.02, 0.0),
 }
 
