@@ -10,17 +10,19 @@
 //   o      = [u ⊙ (V̂_quad + V̂_lin)] W_o
 // and after the chunk's last token the state takes in the chunk: S += K_lin_gᵀ V_g.
 //
-// One step for B sequences (all at position t) is four small launches, none of them a GEMM of
-// any size: with one token per sequence the work is reading the weights and the state once.
+// One step for B sequences (all at position t) is three small launches, and a fourth after the
+// last token of a chunk: with one token per sequence the work is reading the weights and the
+// state once.
 //   proj   h = x (W_u | W_v | W_z) for the B tokens: each workgroup owns 16 rows of the packed
 //          (K-contiguous) weights and multiplies them with 16 token rows on the matrix cores, its
 //          8 waves splitting K, operands fetched straight from global memory into fragments;
 //          epilogue SiLU, the four heads, k_quad, k_lin and v written as row i of the chunk cache
-//   attn   per sequence and 256 value columns: the weights relu(q·k_j / c)² for j <= i, then
+//   attn   per sequence and 64 value columns: the weights relu(q·k_j / c)² for j <= i, then
 //          Σ_j w_j v_j + q_lin S / n over the rows of the chunk cache and of the state, split over
-//          32 row slots and reduced through LDS; y = u ⊙ (·)
+//          64 row slots and reduced through LDS; y = u ⊙ (·)
 //   out    o = y W_o, the same skinny matrix-core product as proj
-//   fold   (after the last token of a chunk) S += K_linᵀ V of the chunk, fp32 FMAs
+//   fold   (after the last token of a chunk) S += K_linᵀ V of the chunk: the forward's tiled
+//          matrix-core GEMM over the chunk's tokens, its epilogue adding into the fp32 state
 // and at t = 0 a fill kernel clears S first.
 
 #include <algorithm>
