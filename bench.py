@@ -198,7 +198,9 @@ def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10, with_sav
     ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8,
                      device=dev)
     out = fg.flash_gau_backward(*args, dO, c, causal, workspace=ws)
-    for _ in range(2):
+    # warm-up: dO was just drawn on the host, with the GPU idle; ~20 ms of work lets the clocks
+    # settle before the timed calls
+    for _ in range(15):
         fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
@@ -211,7 +213,7 @@ def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10, with_sav
     training = None
     if with_saved:
         O = torch.empty_like(args[0])
-        for _ in range(2):
+        for _ in range(10):
             fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
             fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
         torch.cuda.synchronize(dev)
@@ -368,9 +370,12 @@ def decode_measure(inp, dtype, torch, fg, dev, cpu_seconds):
     return rec
 
 
-def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None, steps=10, seed=0):
+def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None, steps=20,
+                 warmup=50, seed=0):
     """Average time (us) of one forward call (flash_gau_forward, or flash_gau_forward_rope when
-    rope_base is given) over `steps` calls after 3 warm-up calls, between two HIP events."""
+    rope_base is given) over `steps` calls after `warmup` calls, between two HIP events. The
+    inputs are generated on the host first, which leaves the GPU idle for seconds: a few warm-up
+    calls would time the clocks ramping back up."""
     from efficient_transformer_attention_amd import inputs as gen
     inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=seed)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -398,7 +403,7 @@ def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None
         if rc != fg.OK:
             raise fg.FlashGauError(rc, "forward")
 
-    for _ in range(3):
+    for _ in range(warmup):
         call()
     ev = HipEvents(2)
     torch.cuda.synchronize()
