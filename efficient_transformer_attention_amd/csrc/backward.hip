@@ -103,6 +103,7 @@ struct MixBArgs {
   T* dVhr;       // [M, e]
   T* dHur;       // [M, e]
   int d, nbg, G, c, e, s, causal, lin;
+  int write_y;   // 0: Y is already in the workspace (the training forward wrote the same values)
 };
 
 template <class E>
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
   T* const dst[3] = {p.Yr, p.dVhr, p.dHur};
 #pragma unroll
   for (int w = 0; w < 3; ++w) {
+    if (w == 0 && !p.write_y) continue;
     g.template stage_rows<T>(
         lds, wave, wm, wn, lane,
         [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
@@ -974,8 +976,11 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
 
   // ---- gate, output projection and V̂
   {
+    // Without the recompute, the training forward's mix stage has already written Y = U ⊙ V̂ to
+    // the forward's Y buffer, bitwise what this stage would write (the same GEMM, the same order
+    // over K, the same epilogue): the weight gradients read it there.
     MixBArgs<E> a{Vt, St, P, Ql, R(BR_HU), reinterpret_cast<const T*>(W_o), dOp, R(BR_YR),
-                  R(BR_DVHR), R(BR_DHUR), d, nbg, G, c, e, s, causal, int(lin)};
+                  R(BR_DVHR), R(BR_DHUR), d, nbg, G, c, e, s, causal, int(lin), recompute ? 1 : 0};
     const int64_t nb = pl.nbg * cdiv(e, bt) * cdiv(c, bt);
     hipLaunchKernelGGL(mixb_kernel<E>, dim3(unsigned(nb)), dim3(kThreads), 0, stream, a);
   }
@@ -1026,7 +1031,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
       o += bp.splits * bp.wcount[i];
     }
     WArgs<E> a{};
-    const T* As[4] = {Xp, Xp, Xp, R(BR_YR)};
+    const T* As[4] = {Xp, Xp, Xp, recompute ? R(BR_YR) : W(FLASHGAU_WS_Y)};
     const T* Bs[4] = {R(BR_DHUR), R(BR_DHVR), R(BR_DHZR), dOp};
     const int Fa[4] = {d, d, d, e};
     const int Fb[4] = {e, e, s, d};

@@ -295,7 +295,7 @@ int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const vo
  * flash_gau_forward_rope / flash_gau_forward do (rope_base 0: none) and also leaves in the
  * workspace (at least flashgau_backward_workspace_size() bytes) everything the backward reads of
  * the forward: the projection over W_u | W_v | W_z with its pre-activations, the heads, the scores,
- * the prefix states. Its mix stage reads the stored X W_u instead of running the gate's GEMM, so
+ * the prefix states and the gated mix Y = U ⊙ (V̂_quad + V̂_lin). Its mix stage reads the stored X W_u instead of running the gate's GEMM, so
  * O may differ from flash_gau_forward's in the last bf16 bit (same tolerance to the exact result).
  * flash_gau_backward_saved then returns the gradients flash_gau_backward would (bitwise the same),
  * reading that workspace instead of recomputing it: it must follow a flash_gau_forward_train of
