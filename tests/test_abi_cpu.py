@@ -55,6 +55,7 @@ def _expected_layout(B, n, d, e, s, c, causal, esz, ng):
     ((8, 256, 64, 1536, 16, 8, False, fg.BF16), 16, 2),
     ((128, 64, 32, 2048, 128, 16, True, fg.BF16), 1, 4),     # one group per sequence
     ((128, 64, 32, 2048, 128, 16, False, fg.BF16), 1, 4),
+    ((128, 64, 32, 2048, 128, 16, True, fg.F32), 1, 4),
     ((8, 4096, 768, 1536, 128, 256, True, fg.BF16), 16, 1),  # one chunk per group
 ])
 def test_state_groups_cover_every_carry_branch(args, ng, gs):

@@ -35,6 +35,10 @@ CASES = {
     "chunk_eq_n_noncausal_f32": (2, 128, 32, 64, 24, 128, False, "f32", None),
     "chunk_eq_n_noncausal_bf16": (2, 256, 64, 128, 32, 256, False, "bf16", None),
     "wide_s_groups_causal_bf16": (4, 512, 64, 256, 256, 32, True, "bf16", None),
+    # one chunk group per sequence (B * state tiles >= 2048): the state gradients walk all chunks
+    # of a sequence in one workgroup, and no carry runs
+    "one_group_causal_bf16": (128, 64, 32, 2048, 128, 16, True, "bf16", None),
+    "one_group_noncausal_bf16": (128, 64, 32, 2048, 128, 16, False, "bf16", None),
 }
 
 

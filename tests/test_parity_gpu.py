@@ -88,6 +88,7 @@ SMALL = {
     "chunk_groups_noncausal_bf16": (8, 256, 64, 1536, 16, 8, False, "bf16"),
     "one_group_causal_bf16": (128, 64, 32, 2048, 128, 16, True, "bf16"),
     "one_group_noncausal_bf16": (128, 64, 32, 2048, 128, 16, False, "bf16"),
+    "one_group_causal_fp32": (128, 64, 32, 2048, 128, 16, True, "f32"),
 }
 
 
