@@ -52,7 +52,8 @@ def run_gpu(inp, views=False):
     if not views:
         return out
     v = fg.workspace_views(ws, B, n, d, e, s, inp.chunk, inp.causal, dt)
-    return out, {k: t.float().cpu().numpy().astype(np.float64) for k, t in v.items()}
+    # CARRY holds only what the carry stage reads (nothing with one chunk group per sequence)
+    return out, {k: t.float().cpu().numpy().astype(np.float64) for k, t in v.items() if k != "CARRY"}
 
 
 def run_oracle(inp, batches=None, intermediates=False):
