@@ -121,7 +121,7 @@ def test_hand_constant_single_pair():
     np.testing.assert_array_equal(Vq[0, :, 0], [5.0, 5.0])
 
 
-# ------------------------------------------------------------------ brute force (the benchmark spec check 1)
+# ------------------------------------------------------------------ brute force: materialised n x n attention matrices
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("n,chunk", [(8, 1), (8, 2), (8, 4), (8, 8), (12, 1), (12, 2), (12, 4), (12, 12),
@@ -148,7 +148,7 @@ def test_local_equals_mha_with_n_over_c_heads():
     assert _rel(oracle.local_quad(Qq, Kq, V, c, True), want) <= 1e-13
 
 
-# ------------------------------------------------------------------ RNN = cumsum (the benchmark spec check 2)
+# ------------------------------------------------------------------ RNN = cumsum: the token recurrence against the chunk scan
 
 @pytest.mark.parametrize("n,chunk", [(12, 1), (12, 3), (12, 4), (16, 8), (16, 16)])
 def test_rnn_recurrence_equals_chunk_scan(n, chunk):
