@@ -6,12 +6,20 @@ e = 1536, s = 128, chunk 256, seeded synthetic inputs (X ~ N(0,1), weights ~ N(0
 gamma ~ N(1, 0.02), beta = 0). A step is one full forward call: all seven kernels (pack, proj,
 scores, states, carry, mix, out) over the whole batch, with inputs already resident in HBM.
 
-Prints one JSON line. `value` is tokens/s = B*n / (wall time of one step), timed over exactly
---steps calls between two device synchronisations. Every 10th of those calls records a HIP event
-before every kernel on the library's stream (an event between two launches idles the queue for a
-few microseconds, so the other calls run without them), which gives every kernel's average
-duration; the roofline object reports the kernel that takes the longest. The CPU baseline is the fp64 oracle timed on
-the host on one sequence of the same batch; its output also checks the GPU's on that sequence.
+Prints one JSON line. Before anything is timed, forward calls run untimed for --settle-ms (the
+host has just spent seconds generating inputs with the GPU idle, and the first calls after that
+run on clocks that are still ramping; `settle_ms` in the line records it), then --warmup untimed
+calls. `value` is tokens/s = B*n / (wall time of one step), timed over exactly --steps calls
+between two device synchronisations, with nothing else on the stream. Two separate passes follow
+outside the timed region: calls that record a HIP event before every kernel on the library's
+stream (per-kernel durations; the roofline object reports the kernel that takes the longest), and
+calls bracketed by events (`step_ms_quantiles`). The CPU baseline is the fp64 oracle timed on the
+host on one sequence of the same batch; its output also checks the GPU's on that sequence.
+
+`configs` holds one row per workload of inputs.WORKLOADS (the eight configurations, the headline
+among them): the same measurement with shorter settle and step counts, tokens/s, fraction of the
+dtype's dense matrix peak, the dominant kernel with its roofline fraction, and the max relative
+error of one sampled sequence (the batch's last) against the fp64 oracle.
 
 For a causal workload the line also carries a "decode" object: the same batch and dimensions
 decoded one token per sequence per step (flash_gau_decode_step), timed over one whole chunk of
@@ -41,7 +49,6 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens/sec per FLASH layer fwd (n=4096 causal bf16); % bf16 MFMA peak"
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core TFLOP/s of MI355X
 HBM_PEAK = 8000.0  # GB/s
-INSTRUMENT = 10    # per-kernel events on every 10th timed step
 
 
 def alg_flops(B, n, d, e, s, c, causal):
@@ -65,26 +72,63 @@ def alg_flops(B, n, d, e, s, c, causal):
             "mix": gate + pv + readout, "out": out}
 
 
+def state_branch(B, n, c, causal, ng):
+    """Which code path the cross-chunk sum takes (ng: chunk groups per sequence of the states
+    stage, as flashgau_state_groups reports): "none" (causal with one chunk: no global term),
+    "one_group" (the states stage walks every chunk of a sequence and writes the states itself,
+    no carry launch), "chunk_per_group" (causal, one chunk per group: the states stage writes chunk
+    totals, the carry stage writes every state), "groups" (causal, several chunks per group: the
+    states stage writes in-group prefixes and group totals, the carry stage adds earlier groups'
+    totals in place), "noncausal_groups" (group totals summed by the carry stage)."""
+    G = n // c
+    if causal and G == 1:
+        return "none"
+    if ng == 1:
+        return "one_group"
+    if not causal:
+        return "noncausal_groups"
+    gs = -(-G // ng)
+    return "chunk_per_group" if gs == 1 else "groups"
+
+
 def alg_bytes(B, n, d, e, s, c, causal, esz, ng):
-    """Bytes each kernel must move at least once between HBM and the chip (ng: chunk groups of
-    the states stage)."""
+    """Bytes each kernel must move at least once between HBM and the chip, for the code path the
+    problem takes (ng: chunk groups per sequence of the states stage; see state_branch). A causal
+    sequence's last chunk feeds no state, so its K_lin and V are not read by the states stage; chunk
+    0's state is zero and the mix stage does not need it."""
     N = B * n
     G = n // c
     gs = -(-G // ng)
-    nst = (B * G if causal else B) * e * s
-    if causal:
-        carry = (2 * B * (G - gs) * e * s + B * (ng - 1) * e * s) * esz if ng > 1 else 0
-        states_out = nst + B * (ng - 1) * e * s
+    es = e * s
+    branch = state_branch(B, n, c, causal, ng)
+    pc = (c * (c + 1) // 2) if causal else c * c  # P entries written by scores, read by mix, per chunk
+    if branch == "none":
+        st_in = st_out = carry = mix_lin = 0
     else:
-        carry = (B * ng * e * s + B * e * s) * esz if ng > 1 else 0
-        states_out = B * ng * e * s if ng > 1 else nst
-    pc = (c * (c + 1) // 2) if causal else c * c  # P entries the mix reads per chunk
+        if causal:
+            st_in = (N - B * c) * (e + s)       # every chunk but the last of each sequence
+            mix_lin = (N - B * c) * s + B * (G - 1) * es  # Q_lin and the states of chunks 1..G-1
+        else:
+            st_in = N * (e + s)
+            mix_lin = N * s + B * es
+        if branch == "one_group":
+            st_out = B * G * es if causal else B * es
+            carry = 0
+        elif branch == "chunk_per_group":
+            st_out = B * (G - 1) * es                  # totals of chunks 0..G-2
+            carry = B * (G - 1) * es + B * G * es      # read them, write every chunk's state
+        elif branch == "groups":
+            st_out = B * G * es + B * (ng - 1) * es    # in-group prefixes + totals of groups 0..ng-2
+            carry = B * (ng - 1) * es + 2 * B * (G - gs) * es  # totals read; later groups' states updated
+        else:  # noncausal_groups
+            st_out = B * ng * es
+            carry = B * ng * es + B * es
     return {
         "pack": 2 * ((2 * e + s) * d + e * d) * esz,
         "proj": (N * d + (e + s) * d + N * (e + 4 * s)) * esz,
-        "scores_states": (2 * N * s + B * G * pc + N * (e + s) + states_out) * esz,
-        "carry": carry,
-        "mix": (N * e + B * G * pc + N * s + nst + N * d + e * d + N * e) * esz,
+        "scores_states": (2 * N * s + B * G * pc + st_in + st_out) * esz,
+        "carry": carry * esz,
+        "mix": (N * e + B * G * pc + mix_lin + N * d + e * d + N * e) * esz,
         "out": (N * e + e * d + N * d) * esz,
     }
 
@@ -417,14 +461,152 @@ def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None
     return us
 
 
+def upload(torch, dev, inp):
+    """The workload's inputs as contiguous device tensors (X and the weights in the storage dtype,
+    gamma and beta fp32)."""
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    return [up(inp.X), up(inp.W_u), up(inp.W_v), up(inp.W_z), up(inp.gamma, torch.float32),
+            up(inp.beta, torch.float32), up(inp.W_o)]
+
+
+def measure_forward(fg, torch, dev, inp, steps, warmup, settle_ms, kernel_steps, quantile_steps):
+    """Times flash_gau_forward on one workload. Order: an untimed settle loop of forward calls for
+    settle_ms (after host-side input generation the GPU has idled for seconds and its clocks have
+    dropped), `warmup` untimed calls, then exactly `steps` calls between two device
+    synchronisations (the timed region: no events, nothing else on the stream). Then two separate
+    passes, outside the timed region: `kernel_steps` calls of flash_gau_forward_timed (a HIP event
+    before every kernel, on the library's stream) for per-kernel durations, and `quantile_steps`
+    calls each bracketed by two events for the step-time distribution. Returns the record and O."""
+    B, n, d, e, s = inp.shape
+    c, causal = inp.chunk, inp.causal
+    dt = fg.BF16 if inp.dtype == "bf16" else fg.F32
+    tens = upload(torch, dev, inp)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, n, d), dtype=tens[0].dtype, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ptrs = tuple(t.data_ptr() for t in tens)
+    nst = len(fg.STAGES)
+
+    def step():
+        rc = fg.forward_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
+                            nbytes, stream)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_forward")
+
+    # settle: fixed wall-clock duration, untimed
+    settle_calls = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(8):
+            step()
+        settle_calls += 8
+        torch.cuda.synchronize(dev)
+    settle_elapsed = (time.perf_counter() - t_settle) * 1e3
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / steps
+
+    # per-kernel durations, a pass of its own
+    events = HipEvents(kernel_steps * (nst + 1))
+    for k in range(kernel_steps):
+        evs = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+        rc = fg.forward_timed_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
+                                  nbytes, stream, evs)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_forward_timed")
+    torch.cuda.synchronize(dev)
+    stage_ms = {st: [] for st in fg.STAGES}
+    for k in range(kernel_steps):
+        h = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+        for i, st in enumerate(fg.STAGES):
+            stage_ms[st].append(events.ms(h[i], h[i + 1]))
+    events.close()
+
+    # step-time distribution, a pass of its own (events between steps only)
+    sev = HipEvents(2 * quantile_steps)
+    for k in range(quantile_steps):
+        sev.hip.hipEventRecord(ctypes.c_void_p(sev.handles[2 * k]), ctypes.c_void_p(stream))
+        step()
+        sev.hip.hipEventRecord(ctypes.c_void_p(sev.handles[2 * k + 1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize(dev)
+    per_step = sorted(sev.ms(sev.handles[2 * k], sev.handles[2 * k + 1])
+                      for k in range(quantile_steps))
+    sev.close()
+
+    def quantile(q):
+        return per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
+
+    esz = 2 if inp.dtype == "bf16" else 4
+    ng = fg.state_groups(B, n, d, e, s, c, causal, dt)
+    flops = alg_flops(B, n, d, e, s, c, causal)
+    nbytes_alg = alg_bytes(B, n, d, e, s, c, causal, esz, ng)
+    peak = PEAK[inp.dtype]
+    stage_avg = {st: statistics.mean(v) for st, v in stage_ms.items()}
+    stages = {}
+    for st in fg.STAGES:
+        t = stage_avg[st] / 1e3
+        stages[st] = {"us": round(stage_avg[st] * 1e3, 2),
+                      "tflops": round(flops[st] / t / 1e12, 2) if flops[st] and t > 0 else 0.0,
+                      "gbs": round(nbytes_alg[st] / t / 1e9, 1) if t > 0 else 0.0}
+    dom = max(fg.STAGES, key=lambda st: stage_avg[st])
+    t_dom = stage_avg[dom] / 1e3
+    if BOUND[dom] == "mfma":
+        achieved, pk, unit = flops[dom] / t_dom / 1e12, peak, "TFLOP/s"
+    else:
+        achieved, pk, unit = nbytes_alg[dom] / t_dom / 1e9, HBM_PEAK, "GB/s"
+    total_flops = sum(flops.values())
+    rec = {
+        "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(B * n / (ms_step / 1e3), 1),
+        "frac_peak": round(total_flops / (ms_step / 1e3) / 1e12 / peak, 4),
+        "peak_tflops": peak,
+        "alg_gflop": round(total_flops / 1e9, 2),
+        "settle_ms": round(settle_elapsed, 1),
+        "settle_calls": settle_calls,
+        "kernel_pass_ms": round(statistics.mean(sum(stage_ms[st][k] for st in fg.STAGES)
+                                                for k in range(kernel_steps)), 4),
+        "step_ms_quantiles": {"p10": round(quantile(0.1), 4), "p50": round(quantile(0.5), 4),
+                              "p90": round(quantile(0.9), 4)},
+        "state_branch": state_branch(B, n, c, causal, ng),
+        "stages": stages,
+        "dominant": {"kernel": dom, "bound": BOUND[dom], "achieved": round(achieved, 2), "peak": pk,
+                     "unit": unit, "frac": round(achieved / pk, 4)},
+    }
+    return rec, O
+
+
+def oracle_sequence_error(inp, O, b):
+    """max |O_gpu - O_ref| / max |O_ref| on sequence b, O_ref from the fp64 oracle."""
+    import oracle
+    ref = oracle.flash_forward(inp.X[b:b + 1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta,
+                               inp.W_o, inp.chunk, inp.causal)
+    got = O[b:b + 1].float().cpu().numpy().astype(np.float64)
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="untimed forward calls for this long before the warm-up (clocks settle)")
     ap.add_argument("--workload", default=None, help="name in inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration rows (every workload of inputs.WORKLOADS)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the causal decoding measurement")
     ap.add_argument("--decode-only", action="store_true",
@@ -463,14 +645,8 @@ def main():
     name = args.workload or gen.HEADLINE
     B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
     inp = gen.workload_inputs(name, seed=0)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    dt = fg.BF16 if dtype == "bf16" else fg.F32
-    esz = 2 if dtype == "bf16" else 4
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-
-    def up(a, t=tdt):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
 
     if args.backward_only:
         print(json.dumps({"workload": name, "backward": backward_measure(
@@ -485,96 +661,18 @@ def main():
               flush=True)
         return
 
-    X, Wu, Wv, Wz, Wo = (up(a) for a in (inp.X, inp.W_u, inp.W_v, inp.W_z, inp.W_o))
-    gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
-    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
-    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
-    O = torch.empty((B, n, d), dtype=tdt, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    ptrs = (X.data_ptr(), Wu.data_ptr(), Wv.data_ptr(), Wz.data_ptr(), gamma.data_ptr(),
-            beta.data_ptr(), Wo.data_ptr())
-    nst = len(fg.STAGES)
-    # Per-kernel HIP events are recorded on every INSTRUMENT-th timed step only: an event marker
-    # between two launches costs a few microseconds of idle queue, so recording eight per step
-    # would slow the very steps being timed.
-    instrumented = list(range(0, args.steps, INSTRUMENT))
-    events = HipEvents(len(instrumented) * (nst + 1))
-
-    def step(k=None):
-        if k is None:
-            rc = fg.forward_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
-                                nbytes, stream)
-        else:
-            evs = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
-            rc = fg.forward_timed_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(),
-                                      ws.data_ptr(), nbytes, stream, evs)
-        if rc != fg.OK:
-            raise fg.FlashGauError(rc, "flash_gau_forward")
-
-    print(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k // INSTRUMENT if k % INSTRUMENT == 0 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    print(f"[bench] {name}: settle {args.settle_ms:.0f} ms, warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    head, O = measure_forward(fg, torch, dev, inp, args.steps, args.warmup, args.settle_ms,
+                              kernel_steps=max(10, min(args.steps, 50)),
+                              quantile_steps=max(10, args.steps))
     print("[bench] timed region done", file=sys.stderr, flush=True)
-
-    ms_step = wall * 1e3 / args.steps
-    stage_ms = {st: [] for st in fg.STAGES}
-    gpu_ms = []
-    for k in range(len(instrumented)):
-        h = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
-        for i, st in enumerate(fg.STAGES):
-            stage_ms[st].append(events.ms(h[i], h[i + 1]))
-        gpu_ms.append(events.ms(h[0], h[nst]))
-    events.close()
-
-    # Step-time distribution, from a separate pass of the same number of steps, each bracketed by
-    # two events on the stream (between steps only, never between kernels); `value` does not use it.
-    sev = HipEvents(2 * args.steps)
-    for k in range(args.steps):
-        events_rec = sev.handles[2 * k:2 * k + 2]
-        sev.hip.hipEventRecord(ctypes.c_void_p(events_rec[0]), ctypes.c_void_p(stream))
-        step()
-        sev.hip.hipEventRecord(ctypes.c_void_p(events_rec[1]), ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    per_step = sorted(sev.ms(sev.handles[2 * k], sev.handles[2 * k + 1]) for k in range(args.steps))
-    sev.close()
-
-    def quantile(q):
-        return per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
-    step_q = {"p10": round(quantile(0.1), 4), "p50": round(quantile(0.5), 4),
-              "p90": round(quantile(0.9), 4)}
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "compute_units": props.multi_processor_count,
               "gcn_arch": getattr(props, "gcnArchName", None),
               "max_sclk_mhz": round(getattr(props, "clock_rate", 0) / 1000.0) or None}
-    stage_avg = {st: statistics.mean(v) for st, v in stage_ms.items()}
-
-    flops = alg_flops(B, n, d, e, s, c, causal)
-    nbytes_alg = alg_bytes(B, n, d, e, s, c, causal, esz, fg.state_groups(B, n, d, e, s, c, causal, dt))
-    total_flops = sum(flops.values())
-    tokens = B * n
-    value = tokens / (ms_step / 1e3)
-    peak = PEAK[dtype]
-    stages = {}
-    for st in fg.STAGES:
-        t = stage_avg[st] / 1e3
-        stages[st] = {"us": round(stage_avg[st] * 1e3, 2),
-                      "tflops": round(flops[st] / t / 1e12, 2) if flops[st] else 0.0,
-                      "gbs": round(nbytes_alg[st] / t / 1e9, 1)}
-    dom = max(fg.STAGES, key=lambda st: stage_avg[st])
-    t_dom = stage_avg[dom] / 1e3
-    if BOUND[dom] == "mfma":
-        achieved, pk, unit = flops[dom] / t_dom / 1e12, peak, "TFLOP/s"
-    else:
-        achieved, pk, unit = nbytes_alg[dom] / t_dom / 1e9, HBM_PEAK, "GB/s"
-    roofline = {"kernel": dom, "bound": BOUND[dom], "achieved": round(achieved, 2), "peak": pk,
-                "unit": unit, "frac": round(achieved / pk, 4),
-                "traffic": measured_traffic(dom, name)}
+    dom = head["dominant"]
+    roofline = dict(dom, traffic=measured_traffic(dom["kernel"], name))
 
     cpu = None
     max_rel_err = None
@@ -583,6 +681,37 @@ def main():
         cpu, ref = cpu_baseline(inp, args.cpu_seconds)
         got = O[:1].float().cpu().numpy().astype(np.float64)
         max_rel_err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    del O
+
+    configs = None
+    if not args.no_configs:
+        configs = []
+        for wname, shape in gen.WORKLOADS.items():
+            wB, wn, wd, we, ws_, wc, wcausal, wdtype = shape
+            row = {"workload": wname, "batch": wB, "seq_len": wn, "d": wd, "e": we, "s": ws_,
+                   "chunk": wc, "causal": wcausal, "dtype": wdtype}
+            if wname == name:
+                rec = {k: head[k] for k in ("ms_per_step", "tokens_per_s", "frac_peak", "peak_tflops",
+                                            "alg_gflop", "step_ms_quantiles", "state_branch",
+                                            "dominant")}
+                rec["max_rel_err"] = max_rel_err
+                rec["sampled_sequence"] = 0
+            else:
+                print(f"[bench] config {wname}", file=sys.stderr, flush=True)
+                winp = gen.workload_inputs(wname, seed=0)
+                full, wO = measure_forward(fg, torch, dev, winp, steps=20, warmup=10, settle_ms=300.0,
+                                           kernel_steps=10, quantile_steps=10)
+                rec = {k: full[k] for k in ("ms_per_step", "tokens_per_s", "frac_peak", "peak_tflops",
+                                            "alg_gflop", "step_ms_quantiles", "state_branch",
+                                            "dominant")}
+                sb = wB - 1
+                rec["max_rel_err"] = (oracle_sequence_error(winp, wO, sb)
+                                      if args.cpu_seconds > 0 else None)
+                rec["sampled_sequence"] = sb
+                del wO
+            row.update(rec)
+            configs.append(row)
+        torch.cuda.empty_cache()
 
     decode = None
     if causal and not args.no_decode:
@@ -592,7 +721,8 @@ def main():
     if not args.no_backward:
         print("[bench] backward pass", file=sys.stderr, flush=True)
         backward = backward_measure(inp, dtype, torch, fg, dev, min(args.cpu_seconds, 10.0))
-        backward["train_step_tokens_per_s"] = round(B * n / ((ms_step + backward["ms_per_step"]) * 1e-3), 1)
+        backward["train_step_tokens_per_s"] = round(
+            B * n / ((head["ms_per_step"] + backward["ms_per_step"]) * 1e-3), 1)
 
     rope = quad = None
     if not args.no_extras:
@@ -611,12 +741,13 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "settle_ms": head["settle_ms"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -624,16 +755,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "seq_len": n, "d": d, "e": e, "s": s,
                    "chunk": c, "causal": causal},
-        "frac_bf16_peak": round(total_flops / (ms_step / 1e3) / 1e12 / PEAK["bf16"], 4)
-        if dtype == "bf16" else None,
-        "alg_gflop": round(total_flops / 1e9, 2),
-        "gpu_ms_per_instrumented_step": round(statistics.mean(gpu_ms), 4),
-        "step_ms_quantiles": step_q,
+        "frac_bf16_peak": head["frac_peak"] if dtype == "bf16" else None,
+        "alg_gflop": head["alg_gflop"],
+        "kernel_pass_ms": head["kernel_pass_ms"],
+        "step_ms_quantiles": head["step_ms_quantiles"],
         "device": device,
         "roofline": roofline,
-        "stages": stages,
+        "stages": head["stages"],
+        "state_branch": head["state_branch"],
         "cpu_baseline": cpu,
         "max_rel_err_seq0": max_rel_err,
+        "configs": configs,
         "decode": decode,
         "backward": backward,
         "rope": rope,

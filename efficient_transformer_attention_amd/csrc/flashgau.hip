@@ -126,6 +126,13 @@ int flashgau_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t 
   return FLASHGAU_OK;
 }
 
+size_t flashgau_workspace_bytes(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                                int64_t chunk, int causal, flashgau_dtype dtype) {
+  Plan p;
+  if (make_plan(B, n, d, e, s, chunk, causal, dtype, &p) != FLASHGAU_OK) return 0;
+  return p.total;
+}
+
 int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                                int64_t chunk, int causal, flashgau_dtype dtype,
                                size_t* out_offsets) {

@@ -756,6 +756,10 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
   const int nk = (p.c * E::kSize + kStageBytes - 1) / kStageBytes;
   const int g0 = grp * p.gs;
   const int nchunks = min(p.G, g0 + p.gs) - g0;
+  // Causal: the sequence's last chunk in walking order feeds no state (its summary would only be
+  // added after the last prefix is taken), so the last group leaves its K_lin and V unread.
+  const bool last_causal = p.causal && grp == p.ng - 1;
+  const int nsum = last_causal ? nchunks - 1 : nchunks;
   const int64_t chunk0 = int64_t(b) * p.G + g0;
   // storage index of the sequence's chunk chunk0 + k (k counted in walking order)
   auto phys = [&](int64_t k) -> int64_t {
@@ -775,7 +779,8 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
 
   G g;
   g.zero();
-  g.run(lds, nchunks * nk,
+  if (nsum == 0 && !(last_causal && write_local)) return;
+  g.run(lds, nsum * nk,
         [&](int t, Src& sa, int& ka, Src& sb, int& kb) {
           const int64_t chunk = phys(t / nk);
           if constexpr (L == kLayoutK) {
@@ -795,6 +800,12 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
           if (write_local && t % nk == 0) write_state(g, p.St + phys(t / nk) * es);
         },
         wave, wm, wn, lane);
+  if (last_causal) {
+    // the prefix of the group's last chunk (inside the group) is the accumulator now; the last
+    // group's total is never read
+    if (write_local) write_state(g, p.St + phys(nchunks - 1) * es);
+    return;
+  }
   // The final tile leaves through LDS (the stages are idle now) as 16-byte runs along s.
   auto write_final = [&](typename E::T* dst) {
     using T = typename E::T;
@@ -811,7 +822,7 @@ __device__ __forceinline__ void states_block(const StatesArgs<E>& p, u32x4* lds,
   };
   if (!p.causal && p.ng == 1)
     write_final(p.St + int64_t(b) * es);
-  else if (!p.causal || grp < p.ng - 1)  // the last group's total is never read when causal
+  else
     write_final(p.Carry + (int64_t(b) * p.ng + grp) * es);
 }
 

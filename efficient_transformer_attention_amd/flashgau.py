@@ -32,7 +32,7 @@ WS_NAMES = ("WCAT_T", "WO_T", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CA
 # Order of the decoding-state buffers (FLASHGAU_DS_* in include/flashgau.h).
 DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
 
-EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_offsets", "flashgau_state_groups",
+EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_bytes", "flashgau_workspace_offsets", "flashgau_state_groups",
            "flash_gau_forward", "flash_gau_forward_rope", "flash_gau_forward_timed",
            "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     i64, sz = ctypes.c_int64, ctypes.c_size_t
     L.flashgau_workspace_size.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
     L.flashgau_workspace_size.restype = ctypes.c_int
+    L.flashgau_workspace_bytes.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int]
+    L.flashgau_workspace_bytes.restype = sz
     L.flashgau_workspace_offsets.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
     L.flashgau_workspace_offsets.restype = ctypes.c_int
     L.flashgau_state_groups.argtypes = [i64] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64)]
@@ -112,6 +114,11 @@ def workspace_size(B, n, d, e, s, chunk, causal, dtype) -> int:
     if rc != OK:
         raise FlashGauError(rc, "flashgau_workspace_size")
     return out.value
+
+
+def workspace_bytes(B, n, d, e, s, chunk, causal, dtype) -> int:
+    """flashgau_workspace_bytes: the workspace size, 0 for an empty or an invalid problem."""
+    return int(lib().flashgau_workspace_bytes(B, n, d, e, s, chunk, int(bool(causal)), dtype))
 
 
 def workspace_offsets(B, n, d, e, s, chunk, causal, dtype) -> dict:
@@ -164,6 +171,62 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t}; use torch.bfloat16 or torch.float32")
 
 
+def _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o, extra=()):
+    """Shape, dtype, device and layout checks of the layer's inputs (and of `extra`: (name, tensor,
+    shape) triples in X's dtype). Returns B, n, d, e, s, the dtype code and the device."""
+    import torch
+    if X.dim() != 3:
+        raise ValueError(f"X must be [B, n, d], got shape {tuple(X.shape)}")
+    B, n, d = X.shape
+    if W_u.dim() != 2 or W_z.dim() != 2:
+        raise ValueError("W_u and W_z must be matrices")
+    e = W_u.shape[1]
+    s = W_z.shape[1]
+    dt = _dtype_code(X.dtype)
+    for name, t, shape in (("W_u", W_u, (d, e)), ("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)),
+                           ("W_o", W_o, (e, d))) + tuple(extra):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != X.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from X dtype {X.dtype}")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if tuple(t.shape) != (4, s) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [4, {s}]")
+    tensors = (X, W_u, W_v, W_z, gamma, beta, W_o) + tuple(t for _, t, _ in extra)
+    dev = X.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous (row-major)")
+    return B, n, d, e, s, dt, dev
+
+
+def _check_output(t, name, shape, dtype, dev):
+    """A caller-supplied output buffer: exact shape and dtype, on the call's device, contiguous
+    (the library writes through its raw address and cannot check any of this)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} dtype {t.dtype}, expected {dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, nbytes, dev):
+    """A caller-supplied workspace: a contiguous uint8 tensor of at least nbytes on the device."""
+    import torch
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {ws.dtype}")
+    if ws.device != dev:
+        raise ValueError(f"workspace is on {ws.device}, expected {dev}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
+
+
 def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=None, workspace=None,
                       stream=None, rope_base=None):
     """One FLASH layer forward on the GPU. X [B, n, d]; W_u, W_v [d, e]; W_z [d, s]; gamma, beta
@@ -172,30 +235,16 @@ def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=Non
     same device) receives the intermediates; it is allocated when not given. ``rope_base`` (e.g.
     10000.0) selects flash_gau_forward_rope: the heads are rotated at their positions."""
     import torch
-    B, n, d = X.shape
-    e = W_u.shape[1]
-    s = W_z.shape[1]
-    dt = _dtype_code(X.dtype)
-    for name, t, shape in (("W_u", W_u, (d, e)), ("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)),
-                           ("W_o", W_o, (e, d))):
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-        if t.dtype != X.dtype:
-            raise TypeError(f"{name} dtype {t.dtype} differs from X dtype {X.dtype}")
-    for name, t in (("gamma", gamma), ("beta", beta)):
-        if tuple(t.shape) != (4, s) or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 [4, {s}]")
-    tensors = (X, W_u, W_v, W_z, gamma, beta, W_o)
-    dev = X.device
-    if dev.type != "cuda" or any(t.device != dev for t in tensors):
-        raise ValueError("all tensors must be on the same GPU")
-    if any(not t.is_contiguous() for t in tensors):
-        raise ValueError("all tensors must be contiguous (row-major)")
+    B, n, d, e, s, dt, dev = _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o)
     nbytes = workspace_size(B, n, d, e, s, chunk, causal, dt)
     if out is None:
         out = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+    else:
+        _check_output(out, "out", (B, n, d), X.dtype, dev)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptrs = (X.data_ptr(), W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), gamma.data_ptr(),
@@ -340,8 +389,16 @@ def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, 
         raise ValueError("x does not match the decoding state")
     if not x.is_contiguous() or any(not g.is_contiguous() or g.dtype != torch.float32 for g in (gamma, beta)):
         raise ValueError("x must be contiguous; gamma and beta contiguous float32 [4, s]")
+    if x.device.type != "cuda" or any(t.device != x.device for t in (packed, gamma, beta, state.buf)):
+        raise ValueError("x, the packed weights, gamma, beta and the state must be on one GPU")
+    if tuple(gamma.shape) != (4, state.s) or tuple(beta.shape) != (4, state.s):
+        raise ValueError(f"gamma and beta must be float32 [4, {state.s}]")
+    if packed.dtype != torch.uint8 or not packed.is_contiguous():
+        raise ValueError("packed must be the contiguous uint8 tensor pack_weights returned")
     if out is None:
         out = torch.empty((B, d), dtype=x.dtype, device=x.device)
+    else:
+        _check_output(out, "out", (B, d), x.dtype, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     rc = decode_step_raw(x.data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
@@ -398,19 +455,16 @@ def flash_gau_forward_train(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, w
     """flash_gau_forward that also leaves in ``workspace`` (uint8, at least
     backward_workspace_size() bytes) what flash_gau_backward_saved reads. Returns O."""
     import torch
-    B, n, d = X.shape
-    e, s = W_u.shape[1], W_z.shape[1]
-    dt = _dtype_code(X.dtype)
+    B, n, d, e, s, dt, dev = _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o)
     nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
-    if workspace.numel() < nbytes:
-        raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    _check_workspace(workspace, nbytes, dev)
     if out is None:
-        out = torch.empty((B, n, d), dtype=X.dtype, device=X.device)
+        out = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+    else:
+        _check_output(out, "out", (B, n, d), X.dtype, dev)
     if stream is None:
-        stream = torch.cuda.current_stream(X.device).cuda_stream
+        stream = torch.cuda.current_stream(dev).cuda_stream
     tensors = (X, W_u, W_v, W_z, gamma, beta, W_o)
-    if any(not t.is_contiguous() for t in tensors):
-        raise ValueError("all tensors must be contiguous (row-major)")
     rc = forward_train_raw(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n,
                            d, e, s, dt, out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
     if rc != OK:
@@ -427,37 +481,30 @@ def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, ro
     allocated when not given. ``saved=True`` calls flash_gau_backward_saved: ``workspace`` must then
     be the one a flash_gau_forward_train of the same inputs filled."""
     import torch
-    B, n, d = X.shape
-    e = W_u.shape[1]
-    s = W_z.shape[1]
-    dt = _dtype_code(X.dtype)
-    for name, t, shape in (("W_u", W_u, (d, e)), ("W_v", W_v, (d, e)), ("W_z", W_z, (d, s)),
-                           ("W_o", W_o, (e, d)), ("dO", dO, (B, n, d))):
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-        if t.dtype != X.dtype:
-            raise TypeError(f"{name} dtype {t.dtype} differs from X dtype {X.dtype}")
-    for name, t in (("gamma", gamma), ("beta", beta)):
-        if tuple(t.shape) != (4, s) or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 [4, {s}]")
+    if X.dim() != 3:
+        raise ValueError(f"X must be [B, n, d], got shape {tuple(X.shape)}")
+    B, n, d, e, s, dt, dev = _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o,
+                                           extra=(("dO", dO, tuple(X.shape)),))
     tensors = (X, W_u, W_v, W_z, gamma, beta, W_o, dO)
-    dev = X.device
-    if dev.type != "cuda" or any(t.device != dev for t in tensors):
-        raise ValueError("all tensors must be on the same GPU")
-    if any(not t.is_contiguous() for t in tensors):
-        raise ValueError("all tensors must be contiguous (row-major)")
     shapes = dict(dX=((B, n, d), X.dtype), dW_u=((d, e), X.dtype), dW_v=((d, e), X.dtype),
                   dW_z=((d, s), X.dtype), dgamma=((4, s), torch.float32),
                   dbeta=((4, s), torch.float32), dW_o=((e, d), X.dtype))
     grads = dict(out or {})
+    unknown = set(grads) - set(shapes)
+    if unknown:
+        raise ValueError(f"unknown gradient names {sorted(unknown)}")
     for k, (shape, tdt) in shapes.items():
         if k not in grads:
             grads[k] = torch.empty(shape, dtype=tdt, device=dev)
+        else:
+            _check_output(grads[k], k, shape, tdt, dev)
     nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
     if saved and workspace is None:
         raise ValueError("saved=True needs the workspace of a flash_gau_forward_train call")
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _check_workspace(workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     call = backward_saved_raw if saved else backward_raw

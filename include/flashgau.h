@@ -98,6 +98,12 @@ enum {
 int flashgau_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
                             int causal, flashgau_dtype dtype, size_t* out_bytes);
 
+/* The same size as a plain return value: bytes of device workspace flash_gau_forward needs, or 0
+ * when the problem is empty (B*n == 0) or invalid (any case in which flashgau_workspace_size
+ * returns an error code; call that function to tell the two apart). Host-only. */
+size_t flashgau_workspace_bytes(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                                int64_t chunk, int causal, flashgau_dtype dtype);
+
 /* Byte offsets of the FLASHGAU_WS_* buffers inside the workspace (each 256-byte aligned), written
  * to out_offsets[0 .. FLASHGAU_WS_COUNT-1]. Host-only. Returns FLASHGAU_OK or an error code. */
 int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,

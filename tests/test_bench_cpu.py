@@ -1,4 +1,5 @@
-"""CPU checks of the benchmark's contract: one GPU only, and its algorithmic FLOP accounting.
+"""CPU checks of the benchmark's contract: one GPU only, and its algorithmic FLOP and byte
+accounting.
 
 The per-configuration totals below were derived independently (by hand, from the work each step
 of the layer must do: the projection 2Nd(e+s) plus the gate 2Nde, the causal local term
@@ -67,3 +68,76 @@ def test_measured_traffic_needs_matching_workload_and_sources():
         assert b.measured_traffic("mix", "c3_causal_bf16_n4096") > 0
     else:
         assert b.measured_traffic("mix", "c3_causal_bf16_n4096") is None
+
+
+# Algorithmic bytes, one shape per code path of the cross-chunk sum. The totals are element counts
+# worked out by hand from what each kernel must read and write on that path (restated here as
+# numbers): scores read Q_quad and K_quad (2Ns) and write P's causal triangle c(c+1)/2 or c² per
+# chunk; the states stage reads K_lin and V of every chunk whose summary is used (causal: all but
+# each sequence's last) and writes, depending on the path, every chunk's in-group prefix, the
+# chunk or group totals, or the sequence total; the carry stage reads those totals and writes or
+# updates the states; mix reads V, P, Q_lin and the states of the chunks with a global term, X and
+# W_u, and writes Y.
+SMALL = (2, 1024, 64, 128, 32, 64)  # B, n, d, e, s, chunk: N = 2048, 16 chunks of 64, e*s = 4096
+
+
+@pytest.mark.parametrize("causal,ng,branch,ss,carry,mix", [
+    # causal, 4 groups of 4 chunks: prefixes B*G*es + group totals B*(ng-1)*es; carry reads those
+    # totals and updates chunks 4..15 in place
+    (True, 4, "groups", 131072 + 66560 + 307200 + 131072 + 24576, 24576 + 2 * 2 * 12 * 4096,
+     262144 + 66560 + 61440 + 122880 + 131072 + 8192 + 262144),
+    # causal, one chunk per group: chunk totals of chunks 0..14, carry writes all 16 states
+    (True, 16, "chunk_per_group", 131072 + 66560 + 307200 + 2 * 15 * 4096, 2 * 15 * 4096 + 2 * 16 * 4096,
+     262144 + 66560 + 61440 + 122880 + 131072 + 8192 + 262144),
+    # causal, one group: the states stage writes every state, no carry launch
+    (True, 1, "one_group", 131072 + 66560 + 307200 + 2 * 16 * 4096, 0,
+     262144 + 66560 + 61440 + 122880 + 131072 + 8192 + 262144),
+    # non-causal, one group: the sequence total only
+    (False, 1, "one_group", 131072 + 131072 + 327680 + 2 * 4096, 0,
+     262144 + 131072 + 65536 + 8192 + 131072 + 8192 + 262144),
+    # non-causal, 4 groups: group totals, summed by the carry stage
+    (False, 4, "noncausal_groups", 131072 + 131072 + 327680 + 2 * 4 * 4096, 2 * 4 * 4096 + 2 * 4096,
+     262144 + 131072 + 65536 + 8192 + 131072 + 8192 + 262144),
+])
+def test_algorithmic_bytes_per_state_branch(causal, ng, branch, ss, carry, mix):
+    b = _bench()
+    B, n, d, e, s, c = SMALL
+    assert b.state_branch(B, n, c, causal, ng) == branch
+    got = b.alg_bytes(B, n, d, e, s, c, causal, 2, ng)
+    assert got["scores_states"] == 2 * ss
+    assert got["carry"] == 2 * carry
+    assert got["mix"] == 2 * mix
+
+
+def test_algorithmic_bytes_single_causal_chunk():
+    # chunk = n, causal: no global term; the scores write the n(n+1)/2 triangle, nothing else moves
+    b = _bench()
+    B, n, d, e, s = 2, 1024, 64, 128, 32
+    assert b.state_branch(B, n, n, True, 1) == "none"
+    got = b.alg_bytes(B, n, d, e, s, n, True, 2, 1)
+    assert got["scores_states"] == 2 * (2 * 2048 * 32 + 2 * (1024 * 1025 // 2))
+    assert got["carry"] == 0
+    assert got["mix"] == 2 * (262144 + 2 * 524800 + 131072 + 8192 + 262144)
+
+
+def test_headline_bytes():
+    # n = 4096, B = 8, causal bf16, 16 chunks per sequence in 16 groups of one
+    b = _bench()
+    got = b.alg_bytes(8, 4096, 768, 1536, 128, 256, True, 2, 16)
+    assert got == {"pack": 14548992, "proj": 187105280, "scores_states": 174620672,
+                   "carry": 97517568, "mix": 317489152, "out": 153354240}
+
+
+def test_committed_counters_cover_the_algorithmic_bytes():
+    # The copy-calibrated HBM traffic of every kernel in the committed rocprofv3 summary must be at
+    # least the algorithmic minimum (a model that claims more bytes than any run moved is wrong).
+    b = _bench()
+    alg = b.alg_bytes(8, 4096, 768, 1536, 128, 256, True, 2, 16)
+    rows = {}
+    for line in open(b.PROFILE_BYTES).read().splitlines():
+        parts = line.split()
+        if parts and parts[0] in alg and len(parts) == 6:
+            rows[parts[0]] = int(parts[5])
+    assert set(rows) == set(alg)
+    for k, v in alg.items():
+        assert rows[k] >= 0.95 * v, (k, rows[k], v)
