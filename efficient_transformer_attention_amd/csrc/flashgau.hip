@@ -28,9 +28,38 @@
 // memory straight into a ring of two or three LDS stages (buffer loads with an LDS destination),
 // so the copies of later K-tiles are in flight while one is multiplied.
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
+
+// ------------------------------------------------------------------ allocation-free forward
+// flash_gau_forward_noalloc's workspace: a file-scope device array, one copy per GPU the library
+// is loaded on, held until the process ends. In host code `scratch` names a host-side stand-in,
+// never the device memory: the device address of each GPU's copy is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of the current device's scratch copy, looked up on the first call per device.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLASHGAU_ERR_HIP;
+  if (dev >= kMaxScratchDevices) return FLASHGAU_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FLASHGAU_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLASHGAU_OK;
+}
 
 template <class E>
 int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
@@ -199,6 +228,24 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       workspace, workspace_bytes, hip_stream, nullptr, 0.0f);
 }
 
+int flash_gau_forward_noalloc(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                              const float* gamma, const float* beta, const void* W_o,
+                              int64_t chunk, int causal, int64_t B, int64_t n, int64_t d, int64_t e,
+                              int64_t s, flashgau_dtype dtype, void* O, void* hip_stream) {
+  Plan pl;
+  const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &pl);
+  if (rc != FLASHGAU_OK) return rc;
+  if (pl.M == 0) return FLASHGAU_OK;
+  if (pl.total > kScratchBytes) return FLASHGAU_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int rs = scratch_for_current_device(&ws);
+  if (rs != FLASHGAU_OK) return rs;
+  return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                      ws, kScratchBytes, hip_stream, nullptr, 0.0f);
+}
+
+size_t flashgau_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, const void* W_z,
                            const float* gamma, const float* beta, const void* W_o, int64_t chunk,
                            int causal, float rope_base, int64_t B, int64_t n, int64_t d, int64_t e,
@@ -272,6 +319,8 @@ const char* flashgau_strerror(int code) {
     case FLASHGAU_ERR_WORKSPACE: return "workspace smaller than flashgau_workspace_size()";
     case FLASHGAU_ERR_ALIASING: return "output or workspace overlaps an input or each other";
     case FLASHGAU_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case FLASHGAU_ERR_TOO_LARGE:
+      return "the problem needs more workspace than flash_gau_forward_noalloc's fixed scratch holds";
     default: return "unknown error";
   }
 }

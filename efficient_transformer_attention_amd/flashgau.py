@@ -25,6 +25,7 @@ ERR_MISALIGNED = -4
 ERR_WORKSPACE = -5
 ERR_ALIASING = -6
 ERR_HIP = -7
+ERR_TOO_LARGE = -8
 
 # Order of the workspace buffers (FLASHGAU_WS_* in include/flashgau.h).
 WS_NAMES = ("WCAT_T", "WO_T", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CARRY")
@@ -33,7 +34,8 @@ WS_NAMES = ("WCAT_T", "WO_T", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CA
 DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
 
 EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_bytes", "flashgau_workspace_offsets", "flashgau_state_groups",
-           "flash_gau_forward", "flash_gau_forward_rope", "flash_gau_forward_timed",
+           "flash_gau_forward", "flash_gau_forward_noalloc", "flashgau_noalloc_scratch_bytes",
+           "flash_gau_forward_rope", "flash_gau_forward_timed",
            "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
            "flash_gau_decode_step", "flashgau_backward_workspace_size", "flash_gau_backward",
@@ -73,6 +75,11 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_forward.restype = ctypes.c_int
+    L.flash_gau_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
+                                            i64, i64, i64, i64, i64, ctypes.c_int, vp, vp]
+    L.flash_gau_forward_noalloc.restype = ctypes.c_int
+    L.flashgau_noalloc_scratch_bytes.argtypes = []
+    L.flashgau_noalloc_scratch_bytes.restype = sz
     L.flash_gau_forward_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, ctypes.c_float,
                                          i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_forward_rope.restype = ctypes.c_int
@@ -142,6 +149,17 @@ def forward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s
     """Direct call of flash_gau_forward with integer addresses; returns the library's code."""
     return lib().flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
                                    B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream)
+
+
+def forward_noalloc_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
+                        stream) -> int:
+    """Direct call of flash_gau_forward_noalloc with integer addresses; returns the library's code."""
+    return lib().flash_gau_forward_noalloc(X, W_u, W_v, W_z, gamma, beta, W_o, chunk,
+                                           int(bool(causal)), B, n, d, e, s, dtype, O, stream)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().flashgau_noalloc_scratch_bytes())
 
 
 def forward_rope_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_base, B, n, d, e, s,

@@ -20,7 +20,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensors are dense row-major; every device pointer is memory owned by the caller.
- *   - The library never allocates, frees or synchronises and keeps no mutable global state.
+ *   - The library never allocates, frees or synchronises. Its only mutable global state is the
+ *     per-device address of flash_gau_forward_noalloc's scratch array, set once per device.
  *   - flash_gau_forward enqueues its kernels on `hip_stream` (NULL = the null stream) and returns
  *     at once. Faults inside a kernel surface at the caller's next synchronisation.
  *   - Every argument is validated on the host before the first launch; on any error nothing has
@@ -55,6 +56,8 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
 #define FLASHGAU_ERR_WORKSPACE (-5)   /* workspace_bytes smaller than flashgau_workspace_size() */
 #define FLASHGAU_ERR_ALIASING (-6)    /* O or the workspace overlaps an input or each other */
 #define FLASHGAU_ERR_HIP (-7)         /* a kernel launch was rejected by the HIP runtime */
+#define FLASHGAU_ERR_TOO_LARGE (-8)   /* flash_gau_forward_noalloc: the problem's workspace exceeds
+                                       its fixed scratch (flashgau_noalloc_scratch_bytes()) */
 
 /* Workspace buffers, in the order of their byte offsets (see flashgau_workspace_offsets). Each
  * holds an intermediate of the one forward path; tests read them to check each stage. Layouts,
@@ -135,6 +138,26 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                       flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
                       void* hip_stream);
+
+/* flash_gau_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same kernels, the same
+ * validation and the same result (bitwise) as flash_gau_forward; the workspace is instead a
+ * device array inside the library, flashgau_noalloc_scratch_bytes() bytes (64 MiB) on every GPU
+ * the library is loaded on, held until the process ends. A problem whose workspace
+ * (flashgau_workspace_size) is larger returns FLASHGAU_ERR_TOO_LARGE before anything is launched.
+ * The call makes no allocation of any kind. On its first call on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress) with the current device, which must be the
+ * stream's device. Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, or host threads) race and must be serialised by the caller. The array
+ * keeps the last call's intermediates; nothing in it needs to start at zero. Arguments as for
+ * flash_gau_forward, without the workspace. Returns FLASHGAU_OK or an error code. */
+int flash_gau_forward_noalloc(const void* X, const void* W_u, const void* W_v, const void* W_z,
+                              const float* gamma, const float* beta, const void* W_o,
+                              int64_t chunk, int causal, int64_t B, int64_t n, int64_t d, int64_t e,
+                              int64_t s, flashgau_dtype dtype, void* O, void* hip_stream);
+
+/* Bytes of the fixed scratch array flash_gau_forward_noalloc uses (host-only). */
+size_t flashgau_noalloc_scratch_bytes(void);
 
 /* flash_gau_forward with a rotary position embedding of the four heads. The FLASH page
  * ("Experimental Analysis") says the paper's models use RoPE but does not define it; the reading

@@ -185,8 +185,8 @@ def test_aliasing_rejected(over):
 
 
 def test_strerror_covers_every_code():
-    texts = {c: fg.strerror(c) for c in range(-7, 1)}
-    assert len(set(texts.values())) == 8
+    texts = {c: fg.strerror(c) for c in range(-8, 1)}
+    assert len(set(texts.values())) == 9
     assert fg.strerror(-99) == "unknown error"
 
 
@@ -461,3 +461,18 @@ def test_workspace_bytes_returns_the_size_or_zero():
     assert fg.workspace_bytes(2, 100, 64, 128, 128, 64, True, fg.BF16) == 0   # n % chunk
     assert fg.workspace_bytes(1, 128, 60, 128, 128, 64, True, fg.BF16) == 0   # d % 8
     assert fg.workspace_bytes(1, 128, 64, 128, 128, 64, True, 7) == 0          # dtype
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    # the size check precedes any HIP call, so it needs no device; the addresses are never used
+    _fake_addresses_allowed()
+    assert fg.noalloc_scratch_bytes() == 64 << 20
+    args = (8, 4096, 768, 1536, 128, 256, True, fg.BF16)
+    assert fg.workspace_bytes(*args) > fg.noalloc_scratch_bytes()
+    base = 1 << 40
+    rc = fg.forward_noalloc_raw(*(base + (i << 30) for i in range(7)), 256, 1, 8, 4096, 768, 1536,
+                                128, fg.BF16, base + (7 << 30), None)
+    assert rc == fg.ERR_TOO_LARGE
+    # an empty problem succeeds without touching the device
+    assert fg.forward_noalloc_raw(None, None, None, None, None, None, None, 64, 1, 0, 256, 64, 128,
+                                  128, fg.BF16, None, None) == fg.OK
