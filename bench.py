@@ -586,6 +586,43 @@ def measure_forward(fg, torch, dev, inp, steps, warmup, settle_ms, kernel_steps,
     return rec, O
 
 
+def time_packed(fg, torch, dev, inp, plain_ms, steps=50, warmup=50):
+    """flash_gau_forward_packed on the same workload: the weights transposed once by
+    flashgau_pack_weights (as a model does once per weight set), then forward calls that skip the
+    transpose. Its output must equal flash_gau_forward's bit for bit."""
+    B, n, d, e, s = inp.shape
+    c, causal = inp.chunk, inp.causal
+    dt = fg.BF16 if inp.dtype == "bf16" else fg.F32
+    X, W_u, W_v, W_z, g, b, W_o = upload(torch, dev, inp)
+    packed = fg.pack_weights(W_u, W_v, W_z, W_o)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+    ref = fg.flash_gau_forward(X, W_u, W_v, W_z, g, b, W_o, c, causal, workspace=ws)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        rc = fg.forward_packed_raw(X.data_ptr(), packed.data_ptr(), packed.numel(), g.data_ptr(),
+                                   b.data_ptr(), c, causal, B, n, d, e, s, dt, O.data_ptr(),
+                                   ws.data_ptr(), nbytes, stream)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_forward_packed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    same = bool(torch.equal(O.view(torch.int16) if O.element_size() == 2 else O.view(torch.int32),
+                            ref.view(torch.int16) if ref.element_size() == 2 else ref.view(torch.int32)))
+    return {"entry": "flash_gau_forward_packed", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B * n / (ms * 1e-3), 1),
+            "plain_forward_ms_per_step": plain_ms, "bitwise_equal_to_plain": same}
+
+
 def oracle_sequence_error(inp, O, b):
     """max |O_gpu - O_ref| / max |O_ref| on sequence b, O_ref from the fp64 oracle."""
     import oracle
@@ -724,6 +761,10 @@ def main():
         backward["train_step_tokens_per_s"] = round(
             B * n / ((head["ms_per_step"] + backward["ms_per_step"]) * 1e-3), 1)
 
+    packed = None
+    if not args.no_extras:
+        packed = time_packed(fg, torch, dev, inp, head["ms_per_step"])
+
     rope = quad = None
     if not args.no_extras:
         print("[bench] rotary embedding and FLASH-Quad timings", file=sys.stderr, flush=True)
@@ -732,10 +773,14 @@ def main():
         rope = {"workload": name, "rope_base": 10000.0, "us_per_step": round(us_rope, 1),
                 "tokens_per_s": round(B * n / (us_rope * 1e-6), 1),
                 "us_per_step_without": round(us_plain, 1)}
+        # the same 16384 tokens as sequences of growing length: FLASH-Quad's cost per token grows
+        # with n, FLASH's does not; the crossover is where flash_speedup passes 1
         quad = []
-        for (qB, qn) in ((2, 8192), (1, 16384)):
+        for qn in (512, 1024, 2048, 4096, 8192, 16384):
+            qB = 16384 // qn
             us_q = time_forward(fg, torch, dev, qB, qn, d, e, s, qn, True, dtype, steps=5)
-            us_f = time_forward(fg, torch, dev, qB, qn, d, e, s, c, True, dtype, steps=5)
+            us_f = (time_forward(fg, torch, dev, qB, qn, d, e, s, c, True, dtype, steps=5)
+                    if qn > c else us_q)
             quad.append({"batch": qB, "seq_len": qn, "flash_quad_chunk_eq_n_us": round(us_q, 1),
                          f"flash_chunk_{c}_us": round(us_f, 1), "flash_speedup": round(us_q / us_f, 2)})
 
@@ -768,6 +813,7 @@ def main():
         "configs": configs,
         "decode": decode,
         "backward": backward,
+        "packed_weights": packed,
         "rope": rope,
         "flash_vs_flash_quad": quad,
     }

@@ -61,10 +61,13 @@ int scratch_for_current_device(void** out) {
   return FLASHGAU_OK;
 }
 
+// packed (optional): weights already transposed by flashgau_pack_weights; the pack stage then
+// launches nothing and the GEMMs read them there (wo_off: byte offset of W_oᵀ inside packed).
 template <class E>
 int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
                const float* gamma, const float* beta, const void* W_o, int causal, float rope_base,
-               void* O, char* ws, hipStream_t stream, hipEvent_t const* events) {
+               void* O, char* ws, hipStream_t stream, hipEvent_t const* events,
+               const void* packed = nullptr, size_t wo_off = 0) {
   using T = typename E::T;
   using S = Shapes<E>;
   // events (optional): events[i] is recorded right before stage i is launched, and
@@ -74,8 +77,10 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     if (!events) return true;
     return hipEventRecord(events[stage++], stream) == hipSuccess;
   };
-  T* WcatT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WCAT_T]);
-  T* WoT = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WO_T]);
+  T* WcatT = packed ? reinterpret_cast<T*>(const_cast<void*>(packed))
+                    : reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WCAT_T]);
+  T* WoT = packed ? reinterpret_cast<T*>(reinterpret_cast<char*>(const_cast<void*>(packed)) + wo_off)
+                  : reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WO_T]);
   T* Vt = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_VT]);
   T* Qq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_QQ]);
   T* Kq = reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_KQ]);
@@ -88,7 +93,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
 
   if (!mark()) return FLASHGAU_ERR_HIP;
-  launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
+  if (!packed) launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt,
@@ -173,29 +178,41 @@ int flashgau_workspace_offsets(int64_t B, int64_t n, int64_t d, int64_t e, int64
   return FLASHGAU_OK;
 }
 
+// The weights come either as the four matrices (W_u .. W_o) or as one packed buffer (packed,
+// packed_bytes; the matrices are then ignored).
 static int forward_impl(const void* X, const void* W_u, const void* W_v, const void* W_z,
                         const float* gamma, const float* beta, const void* W_o, int64_t chunk,
                         int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                         flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
-                        void* hip_stream, hipEvent_t const* events, float rope_base) {
+                        void* hip_stream, hipEvent_t const* events, float rope_base,
+                        const void* packed = nullptr, size_t packed_bytes = 0) {
   Plan pl;
   const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &pl);
   if (rc != FLASHGAU_OK) return rc;
   if (!(rope_base >= 0.0f) || !std::isfinite(rope_base)) return FLASHGAU_ERR_BAD_SHAPE;
+  size_t wo_off = 0, packed_total = 0;
+  if (packed) {
+    const int rp = packed_plan(d, e, s, dtype, &wo_off, &packed_total);
+    if (rp != FLASHGAU_OK) return rp;
+  }
   if (pl.M == 0) return FLASHGAU_OK;
-  if (!X || !W_u || !W_v || !W_z || !gamma || !beta || !W_o || !O || !workspace)
-    return FLASHGAU_ERR_NULL_PTR;
-  if (misaligned(X) || misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o) ||
-      misaligned(O) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
-      (reinterpret_cast<uintptr_t>(beta) & 3u))
+  if (!X || !gamma || !beta || !O || !workspace) return FLASHGAU_ERR_NULL_PTR;
+  if (!packed && (!W_u || !W_v || !W_z || !W_o)) return FLASHGAU_ERR_NULL_PTR;
+  if (misaligned(X) || misaligned(O) || misaligned(workspace) ||
+      (reinterpret_cast<uintptr_t>(gamma) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return FLASHGAU_ERR_MISALIGNED;
+  if (packed ? misaligned(packed)
+             : (misaligned(W_u) || misaligned(W_v) || misaligned(W_z) || misaligned(W_o)))
     return FLASHGAU_ERR_MISALIGNED;
   if (workspace_bytes < pl.total) return FLASHGAU_ERR_WORKSPACE;
+  if (packed && packed_bytes < packed_total) return FLASHGAU_ERR_WORKSPACE;
   const size_t es = size_t(pl.esz);
   const size_t nX = size_t(pl.M) * pl.d * es, nO = nX;
   const size_t nWu = size_t(pl.d) * pl.e * es, nWz = size_t(pl.d) * pl.s * es;
   const size_t nWo = size_t(pl.e) * pl.d * es, nGB = size_t(4) * pl.s * sizeof(float);
-  const void* ins[] = {X, W_u, W_v, W_z, W_o, gamma, beta};
-  const size_t nin[] = {nX, nWu, nWu, nWz, nWo, nGB, nGB};
+  const void* ins[] = {X, gamma, beta, packed ? packed : W_u, packed ? nullptr : W_v,
+                       packed ? nullptr : W_z, packed ? nullptr : W_o};
+  const size_t nin[] = {nX, nGB, nGB, packed ? packed_total : nWu, nWu, nWz, nWo};
   for (int i = 0; i < 7; ++i)
     if (overlaps(O, nO, ins[i], nin[i]) || overlaps(workspace, pl.total, ins[i], nin[i]))
       return FLASHGAU_ERR_ALIASING;
@@ -204,9 +221,9 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == FLASHGAU_BF16)
     return launch_all<BF16>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
-                            ws, stream, events);
+                            ws, stream, events, packed, wo_off);
   return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
-                         ws, stream, events);
+                         ws, stream, events, packed, wo_off);
 }
 
 int flashgau_state_groups(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
@@ -226,6 +243,17 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       void* hip_stream) {
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, hip_stream, nullptr, 0.0f);
+}
+
+int flash_gau_forward_packed(const void* X, const void* packed, size_t packed_bytes,
+                             const float* gamma, const float* beta, int64_t chunk, int causal,
+                             int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                             flashgau_dtype dtype, void* O, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  if (!packed) return FLASHGAU_ERR_NULL_PTR;
+  return forward_impl(X, nullptr, nullptr, nullptr, gamma, beta, nullptr, chunk, causal, B, n, d, e,
+                      s, dtype, O, workspace, workspace_bytes, hip_stream, nullptr, 0.0f, packed,
+                      packed_bytes);
 }
 
 int flash_gau_forward_noalloc(const void* X, const void* W_u, const void* W_v, const void* W_z,
@@ -314,7 +342,9 @@ const char* flashgau_strerror(int code) {
     case FLASHGAU_ERR_BAD_SHAPE:
       return "bad shape or argument (size < 1, n % chunk != 0, a size overflows, position or "
              "rotary base out of range)";
-    case FLASHGAU_ERR_UNSUPPORTED: return "unsupported (dtype, or d, e, s, chunk not a multiple of 8)";
+    case FLASHGAU_ERR_UNSUPPORTED:
+      return "unsupported (dtype; d, e, s, chunk not a multiple of 8; or a chunk so long that the "
+             "B*n*chunk score buffer exceeds 2^33 elements)";
     case FLASHGAU_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
     case FLASHGAU_ERR_WORKSPACE: return "workspace smaller than flashgau_workspace_size()";
     case FLASHGAU_ERR_ALIASING: return "output or workspace overlaps an input or each other";

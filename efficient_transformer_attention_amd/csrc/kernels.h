@@ -384,57 +384,67 @@ __device__ __forceinline__ void balanced_wave(int w, int& wm, int& wn) {
 }
 
 // ------------------------------------------------------------------------------ pack
-// Transposes src [R, C] into dst [C, R] in 64x64 tiles: 16-byte row reads, an LDS tile padded by
-// one element per row, 16-byte row writes. R and C are multiples of 8.
+// Transposes src [R, C] into dst [C, R] (R and C multiples of 8) without LDS: each lane moves a
+// V x V block (V = 16 bytes / element size: 8 x 8 bf16 or 4 x 4 fp32) with V 16-byte row loads,
+// transposes it in registers and writes V 16-byte rows. The 64 lanes of a wave cover an
+// 8V x 8V tile, lane (i, j) = (lane / 8, lane % 8) the block at rows 8... of (i, j): eight lanes
+// with one i read 128 contiguous bytes of a source row, eight lanes with one j write 128
+// contiguous bytes of a destination row. A block lies wholly inside or wholly outside the matrix.
 template <class E>
 struct TransposeJob {
   const typename E::T* src;  // [R, C]
   typename E::T* dst;        // [C, R]
   int R, C;
-  int tiles_c;     // tiles along C
-  int first_tile;  // index of this job's first tile in the launch
+  int tiles_c;     // wave tiles along C
+  int first_tile;  // index of this job's first wave tile in the launch
 };
 template <class E>
 struct PackArgs {
   TransposeJob<E> job[4];
   int njobs;
+  int ntiles;  // wave tiles over all jobs
 };
+
+// Transposes a 8x8 block of bf16 held as 8 rows of 4 packed pairs: out row k = column k of in.
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8], BF16) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)  // (row 2m, row 2m+1) of column k: low or high halves of pair k/2
+      out[k][m] = __builtin_amdgcn_perm(in[2 * m + 1][k >> 1], in[2 * m][k >> 1],
+                                        (k & 1) ? 0x07060302u : 0x05040100u);
+}
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4], F32) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) out[k][m] = in[m][k];
+}
 
 template <class E>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs<E> args) {
-  using T = typename E::T;
-  constexpr int kPer16 = 16 / E::kSize;  // elements per 16-byte access
-  __shared__ T tile[64][64 + 1];
+  constexpr int V = 16 / E::kSize;  // block edge
+  constexpr int TE = 8 * V;         // wave tile edge
+  const int tile = int(blockIdx.x) * 4 + int(threadIdx.x >> 6);
+  if (tile >= args.ntiles) return;
   int jb = 0;
 #pragma unroll
   for (int i = 1; i < 4; ++i)
-    if (i < args.njobs && int(blockIdx.x) >= args.job[i].first_tile) jb = i;
-  const TransposeJob<E> J = args.job[jb];
-  const int t = blockIdx.x - J.first_tile;
-  const int r0 = (t / J.tiles_c) * 64;
-  const int c0 = (t % J.tiles_c) * 64;
-  const int tid = threadIdx.x;
-  constexpr int kVecPerRow = 64 / kPer16;
-  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
-    const int rr = idx / kVecPerRow, cv = (idx % kVecPerRow) * kPer16;
-    if (r0 + rr < J.R && c0 + cv < J.C) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(J.src + int64_t(r0 + rr) * J.C + c0 + cv);
-      const T* e = reinterpret_cast<const T*>(&v);
+    if (i < args.njobs && tile >= args.job[i].first_tile) jb = i;
+  const TransposeJob<E>& J = args.job[jb];
+  const int t = tile - J.first_tile;
+  const int lane = threadIdx.x & 63;
+  const int r = (t / J.tiles_c) * TE + (lane >> 3) * V;  // first source row of the lane's block
+  const int col = (t % J.tiles_c) * TE + (lane & 7) * V;  // first source column
+  if (r >= J.R || col >= J.C) return;
+  u32x4 in[V], out[V];
 #pragma unroll
-      for (int k = 0; k < kPer16; ++k) tile[rr][cv + k] = e[k];
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
-    const int cc = idx / kVecPerRow, rv = (idx % kVecPerRow) * kPer16;
-    if (c0 + cc < J.C && r0 + rv < J.R) {
-      u32x4 v;
-      T* e = reinterpret_cast<T*>(&v);
+  for (int k = 0; k < V; ++k)
+    in[k] = *reinterpret_cast<const u32x4*>(J.src + int64_t(r + k) * J.C + col);
+  transpose_block(in, out, E());
 #pragma unroll
-      for (int k = 0; k < kPer16; ++k) e[k] = tile[rv + k][cc];
-      *reinterpret_cast<u32x4*>(J.dst + int64_t(c0 + cc) * J.R + r0 + rv) = v;
-    }
-  }
+  for (int k = 0; k < V; ++k)
+    *reinterpret_cast<u32x4*>(J.dst + int64_t(col + k) * J.R + r) = out[k];
 }
 
 // ------------------------------------------------------------------------------ proj
@@ -1172,6 +1182,9 @@ struct Plan {
   size_t total;
 };
 
+// largest score buffer B*n*chunk (elements) the forward materialises
+constexpr int64_t kMaxScoreElems = int64_t(1) << 33;
+
 // states tile (both element types) and the workgroup count the chunk grouping aims for
 constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
 
@@ -1212,6 +1225,9 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   if (!mul_ok(M, s, &cnt[FLASHGAU_WS_QQ])) return FLASHGAU_ERR_BAD_SHAPE;
   cnt[FLASHGAU_WS_KQ] = cnt[FLASHGAU_WS_QL] = cnt[FLASHGAU_WS_KLT] = cnt[FLASHGAU_WS_QQ];
   if (!mul_ok(M, chunk, &cnt[FLASHGAU_WS_P])) return FLASHGAU_ERR_BAD_SHAPE;
+  // Every chunk's c x c scores are kept in HBM; past 2^33 of them (16 GiB in bf16, e.g. one
+  // sequence of 131072 tokens as a single chunk) a shorter chunk is the layer to run.
+  if (cnt[FLASHGAU_WS_P] > kMaxScoreElems) return FLASHGAU_ERR_UNSUPPORTED;
   if (!mul_ok(causal ? p->nbg : B, e, &t0) || !mul_ok(t0, s, &cnt[FLASHGAU_WS_ST]))
     return FLASHGAU_ERR_BAD_SHAPE;
   cnt[FLASHGAU_WS_Y] = cnt[FLASHGAU_WS_VT];
@@ -1246,6 +1262,7 @@ template <class E>
 void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* W_o, int d, int e,
                  int s, typename E::T* WcatT, typename E::T* WoT, hipStream_t stream) {
   using T = typename E::T;
+  constexpr int TE = 8 * (16 / E::kSize);
   PackArgs<E> a;
   const int R[4] = {d, d, d, e};
   const int C[4] = {e, e, s, d};
@@ -1254,12 +1271,13 @@ void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* 
   T* dst[4] = {WcatT, WcatT + int64_t(e) * d, WcatT + int64_t(2 * e) * d, WoT};
   int tiles = 0;
   for (int i = 0; i < 4; ++i) {
-    const int tr = int(cdiv(R[i], 64)), tc = int(cdiv(C[i], 64));
+    const int tr = int(cdiv(R[i], TE)), tc = int(cdiv(C[i], TE));
     a.job[i] = {src[i], dst[i], R[i], C[i], tc, tiles};
     tiles += tr * tc;
   }
   a.njobs = 4;
-  hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(tiles)), dim3(256), 0, stream, a);
+  a.ntiles = tiles;
+  hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(cdiv(tiles, 4))), dim3(256), 0, stream, a);
 }
 
 }  // namespace

@@ -34,7 +34,8 @@ WS_NAMES = ("WCAT_T", "WO_T", "VT", "QQ", "KQ", "QL", "KLT", "P", "ST", "Y", "CA
 DS_NAMES = ("S", "KQ", "KL", "V", "U", "QQ", "QL", "Y")
 
 EXPORTS = ("flashgau_workspace_size", "flashgau_workspace_bytes", "flashgau_workspace_offsets", "flashgau_state_groups",
-           "flash_gau_forward", "flash_gau_forward_noalloc", "flashgau_noalloc_scratch_bytes",
+           "flash_gau_forward", "flash_gau_forward_packed", "flash_gau_forward_noalloc",
+           "flashgau_noalloc_scratch_bytes",
            "flash_gau_forward_rope", "flash_gau_forward_timed",
            "flashgau_packed_weights_size",
            "flashgau_pack_weights", "flashgau_decode_state_size", "flashgau_decode_state_offsets",
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.flash_gau_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     L.flash_gau_forward.restype = ctypes.c_int
+    L.flash_gau_forward_packed.argtypes = [vp, vp, sz, vp, vp, i64, ctypes.c_int, i64, i64, i64, i64,
+                                           i64, ctypes.c_int, vp, vp, sz, vp]
+    L.flash_gau_forward_packed.restype = ctypes.c_int
     L.flash_gau_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int,
                                             i64, i64, i64, i64, i64, ctypes.c_int, vp, vp]
     L.flash_gau_forward_noalloc.restype = ctypes.c_int
@@ -149,6 +153,13 @@ def forward_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s
     """Direct call of flash_gau_forward with integer addresses; returns the library's code."""
     return lib().flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
                                    B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream)
+
+
+def forward_packed_raw(X, packed, packed_bytes, gamma, beta, chunk, causal, B, n, d, e, s, dtype, O,
+                       workspace, workspace_bytes, stream) -> int:
+    """Direct call of flash_gau_forward_packed with integer addresses; returns the library's code."""
+    return lib().flash_gau_forward_packed(X, packed, packed_bytes, gamma, beta, chunk, int(bool(causal)),
+                                          B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream)
 
 
 def forward_noalloc_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,

@@ -51,7 +51,8 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
 #define FLASHGAU_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
 #define FLASHGAU_ERR_BAD_SHAPE (-2)   /* negative/zero size, n % chunk != 0, a size overflows, or a
                                        position / rotary base out of range */
-#define FLASHGAU_ERR_UNSUPPORTED (-3) /* unknown dtype, or d, e, s, chunk not a multiple of 8 */
+#define FLASHGAU_ERR_UNSUPPORTED (-3) /* unknown dtype; d, e, s, chunk not a multiple of 8; or the
+                                       score buffer B*n*chunk above 2^33 elements (see P below) */
 #define FLASHGAU_ERR_MISALIGNED (-4)  /* a tensor pointer is not 16-byte aligned */
 #define FLASHGAU_ERR_WORKSPACE (-5)   /* workspace_bytes smaller than flashgau_workspace_size() */
 #define FLASHGAU_ERR_ALIASING (-6)    /* O or the workspace overlaps an input or each other */
@@ -69,7 +70,10 @@ typedef enum { FLASHGAU_F32 = 0, FLASHGAU_BF16 = 1 } flashgau_dtype;
  *   KLT     [B*G, s, c]   the head K_lin, transposed inside each chunk
  *   P       [B*G, c, c]   relu(Q_quad K_quadᵀ / c)² per chunk. Causal: the entries above the
  *                         diagonal that the mix stage reads are zero; blocks of entries lying
- *                         entirely above the diagonal are left unwritten (never read)
+ *                         entirely above the diagonal are left unwritten (never read). Every
+ *                         chunk's scores are materialised, so B*n*chunk may not exceed 2^33
+ *                         (16 GiB in bf16): a longer single chunk (FLASH-Quad, chunk = n, beyond
+ *                         n = 92681 for B = 1) returns FLASHGAU_ERR_UNSUPPORTED
  *   ST      [B*G, e, s] (causal) or [B, e, s] (non-causal): the state S_g / n, transposed.
  *                         Left unwritten when causal and n == chunk (the one chunk's prefix is
  *                         empty, so the global term vanishes and its stages launch nothing)
@@ -138,6 +142,19 @@ int flash_gau_forward(const void* X, const void* W_u, const void* W_v, const voi
                       int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                       flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
                       void* hip_stream);
+
+/* flash_gau_forward with the weights packed once per weight set by flashgau_pack_weights (the
+ * transposed layout every GEMM of the forward reads, declared with the decoding entry points
+ * below): the call then runs no transpose. packed, packed_bytes: that buffer (at least
+ * flashgau_packed_weights_size(d, e, s, dtype) bytes, 16-byte aligned, same d, e, s and dtype);
+ * it must not overlap O or the workspace. The WCAT_T and WO_T regions of the workspace are left
+ * unwritten. Every other argument, the validation and the result (bitwise) are as for
+ * flash_gau_forward of the weights that were packed. Returns FLASHGAU_OK or an error code. */
+int flash_gau_forward_packed(const void* X, const void* packed, size_t packed_bytes,
+                             const float* gamma, const float* beta, int64_t chunk, int causal,
+                             int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
+                             flashgau_dtype dtype, void* O, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
 
 /* flash_gau_forward for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same kernels, the same

@@ -85,6 +85,7 @@ __all__ = [
     "combine",
     "flash_forward",
     "brute_force_forward",
+    "forward_rows",
     "rnn_global_linear",
     "cumsum_global_linear",
     "gau_forward",
@@ -324,6 +325,42 @@ def brute_force_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_
         a_lin = np.where(lin_mask, Ql[b] @ Kl[b].T / n, 0.0)
         O[b] = (U[b] * ((a_quad + a_lin) @ V[b])) @ _f64(W_o)
     return O
+
+
+def forward_rows(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rows, rope_base=None):
+    """Selected output rows of ONE sequence, each computed on its own from the definitions, for
+    sequences too long for the n×n matrices of brute_force_forward.
+
+    X is [n, d] (one sequence); rows are token indices. Row i of chunk g = i // c gets
+    local_i = Σ_j relu(qq_i·kq_j / c)² v_j over the keys j of chunk g (j <= i when causal; "Mixed
+    Chunk", first display), global_i = Σ_j (ql_i·kl_j / n) v_j over the keys j of the chunks before
+    g (causal) or of every chunk (non-causal; "Mixed Chunk", second and third displays, the /n
+    reading), and o_i = (u_i ⊙ (local_i + global_i)) W_o (last display). U, V and the heads come
+    from project and scale_offset_heads (rotated when ``rope_base`` is given). Returns
+    [len(rows), d] in float64.
+    """
+    X = _f64(X)
+    if X.ndim != 2:
+        raise ValueError("forward_rows takes one sequence [n, d]")
+    n = X.shape[0]
+    _chunks(n, chunk)
+    rows = [int(r) for r in rows]
+    last = max(rows) + 1 if causal else n
+    U, V, Z = project(X[:last], W_u, W_v, W_z)
+    Qq, Kq, Ql, Kl = scale_offset_heads(Z, gamma, beta)
+    if rope_base is not None:
+        pos = np.arange(last)
+        Qq, Kq, Ql, Kl = (rotary(h, pos, rope_base) for h in (Qq, Kq, Ql, Kl))
+    out = np.zeros((len(rows), _f64(W_o).shape[1]))
+    for k, i in enumerate(rows):
+        g0 = (i // chunk) * chunk
+        hi = i + 1 if causal else g0 + chunk
+        w = np.maximum(Kq[g0:hi] @ Qq[i] / chunk, 0.0) ** 2
+        local = w @ V[g0:hi]
+        lin_keys = slice(0, g0) if causal else slice(0, n)
+        glob = ((Kl[lin_keys] @ Ql[i]) / n) @ V[lin_keys]
+        out[k] = (U[i] * (local + glob)) @ _f64(W_o)
+    return out
 
 
 def rnn_global_linear(Ql, Kl, V, chunk, n):

@@ -476,3 +476,14 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     # an empty problem succeeds without touching the device
     assert fg.forward_noalloc_raw(None, None, None, None, None, None, None, 64, 1, 0, 256, 64, 128,
                                   128, fg.BF16, None, None) == fg.OK
+
+
+def test_score_buffer_limit():
+    # chunk = n keeps n*n scores per sequence: 2^33 elements is the most the forward materialises
+    assert fg.workspace_size(1, 65536, 64, 128, 128, 65536, True, fg.BF16) > 2 * 65536 ** 2
+    with pytest.raises(fg.FlashGauError) as ei:
+        fg.workspace_size(1, 131072, 64, 128, 128, 131072, True, fg.BF16)
+    assert ei.value.code == fg.ERR_UNSUPPORTED
+    assert "score buffer" in fg.strerror(fg.ERR_UNSUPPORTED)
+    # the same sequence in chunks of 512 is fine
+    assert fg.workspace_size(1, 131072, 64, 128, 128, 512, True, fg.BF16) > 0

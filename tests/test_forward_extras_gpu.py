@@ -1,0 +1,113 @@
+"""GPU checks around the forward's boundary: the weight transpose is exact, the packed-weights
+entry point returns bitwise what flash_gau_forward does, and the forward writes nothing outside O
+and its workspace (guard bands of 0xFF bytes around both stay untouched).
+"""
+
+import numpy as np
+import pytest
+
+from efficient_transformer_attention_amd import flashgau as fg
+from efficient_transformer_attention_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    # name: (B, n, d, e, s, chunk, causal, dtype)
+    "ragged_causal_bf16": (2, 216, 200, 136, 24, 72, True, "bf16"),
+    "ragged_noncausal_fp32": (3, 144, 40, 88, 136, 48, False, "f32"),
+    "c2_causal_bf16": (4, 1024, 512, 1024, 128, 256, True, "bf16"),
+    "one_chunk_causal_bf16": (2, 256, 128, 256, 128, 256, True, "bf16"),
+}
+GUARD = 4096  # bytes on each side
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _setup(name, seed=0):
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype = SHAPES[name]
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=seed, beta_std=0.1)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(t).contiguous()
+
+    args = [up(inp.X), up(inp.W_u), up(inp.W_v), up(inp.W_z), up(inp.gamma, torch.float32),
+            up(inp.beta, torch.float32), up(inp.W_o)]
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+    print(f"[gpu case] {name}", flush=True)
+    return (B, n, d, e, s, c, causal, dt, tdt), args
+
+
+def _bits(t):
+    torch = _torch()
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+@pytest.mark.parametrize("name", ["ragged_causal_bf16", "ragged_noncausal_fp32"])
+def test_weight_transpose_is_exact(name):
+    torch = _torch()
+    (B, n, d, e, s, c, causal, dt, tdt), args = _setup(name)
+    X, W_u, W_v, W_z, g, b, W_o = args
+    ws = torch.empty(fg.workspace_size(B, n, d, e, s, c, causal, dt), dtype=torch.uint8, device="cuda")
+    fg.flash_gau_forward(*args, c, causal, workspace=ws)
+    packed = fg.pack_weights(W_u, W_v, W_z, W_o)
+    torch.cuda.synchronize()
+    v = fg.workspace_views(ws, B, n, d, e, s, c, causal, dt)
+    want_cat = torch.cat([W_u, W_v, W_z], dim=1).t().contiguous()
+    assert torch.equal(_bits(v["WCAT_T"]), _bits(want_cat))
+    assert torch.equal(_bits(v["WO_T"]), _bits(W_o.t().contiguous()))
+    esz = 2 if dt == fg.BF16 else 4
+    cat_bytes = (2 * e + s) * d * esz
+    wo_off = (cat_bytes + 255) // 256 * 256
+    assert torch.equal(_bits(packed[:cat_bytes].view(tdt).view(2 * e + s, d)), _bits(want_cat))
+    assert torch.equal(_bits(packed[wo_off:wo_off + d * e * esz].view(tdt).view(d, e)),
+                       _bits(W_o.t().contiguous()))
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_packed_weights_forward_is_bitwise_the_forward(name):
+    torch = _torch()
+    (B, n, d, e, s, c, causal, dt, tdt), args = _setup(name, seed=3)
+    X, W_u, W_v, W_z, g, b, W_o = args
+    ref = fg.flash_gau_forward(*args, c, causal)
+    packed = fg.pack_weights(W_u, W_v, W_z, W_o)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(ref, float("nan"))
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):  # twice: the second call reuses everything the first left
+        rc = fg.forward_packed_raw(X.data_ptr(), packed.data_ptr(), packed.numel(), g.data_ptr(),
+                                   b.data_ptr(), c, causal, B, n, d, e, s, dt, out.data_ptr(),
+                                   ws.data_ptr(), nbytes, stream)
+        assert rc == fg.OK
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref))
+    # a packed buffer one byte short is refused before anything runs
+    rc = fg.forward_packed_raw(X.data_ptr(), packed.data_ptr(), packed.numel() - 1, g.data_ptr(),
+                               b.data_ptr(), c, causal, B, n, d, e, s, dt, out.data_ptr(),
+                               ws.data_ptr(), nbytes, stream)
+    assert rc == fg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_forward_writes_only_its_output_and_workspace(name):
+    torch = _torch()
+    (B, n, d, e, s, c, causal, dt, tdt), args = _setup(name, seed=1)
+    esz = 2 if dt == fg.BF16 else 4
+    ref = fg.flash_gau_forward(*args, c, causal)
+    o_bytes = B * n * d * esz
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+    o_buf = torch.full((o_bytes + 2 * GUARD,), 0xFF, dtype=torch.uint8, device="cuda")
+    w_buf = torch.full((nbytes + 2 * GUARD,), 0xFF, dtype=torch.uint8, device="cuda")
+    O = o_buf[GUARD:GUARD + o_bytes].view(tdt).view(B, n, d)
+    ws = w_buf[GUARD:GUARD + nbytes]
+    fg.flash_gau_forward(*args, c, causal, out=O, workspace=ws)
+    torch.cuda.synchronize()
+    for buf, size in ((o_buf, o_bytes), (w_buf, nbytes)):
+        assert bool((buf[:GUARD] == 0xFF).all())
+        assert bool((buf[GUARD + size:] == 0xFF).all())
+    assert torch.equal(_bits(O), _bits(ref))

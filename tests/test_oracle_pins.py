@@ -314,3 +314,36 @@ def test_branch_magnitudes_at_workload_distribution():
     _, it = oracle.flash_forward(**_args(inp), return_intermediates=True)
     rms = lambda a: float(np.sqrt(np.mean(a ** 2)))  # noqa: E731
     assert rms(it["Vl"][:, 256:]) > 10 * rms(it["Vq"])
+
+
+# ------------------------------------------------------------------ row-wise evaluation for long sequences
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n,chunk,rope", [(16, 4, None), (16, 16, None), (24, 8, 100.0), (12, 1, None),
+                                          (32, 32, 10.0)])
+def test_forward_rows_match_chunked_and_brute_force(n, chunk, rope, causal):
+    # every row, and a ragged selection, of each sequence against the chunked oracle (itself pinned
+    # by brute force above) and against the materialised n x n matrices
+    inp = _small(n=n, chunk=chunk, causal=causal, seed=n + chunk)
+    O = oracle.flash_forward(**_args(inp), rope_base=rope)
+    O_bf = oracle.brute_force_forward(**_args(inp), rope_base=rope)
+    for b in range(inp.X.shape[0]):
+        kw = _args(inp)
+        kw["X"] = inp.X[b]
+        for rows in (list(range(n)), [n - 1, 0, n // 2, 1]):
+            got = oracle.forward_rows(**kw, rows=rows, rope_base=rope)
+            assert _rel(got, O[b, rows]) <= 1e-12
+            assert _rel(got, O_bf[b, rows]) <= 1e-12
+
+
+def test_forward_rows_single_chunk_is_the_quadratic_gau():
+    # chunk = n, causal: row i is (u_i ⊙ Σ_{j<=i} relu(q_i·k_j / n)² v_j) W_o (the appendix's 1/n²)
+    inp = _small(B=1, n=20, chunk=20, causal=True, seed=11)
+    U, V, Z = oracle.project(inp.X[0], inp.W_u, inp.W_v, inp.W_z)
+    Qq, Kq, _, _ = oracle.scale_offset_heads(Z, inp.gamma, inp.beta)
+    rows = [0, 7, 19]
+    want = np.stack([(U[i] * sum(max(Qq[i] @ Kq[j] / 20, 0.0) ** 2 * V[j] for j in range(i + 1))) @ inp.W_o
+                     for i in rows])
+    kw = _args(inp)
+    kw["X"] = inp.X[0]
+    assert _rel(oracle.forward_rows(**kw, rows=rows), want) <= 1e-12

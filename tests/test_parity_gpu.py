@@ -262,3 +262,23 @@ def test_parity_full_size_sampled_sequences(name):
     err = _rel(got[sample], ref)
     print(f"  sequences {sample}: max rel err {err:.3e}", flush=True)
     assert err <= TOL[inp.dtype]
+
+
+# FLASH-Quad (chunk = n) at the long sequences the benchmark compares with FLASH: one whole
+# sequence per shape, its output checked row by row against the oracle's row-wise evaluation
+# (every sampled row sums relu²(q·k / n) v over all its earlier keys, up to 16384 of them).
+LONG_QUAD = [(2, 8192, 1), (1, 16384, 0)]  # (B, n, sequence checked)
+
+
+@pytest.mark.parametrize("B,n,seq", LONG_QUAD)
+def test_flash_quad_long_sequences(B, n, seq):
+    d, e, s = 768, 1536, 128
+    _announce(f"flash_quad B={B} n={n} chunk=n")
+    inp = gen.make_inputs(B, n, d, e, s, n, True, "bf16", seed=5, beta_std=0.1)
+    O = run_gpu(inp)
+    rng = np.random.default_rng(n)
+    rows = sorted({0, 1, 2, n // 2, n - 2, n - 1, *rng.integers(0, n, 40).tolist()})
+    ref = oracle.forward_rows(inp.X[seq], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o,
+                              n, True, rows)
+    assert np.isfinite(O).all()
+    assert _rel(O[seq, rows], ref) <= TOL["bf16"]
