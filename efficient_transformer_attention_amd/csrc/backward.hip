@@ -939,10 +939,7 @@ int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const 
   }
   {
     OutArgs<E> a{W(FLASHGAU_WS_WO_T), W(FLASHGAU_WS_Y), reinterpret_cast<T*>(O), M, d, e};
-    const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
-    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
-                                    S::kOutPrio>),
-                       dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
+    launch_out<E>(a, stream);
   }
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
 }

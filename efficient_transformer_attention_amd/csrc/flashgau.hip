@@ -137,10 +137,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
     OutArgs<E> a{WoT, Y, reinterpret_cast<T*>(O), M, d, e};
-    const int64_t nb = cdiv(d, S::kOutBM) * cdiv(M, S::kOutBN);
-    hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
-                                    S::kOutPrio>),
-                       dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
+    launch_out<E>(a, stream);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;

@@ -21,7 +21,9 @@ namespace {
 // Operand tiles travel from global memory straight into a ring of NS LDS stages (no staging
 // registers): with NS = 3 the loads of tile t+2 fly while tile t is multiplied, one barrier per
 // tile; with NS = 2 (tiles too large for three stages) the loads of tile t+2 are issued after
-// tile t has been consumed, two barriers per tile. PRIO raises the wave priority while it issues
+// tile t has been consumed, two barriers per tile, or, with SB (single barrier), the loads of
+// tile t+1 are issued right after the barrier that opens tile t (the stage they fill held tile
+// t-1, which every wave finished before that barrier), one barrier per tile. PRIO raises the wave priority while it issues
 // matrix instructions; iglp_opt(1) asks the scheduler to interleave the LDS reads with them.
 //
 // Operand layouts (AL for A, BL for B): kLayoutK (the default) stores each of the tile's rows with
@@ -34,7 +36,7 @@ namespace {
 constexpr int kLayoutK = 0, kLayoutMN = 1;
 
 template <class E, int BM, int BN, int WM, int WN, int NS = 3, bool PRIO = false, int IGLP = 1,
-          int AL = kLayoutK, int BL = kLayoutK>
+          int AL = kLayoutK, int BL = kLayoutK, bool SB = false>
 struct TileGemm {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kWaves = WM * WN;
@@ -196,6 +198,17 @@ struct TileGemm {
   __device__ __forceinline__ static void pipeline(u32x4* lds, int nt, Tiles&& tiles, Body&& body,
                                                   int wave, int lane) {
     if (nt <= 0) return;
+    if constexpr (NS == 2 && SB) {
+      issue_tile(lds, tiles, 0, wave, lane);
+      for (int t = 0; t < nt; ++t) {
+        wait_vm<0>();     // this wave's copies of tile t are done (nothing else is in flight)
+        __syncthreads();  // tile t is in LDS for every wave; every wave is done with tile t-1
+        if (t + 1 < nt) issue_tile(lds, tiles, t + 1, wave, lane);
+        body(t, lds + (t % NS) * kStage);
+      }
+      __syncthreads();
+      return;
+    }
     issue_tile(lds, tiles, 0, wave, lane);
     if (nt > 1) issue_tile(lds, tiles, 1, wave, lane);
     for (int t = 0; t < nt; ++t) {
@@ -1094,9 +1107,9 @@ struct OutArgs {
   int M, d, e;
 };
 
-template <class E, int BM, int BN, int WM, int WN, int NS, bool PRIO>
+template <class E, int BM, int BN, int WM, int WN, int NS, bool PRIO, bool SB = false>
 __global__ __launch_bounds__(64 * WM * WN) void out_kernel(OutArgs<E> p) {
-  using G = TileGemm<E, BM, BN, WM, WN, NS, PRIO>;
+  using G = TileGemm<E, BM, BN, WM, WN, NS, PRIO, 1, kLayoutK, kLayoutK, SB>;
   __shared__ u32x4 lds[G::kLds];
   const int ntd = (p.d + BM - 1) / BM;
   const int ntt = (p.M + BN - 1) / BN;
@@ -1146,6 +1159,9 @@ template <> struct Shapes<BF16> {
   static constexpr int kMixBM = 128, kMixBN = 128, kMixWM = 2, kMixWN = 4, kMixNS = 2;
   static constexpr int kOutBM = 256, kOutBN = 128, kOutWM = 4, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = true;
+  // the output GEMM's large tile (256 x 256, 8 waves of 128 x 64, single-barrier two-stage ring),
+  // taken when its tile count fills the CUs' rounds better (launch_out)
+  static constexpr bool kOutBig = true;
 };
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
@@ -1155,6 +1171,7 @@ template <> struct Shapes<F32> {
   static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
   static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
+  static constexpr bool kOutBig = false;
 };
 
 // The scores stage leaves P tiles entirely above the diagonal unwritten. The mix stage never
@@ -1255,6 +1272,38 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   const int64_t pack_tiles = cdiv(d, 64) * (2 * cdiv(e, 64) + cdiv(s, 64)) + cdiv(e, 64) * cdiv(d, 64);
   if (pack_tiles > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
   return FLASHGAU_OK;
+}
+
+// The output GEMM O = Y W_o. bf16 has two tile shapes, both one workgroup per CU: 256 (features)
+// x 128 (tokens) with a three-stage ring, and 256 x 256 with a single-barrier two-stage ring,
+// which does the work of two of the smaller tiles in about 1.65 times their time (measured at
+// d = 768 and 1024, e = 1536 and 2048). The launch takes the shape whose tiles fill the chip's
+// rounds of kCUs workgroups better: at B*n = 32768, d = 768 the small tiles make 3 full rounds
+// and the large 1.5; at B*n = 16384 (d = 768) or d = 1024 the large tiles win.
+constexpr int64_t kCUs = 256;  // MI355X compute units
+
+inline bool out_big_tiles(int64_t M, int64_t d, bool big_ok) {
+  if (!big_ok) return false;
+  // 1.65 x the rounds of large tiles against the rounds of small tiles, in integers
+  const int64_t small = cdiv(d, 256) * cdiv(M, 128), large = cdiv(d, 256) * cdiv(M, 256);
+  return 100 * cdiv(large, kCUs) * 165 < 100 * 100 * cdiv(small, kCUs);
+}
+
+template <class E>
+void launch_out(const OutArgs<E>& a, hipStream_t stream) {
+  using S = Shapes<E>;
+  if constexpr (S::kOutBig) {
+    if (out_big_tiles(a.M, a.d, true)) {
+      const int64_t nb = cdiv(a.d, 256) * cdiv(a.M, 256);
+      hipLaunchKernelGGL((out_kernel<E, 256, 256, 2, 4, 2, false, true>), dim3(unsigned(nb)),
+                         dim3(512), 0, stream, a);
+      return;
+    }
+  }
+  const int64_t nb = cdiv(a.d, S::kOutBM) * cdiv(a.M, S::kOutBN);
+  hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
+                                  S::kOutPrio>),
+                     dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
 }
 
 // pack: (W_u | W_v | W_z)ᵀ into WcatT [2e+s, d] and W_oᵀ into WoT [d, e], one launch.

@@ -282,3 +282,13 @@ def test_flash_quad_long_sequences(B, n, seq):
                               n, True, rows)
     assert np.isfinite(O).all()
     assert _rel(O[seq, rows], ref) <= TOL["bf16"]
+
+
+def test_parity_large_output_tiles_ragged():
+    # B*n = 16384 with d = 520: the output GEMM takes its 256 x 256 tiles (192 of them, one round,
+    # against two rounds of 256 x 128 tiles), the last feature tile holding only 8 of 256 rows
+    _announce("large output tiles, ragged d")
+    inp = gen.make_inputs(1, 16384, 520, 264, 24, 256, True, "bf16", seed=9, beta_std=0.1)
+    got = run_gpu(inp)
+    ref = run_oracle(inp)
+    assert _rel(got, ref) <= TOL["bf16"]
