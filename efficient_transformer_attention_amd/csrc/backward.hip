@@ -27,6 +27,9 @@
 // nothing is transposed in memory. Tiles are 128 x 128 with 8 waves for bf16 and 64 x 64 with
 // 4 waves for fp32 (256-byte rows either way, as the MN-major tiles need).
 
+#include <mutex>
+#include <vector>
+
 #include "kernels.h"
 
 namespace {
@@ -49,6 +52,24 @@ template <class E, int AL = KK, int BL = KK>
 using BGemm = TileGemm<E, BShapes<E>::BT, BShapes<E>::BT, BShapes<E>::WM, BShapes<E>::WN,
                        BShapes<E>::NS, false, 1, AL, BL>;
 
+// The input and weight gradients are the longest contractions (over the 2e + s gate features, or
+// over a token range): bf16 runs them on 256 x 256 tiles, 8 waves of 128 x 64 with a
+// single-barrier two-stage ring, which read half the LDS fragment bytes per product that the
+// 128 x 128 tiles' 64 x 32 wave tiles do. The fp32 partials of such a tile are staged in two
+// passes (the whole wave tile would not fit the LDS tiles).
+template <class E> struct XShapes;
+template <> struct XShapes<BF16> {
+  static constexpr int BT = 256, WM = 2, WN = 4, NS = 2, kPasses = 2;
+  static constexpr bool SB = true;
+};
+template <> struct XShapes<F32> {
+  static constexpr int BT = 64, WM = 2, WN = 2, NS = 3, kPasses = 1;
+  static constexpr bool SB = false;
+};
+template <class E, int AL = KK, int BL = KK>
+using XGemm = TileGemm<E, XShapes<E>::BT, XShapes<E>::BT, XShapes<E>::WM, XShapes<E>::WN,
+                       XShapes<E>::NS, false, 1, AL, BL, XShapes<E>::SB>;
+
 template <class E>
 __device__ __forceinline__ int ksteps(int elems) {
   return (elems * E::kSize + kStageBytes - 1) / kStageBytes;
@@ -62,7 +83,7 @@ constexpr int kadv() {
 
 // One tile of C = A Bᵀ over nk K-tiles from the offsets ka0, kb0 (bytes or rows, by layout),
 // stored fp32 row-major at out (pitch ldo), rows < rows and columns < cols only.
-template <class G>
+template <class G, int PASSES = 1>
 __device__ __forceinline__ void gemm_to_f32(u32x4* lds, const Src& a, int ka0, const Src& b, int kb0,
                                             int nk, float* out, int64_t ldo, int rows, int cols) {
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -77,7 +98,7 @@ __device__ __forceinline__ void gemm_to_f32(u32x4* lds, const Src& a, int ka0, c
           kb = kb0 + t * kadv<G, false>();
         },
         NoPre(), wave, wm, wn, lane);
-  g.template stage_cols<float>(
+  g.template stage_cols<float, PASSES>(
       lds, wave, wm, wn, lane,
       [&](int, int, int, int, const f32x4& v, float* o) {
 #pragma unroll
@@ -608,9 +629,9 @@ struct DXArgs {
 // dXᵀ tiles (input features x tokens) over the three K ranges e | e | s.
 template <class E>
 __device__ __forceinline__ void dx_block(const DXArgs<E>& p, u32x4* lds, int lid) {
-  using G = BGemm<E>;
+  using G = XGemm<E>;
   using T = typename E::T;
-  constexpr int BT = BShapes<E>::BT, WN = BShapes<E>::WN;
+  constexpr int BT = XShapes<E>::BT, WN = XShapes<E>::WN;
   const int ntd = (p.d + BT - 1) / BT;
   const int nt = lid / ntd, mt = lid % ntd;
   const int m0 = mt * BT, n0 = nt * BT;  // m: input feature, n: token
@@ -672,8 +693,8 @@ struct WArgs {
 
 template <class E>
 __device__ __forceinline__ void wgrad_block(const WArgs<E>& p, u32x4* lds, int lid) {
-  using G = BGemm<E, MN, MN>;
-  constexpr int BT = BShapes<E>::BT;
+  using G = XGemm<E, MN, MN>;
+  constexpr int BT = XShapes<E>::BT;
   WJob<E> J = p.job[0];
 #pragma unroll
   for (int i = 1; i < 4; ++i)
@@ -688,16 +709,17 @@ __device__ __forceinline__ void wgrad_block(const WArgs<E>& p, u32x4* lds, int l
   const int ntok = min(p.M, tbeg + p.tps) - tbeg;
   const Src a = make_src_mn(J.A, tbeg, J.Fa, E::kSize, ntok, m0, J.Fa - m0);
   const Src b = make_src_mn(J.B, tbeg, J.Fb, E::kSize, ntok, n0, J.Fb - n0);
-  gemm_to_f32<G>(lds, a, 0, b, 0, ksteps<E>(ntok), J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0,
+  gemm_to_f32<G, XShapes<E>::kPasses>(lds, a, 0, b, 0, ksteps<E>(ntok), J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0,
                  J.Fb, J.Fa - m0, J.Fb - n0);
 }
 
 // One launch for the input and weight gradients, which read the same finished inputs: the
 // weight-gradient tiles first, then the dX tiles.
 template <class E>
-__global__ __launch_bounds__(BGemm<E>::kThreads) void dx_wgrad_kernel(DXArgs<E> x, WArgs<E> w,
+__global__ __launch_bounds__(XGemm<E>::kThreads) void dx_wgrad_kernel(DXArgs<E> x, WArgs<E> w,
                                                                       int n_w, int n_dx) {
-  __shared__ u32x4 lds[BGemm<E>::kLds];
+  static_assert(XGemm<E>::kLds == XGemm<E, MN, MN>::kLds, "one LDS size for both tile kinds");
+  __shared__ u32x4 lds[XGemm<E>::kLds];
   const int bid = blockIdx.x;
   if (bid < n_w)
     wgrad_block<E>(w, lds, xcd_remap(bid, n_w));
@@ -788,11 +810,105 @@ struct BPlan {
   int64_t wcount[4];      // elements of dW_u, dW_v, dW_z, dW_o
   int64_t nzb;            // dz row blocks
   int64_t bt;             // backward tile
+  int64_t xbt;            // tile of the input and weight gradients
   size_t off[BR_COUNT];
   size_t total;
 };
 
-constexpr int64_t kWgradTargetBlocks = 2048;
+// Token-range splits of the weight gradients. The input/weight-gradient launch hands its tiles
+// out in launch order (the weight-gradient tiles, split after split, then the dX tiles) to
+// whichever slot frees first; bf16's 128 KB tiles hold one slot per CU. The host replays that
+// greedy schedule for each candidate split count and keeps the one that finishes first once the
+// fp32 partials are charged: every split writes one fp32 copy of all four weight gradients,
+// which the reduction reads back.
+//
+// Greedy placement of k equal tiles of w stages on slots that free at times t: the tiles start at
+// the k smallest of the times t_i + j w (j >= 0), so a search for the k-th smallest start places
+// them all at once, whatever k is.
+void place_equal_tiles(std::vector<int64_t>& t, int64_t k, int64_t w) {
+  if (k <= 0) return;
+  auto starts_below = [&](int64_t T) {
+    int64_t c = 0;
+    for (int64_t x : t)
+      if (x < T) c += (T - x + w - 1) / w;
+    return c;
+  };
+  int64_t lo = *std::min_element(t.begin(), t.end()), hi = lo + (k - 1) * w;
+  while (lo < hi) {  // the k-th smallest start
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (starts_below(mid + 1) >= k) hi = mid; else lo = mid + 1;
+  }
+  int64_t rest = k - starts_below(lo);  // tiles that start exactly at lo
+  for (int64_t& x : t) {
+    int64_t c = x < lo ? (lo - x + w - 1) / w : 0;
+    if (rest > 0 && x <= lo && (lo - x) % w == 0) {
+      ++c;
+      --rest;
+    }
+    x += c * w;
+  }
+}
+
+struct SplitModel {
+  int64_t slots;        // workgroups resident at once over the 256 CUs
+  double stage_us;      // one K-stage of one tile on one slot
+  int64_t tile_extra;   // prologue and epilogue of a tile, in stages
+  double hbm_bytes_us;  // sustained HBM bytes per microsecond for the partials
+};
+
+double schedule_us(const SplitModel& m, int64_t tiles_per_split, int64_t splits, int64_t tps,
+                   int64_t M, int64_t ks, int64_t n_dx, int64_t dx_stages, int64_t wtot) {
+  std::vector<int64_t> t(size_t(m.slots), 0);
+  const int64_t last = M - (splits - 1) * tps;
+  place_equal_tiles(t, (splits - 1) * tiles_per_split, tps / ks + m.tile_extra);
+  place_equal_tiles(t, tiles_per_split, cdiv(last, ks) + m.tile_extra);
+  place_equal_tiles(t, n_dx, dx_stages + m.tile_extra);
+  const int64_t span = *std::max_element(t.begin(), t.end());
+  return double(span) * m.stage_us + double(splits) * double(wtot) * 8.0 / m.hbm_bytes_us;
+}
+
+// Tokens per split for a shape (a multiple of the stage's ks tokens); the last few answers are
+// kept, since the search costs a few milliseconds and a training loop repeats its shapes.
+int64_t pick_tps(int64_t M, int64_t d, int64_t e, int64_t s, flashgau_dtype dtype, int64_t xbt,
+                 int64_t ks) {
+  struct Entry { int64_t M, d, e, s, dtype, tps; };
+  static std::mutex mu;
+  static Entry cache[8];
+  static int next = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& c : cache)
+      if (c.tps && c.M == M && c.d == d && c.e == e && c.s == s && c.dtype == dtype) return c.tps;
+  }
+  // bf16: one 256 x 256 tile per CU at about half the CU's share of 2.5 PFLOP/s; fp32: three
+  // 64 x 64 tiles per CU sharing half its share of 157.3 TFLOP/s; partials at about 5 TB/s.
+  const bool bf = dtype == FLASHGAU_BF16;
+  const double stage_flops = 2.0 * double(xbt) * double(xbt) * double(ks);
+  const double cu_flops_us = (bf ? 2.5e9 : 157.3e6) / 256 * 0.5;
+  const int64_t per_cu = bf ? 1 : 3;
+  const SplitModel m{256 * per_cu, stage_flops / (cu_flops_us / double(per_cu)), 3, 5.0e6};
+  const int64_t tiles_per_split = 2 * cdiv(d, xbt) * cdiv(e, xbt) + cdiv(d, xbt) * cdiv(s, xbt) +
+                                  cdiv(e, xbt) * cdiv(d, xbt);
+  const int64_t wtot = 3 * d * e + d * s;
+  const int64_t n_dx = cdiv(d, xbt) * cdiv(M, xbt);
+  const int64_t dx_stages = 2 * cdiv(e, ks) + cdiv(s, ks);
+  const int64_t max_splits = std::min<int64_t>(64, cdiv(M, ks));
+  double best = 0.0;
+  int64_t best_tps = 0;
+  for (int64_t want = 1; want <= max_splits; ++want) {
+    const int64_t tps = cdiv(cdiv(M, want), ks) * ks;
+    if (cdiv(M, tps) != want) continue;  // the same ranges as a smaller count
+    const double t = schedule_us(m, tiles_per_split, want, tps, M, ks, n_dx, dx_stages, wtot);
+    if (best_tps == 0 || t < best) {
+      best = t;
+      best_tps = tps;
+    }
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  cache[next] = Entry{M, d, e, s, int64_t(dtype), best_tps};
+  next = (next + 1) % 8;
+  return best_tps;
+}
 
 int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
                flashgau_dtype dtype, BPlan* bp) {
@@ -809,14 +925,13 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
   }
   const int64_t M = f.M, nbg = f.nbg;
   bp->bt = dtype == FLASHGAU_BF16 ? BShapes<BF16>::BT : BShapes<F32>::BT;
-  const int64_t bt = bp->bt;
+  bp->xbt = dtype == FLASHGAU_BF16 ? XShapes<BF16>::BT : XShapes<F32>::BT;
+  const int64_t bt = bp->bt, xbt = bp->xbt;
   bp->slots = causal ? nbg : B;
-  const int64_t tiles_per_split = 2 * cdiv(d, bt) * cdiv(e, bt) + cdiv(d, bt) * cdiv(s, bt) +
-                                  cdiv(e, bt) * cdiv(d, bt);
-  // token ranges of whole stage lengths (a multiple of the chunk, so also of 8)
-  const int64_t ks = kStageBytes / f.esz;
-  const int64_t splits0 = std::max<int64_t>(1, std::min<int64_t>(cdiv(M, ks), cdiv(kWgradTargetBlocks, tiles_per_split)));
-  bp->tps = cdiv(cdiv(M, splits0), ks) * ks;
+  const int64_t tiles_per_split = 2 * cdiv(d, xbt) * cdiv(e, xbt) + cdiv(d, xbt) * cdiv(s, xbt) +
+                                  cdiv(e, xbt) * cdiv(d, xbt);
+  const int64_t ks = kStageBytes / f.esz;  // tokens per K-stage
+  bp->tps = pick_tps(M, d, e, s, dtype, xbt, ks);
   bp->splits = cdiv(M, bp->tps);
   bp->nzb = cdiv(M, kZRows);
   const int64_t esz = f.esz;
@@ -852,7 +967,7 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
       nbg * nte * ntc,                                                        // mixb
       nbg * ntc * ntc + nbg * ntc * nts + B * f.ng * cdiv(s, bt) * cdiv(e, bt),  // dscores_states
       3 * nbg * ntc * nts + nbg * nte * ntc,                                  // dheads + dv
-      cdiv(d, bt) * cdiv(M, bt) + bp->splits * tiles_per_split,               // dx + wgrad
+      cdiv(d, xbt) * cdiv(M, xbt) + bp->splits * tiles_per_split,             // dx + wgrad
       cdiv(wtot / 4, 256),                                                    // reduce
       bp->nzb * cdiv(s / 2, 256),                                             // dz
   };
@@ -962,7 +1077,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   const T* dOp = reinterpret_cast<const T*>(dO);
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
   const int nbg = int(pl.nbg), G = int(pl.G), B = int(pl.B);
-  const int bt = int(bp.bt);
+  const int bt = int(bp.bt), xbt = int(bp.xbt);
   const bool lin = !(causal && pl.G == 1);
   const int rope = rope_base > 0.0f ? 1 : 0;
   const double log2_base = rope ? log2(double(rope_base)) : 0.0;
@@ -1034,7 +1149,7 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     const int Fb[4] = {e, e, s, d};
     int total = 0;
     for (int i = 0; i < 4; ++i) {
-      const int tm = int(cdiv(Fa[i], bt)), tn = int(cdiv(Fb[i], bt));
+      const int tm = int(cdiv(Fa[i], xbt)), tn = int(cdiv(Fb[i], xbt));
       a.job[i] = {As[i], Bs[i], part[i], Fa[i], Fb[i], tm, tn, total};
       total += int(bp.splits) * tm * tn;
     }
@@ -1045,8 +1160,8 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     DXArgs<E> x{reinterpret_cast<const T*>(W_u), reinterpret_cast<const T*>(W_v),
                 reinterpret_cast<const T*>(W_z), R(BR_DHUR), R(BR_DHVR), R(BR_DHZR),
                 reinterpret_cast<T*>(dX), M, d, e, s};
-    const int64_t n_dx = cdiv(d, bt) * cdiv(M, bt);
-    hipLaunchKernelGGL(dx_wgrad_kernel<E>, dim3(unsigned(total + n_dx)), dim3(kThreads), 0, stream,
+    const int64_t n_dx = cdiv(d, xbt) * cdiv(M, xbt);
+    hipLaunchKernelGGL(dx_wgrad_kernel<E>, dim3(unsigned(total + n_dx)), dim3(XGemm<E>::kThreads), 0, stream,
                        x, a, total, int(n_dx));
   }
   // ---- reductions

@@ -28,8 +28,9 @@ namespace {
 //
 // Operand layouts (AL for A, BL for B): kLayoutK (the default) stores each of the tile's rows with
 // its K elements contiguous; kLayoutMN stores the operand as K rows of M-contiguous elements (a
-// token-major tensor read with K = tokens, say). An MN tile is KS K-rows of BM elements, 256 bytes
-// each; it travels into LDS as straight 1 KB copies whose source chunks are permuted (below), and
+// token-major tensor read with K = tokens, say). An MN tile is one or more 256-byte column blocks,
+// each KS K-rows of 256 bytes, stored one after the other; it travels into LDS as straight 1 KB
+// copies whose source chunks are permuted (below), and
 // its fragments are read with the transposing LDS reads of CDNA4 (ds_read_b64_tr_b16: in every
 // 16-lane group, lane i's k-th element comes from lane i/4 + 4k at column offset i % 4), four
 // 4-byte reads per fragment for fp32.
@@ -53,8 +54,10 @@ struct TileGemm {
   static_assert(BM % 8 == 0, "A rows end on an 8-row boundary");
   static constexpr int KS = kStageBytes / E::kSize;  // K elements per stage
   static constexpr int kWM = WM, kWN = WN, kAL = AL, kBL = BL;
-  static_assert(AL == kLayoutK || BM * E::kSize == 256, "an MN-major A tile is 256 bytes wide");
-  static_assert(BL == kLayoutK || BN * E::kSize == 256, "an MN-major B tile is 256 bytes wide");
+  static_assert(AL == kLayoutK || (BM * E::kSize) % 256 == 0, "an MN-major A tile is 256-byte blocks");
+  static_assert(BL == kLayoutK || (BN * E::kSize) % 256 == 0, "an MN-major B tile is 256-byte blocks");
+  static constexpr int kMNSlabs = KS / 4;               // 1 KB slabs per 256-byte block of an MN tile
+  static constexpr int kMNBlk = 256 / (16 * E::kSize);  // 16-element fragment blocks per 256 bytes
 
   // Chunk swizzle of an MN tile's K row p (even, so the two chunks of a 16-element fragment row
   // stay adjacent): the 8 K rows one transposing read serves per half-wave (p = 8g + r, r < 4,
@@ -76,9 +79,10 @@ struct TileGemm {
   // slab of the stage (A's slabs first, then B's). K-major operand: ka is the byte offset along K;
   // slab s holds rows [8s, 8s+8), lane l fetches row + l/8, logical chunk (l % 8) ^ (l / 8), which
   // lands at physical chunk l % 8: the XOR-swizzled layout. MN-major operand: ka is the first K
-  // row; slab s holds K rows [4s, 4s+4), lane l fetches K row 4s + l/16, logical chunk
-  // (l % 16) ^ mn_swizzle(row), landing at physical chunk l % 16; src.kbytes bounds the valid
-  // M bytes of a row, and rows past the descriptor's range read as zeros.
+  // row; slab s fills column block s / kMNSlabs with its K rows [4r, 4r+4), r = s % kMNSlabs: lane
+  // l fetches K row 4r + l/16, logical chunk (l % 16) ^ mn_swizzle(row) of the block, landing at
+  // physical chunk l % 16; src.kbytes bounds the valid M bytes of a row, and rows past the
+  // descriptor's range read as zeros.
   __device__ __forceinline__ static void issue(u32x4* lds, int stage, const Src& a, int ka,
                                                const Src& b, int kb, int wave, int lane) {
     const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds)) + uint32_t(stage * kStage) * 16;
@@ -91,8 +95,8 @@ struct TileGemm {
       const int slab = is_a ? rg : rg - BM / 8;
       uint32_t voff;
       if ((is_a ? AL : BL) == kLayoutMN) {
-        const int row = slab * 4 + (lane >> 4);
-        const int col = ((lane & 15) ^ mn_swizzle(row)) * 16;
+        const int row = (slab % kMNSlabs) * 4 + (lane >> 4);
+        const int col = (slab / kMNSlabs) * 256 + ((lane & 15) ^ mn_swizzle(row)) * 16;
         voff = col < src.kbytes ? uint32_t((is_a ? ka : kb) + row) * src.ld + uint32_t(col) : kOutOfRange;
       } else {
         const int row = slab * 8 + (lane >> 3);
@@ -113,8 +117,8 @@ struct TileGemm {
     } else if constexpr (sizeof(typename E::T) == 2) {
       // K rows 32 ks + 8 q + lr/4 (+4), 8 bytes at column 16 blk + 4 (lr % 4)
       typedef short v4i16 __attribute__((ext_vector_type(4)));
-      const char* base = reinterpret_cast<const char*>(R);
-      const int cb = blk * 32 + 8 * (lr & 3);  // byte within the 256-byte K row
+      const char* base = reinterpret_cast<const char*>(R) + (blk / kMNBlk) * (KS * 256);
+      const int cb = (blk % kMNBlk) * 32 + 8 * (lr & 3);  // byte within the block's K row
       const int p0 = 32 * ks + 8 * q + (lr >> 2);
       const int p1 = p0 + 4;
       const char* a0 = base + p0 * 256 + ((((cb >> 4) ^ mn_swizzle(p0)) << 4) | (cb & 15));
@@ -127,8 +131,8 @@ struct TileGemm {
       return u32x4{w0[0], w0[1], w1[0], w1[1]};
     } else {
       // fp32: the four K rows 16 ks + 4 q + c of column 16 blk + lr
-      const char* base = reinterpret_cast<const char*>(R);
-      const int cb = blk * 64 + 4 * lr;
+      const char* base = reinterpret_cast<const char*>(R) + (blk / kMNBlk) * (KS * 256);
+      const int cb = (blk % kMNBlk) * 64 + 4 * lr;
       u32x4 r;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -284,40 +288,48 @@ struct TileGemm {
 
   // The same for results contiguous along the tile's columns: staged as [row][col] rows of WTN
   // elements (element-wise LDS writes), handed out as emit(row, col, chunk) with col a multiple
-  // of 16/sizeof(T).
-  template <class T, class Conv, class Emit>
+  // of 16/sizeof(T). With PASSES > 1 the wave's rows go through its region in that many slices
+  // (for wave tiles whose staged copy would not fit the LDS tiles).
+  template <class T, int PASSES = 1, class Conv, class Emit>
   __device__ __forceinline__ void stage_cols(u32x4* lds, int wave, int wm, int wn, int lane,
                                              Conv&& conv, Emit&& emit) const {
+    static_assert(TM % PASSES == 0, "passes split the fragment rows evenly");
+    constexpr int kTMP = TM / PASSES;  // fragment rows per pass
+    constexpr int kRows = kTMP * 16;
     constexpr int kCpr = WTN * int(sizeof(T)) / 16;
-    constexpr int kRegionBytes = WTM * WTN * int(sizeof(T));
+    constexpr int kRegionBytes = kRows * WTN * int(sizeof(T));
     static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "staged row must be 2^k chunks");
     static_assert(WM * WN * kRegionBytes <= kLds * 16, "staging regions exceed the LDS tiles");
     char* region = reinterpret_cast<char*>(lds) + wave * kRegionBytes;
     const int lr = lane & 15;
     const int q = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = i * 16 + q * 4;
-        const int col = j * 16 + lr;
-        T v[4];
-        conv(i, j, wm * WTM + row, wn * WTN + col, acc[i][j], v);
-        const int byte = col * int(sizeof(T));
+      for (int ii = 0; ii < kTMP; ++ii)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int rr = row + k;
-          char* dst = region + rr * (kCpr * 16) + (((byte >> 4) ^ (rr & (kCpr - 1))) << 4) + (byte & 15);
-          *reinterpret_cast<T*>(dst) = v[k];
+        for (int j = 0; j < TN; ++j) {
+          const int i = ps * kTMP + ii;
+          const int row = ii * 16 + q * 4;  // pass-local
+          const int col = j * 16 + lr;
+          T v[4];
+          conv(i, j, wm * WTM + ps * kRows + row, wn * WTN + col, acc[i][j], v);
+          const int byte = col * int(sizeof(T));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rr = row + k;
+            char* dst = region + rr * (kCpr * 16) + (((byte >> 4) ^ (rr & (kCpr - 1))) << 4) + (byte & 15);
+            *reinterpret_cast<T*>(dst) = v[k];
+          }
         }
-      }
 #pragma unroll
-    for (int k = 0; k < WTM * kCpr / 64; ++k) {
-      const int idx = lane + k * 64;
-      const int row = idx / kCpr, ch = idx % kCpr;
-      const u32x4 chunk = *reinterpret_cast<const u32x4*>(
-          region + row * (kCpr * 16) + ((ch ^ (row & (kCpr - 1))) << 4));
-      emit(wm * WTM + row, wn * WTN + ch * (16 / int(sizeof(T))), chunk);
+      for (int k = 0; k < kRows * kCpr / 64; ++k) {
+        const int idx = lane + k * 64;
+        const int row = idx / kCpr, ch = idx % kCpr;
+        const u32x4 chunk = *reinterpret_cast<const u32x4*>(
+            region + row * (kCpr * 16) + ((ch ^ (row & (kCpr - 1))) << 4));
+        emit(wm * WTM + ps * kRows + row, wn * WTN + ch * (16 / int(sizeof(T))), chunk);
+      }
     }
   }
 
