@@ -25,7 +25,8 @@
 // reads its token-major operands as MN-major tiles (K rows of M-contiguous elements, fragments
 // through the transposing LDS reads), so every intermediate is stored once, token-major, and
 // nothing is transposed in memory. Tiles are 128 x 128 with 8 waves for bf16 and 64 x 64 with
-// 4 waves for fp32 (256-byte rows either way, as the MN-major tiles need).
+// 4 waves for fp32 (one 256-byte column block per MN-major operand), except the input and weight
+// gradients, which bf16 runs on 256 x 256 tiles (two column blocks).
 
 #include <mutex>
 #include <vector>
