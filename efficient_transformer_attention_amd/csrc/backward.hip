@@ -5,8 +5,9 @@
 // page motivates the chunked form by its parallel training and prints no gradient, so the steps
 // below are the chain rule of the forward's steps, in reverse order, for the loss Σ O ⊙ dO:
 //
-//   recompute  pack, proj (the gate's columns too, and the pre-activations), per-chunk scores P
-//              and the exclusive prefix states S_g / n (the forward's own kernels)
+//   recompute  pack, proj (also storing the pre-activations), H_u = X W_u on the output
+//              projection's GEMM, per-chunk scores P and the exclusive prefix states S_g / n (the
+//              forward's own kernels)
 //   mixb       per (chunk, value-column tile, token tile) two GEMMs into two accumulators:
 //              V̂ᵀ = [V_gᵀ | S_gᵀ][P_g | Q_lin,g]ᵀ and dYᵀ = W_o dOᵀ; epilogue, with H_u = X W_u from
 //              the projection: Y = U ⊙ V̂ (for dW_o), dV̂ = dY ⊙ U, dH_u = dY ⊙ V̂ ⊙ SiLU'(H_u)
@@ -981,9 +982,10 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
 }
 
 // ------------------------------------------------------------------------------ launches
-// The forward's intermediates as the backward reads them: pack, the projection over all three
-// weights (also storing H_u and H_v | H_z), scores and prefix states. `flash_gau_backward` runs this
-// first; `flash_gau_forward_train` runs it as part of a forward and leaves it in the workspace.
+// The forward's intermediates as the backward reads them: pack, the projection over W_v | W_z
+// (also storing the pre-activations H_v | H_z), the gate's pre-activations H_u, scores and prefix
+// states. `flash_gau_backward` runs this first; `flash_gau_forward_train` runs it as part of a
+// forward and leaves it in the workspace.
 template <class E>
 void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
                       const void* W_z, const float* gamma, const float* beta, const void* W_o,
@@ -1006,12 +1008,18 @@ void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const voi
   const float inv_n = float(1.0 / double(pl.n));
   launch_pack<E>(W_u, W_v, W_z, W_o, d, e, s, WcatT, WoT, stream);
   {
-    ProjArgs<E> a{Xp, WcatT, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
-                  int(pl.n), rope, log2_base, R(BR_HR), R(BR_HU)};
-    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(2 * e + s, S::kProjBN);
+    ProjArgs<E> a{Xp, WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
+                  int(pl.n), rope, log2_base, R(BR_HR)};
+    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(e + s, S::kProjBN);
     hipLaunchKernelGGL(
         (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, true>),
         dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
+  }
+  {
+    // the gate's pre-activations H_u = X W_u, token-major: the output projection's GEMM (and its
+    // large tiles) with W_uᵀ, the first e rows of the packed weights, in W_oᵀ's place and X in Y's
+    OutArgs<E> g{WcatT, Xp, R(BR_HU), M, e, d};
+    launch_out<E>(g, stream);
   }
   {
     ScoresArgs<E> sa{Qq, Kq, P, nbg, c, s, causal, 1.0f / float(c)};

@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs<E> args) {
 template <class E>
 struct ProjArgs {
   const typename E::T* X;     // [M, d]
-  const typename E::T* WvzT;  // [e+s, d]: rows of (W_v | W_z)ᵀ; EXTRA: [2e+s, d], (W_u | W_v | W_z)ᵀ
+  const typename E::T* WvzT;  // [e+s, d]: rows of (W_v | W_z)ᵀ
   typename E::T* Vt;          // [M/c, e, c]
   typename E::T* Qq;          // [M, s]
   typename E::T* Kq;          // [M, s]
@@ -490,21 +490,19 @@ struct ProjArgs {
   int n;             // sequence length: a token's position is its row modulo n
   int rope;          // rotate the four heads (rotary position embedding)
   double log2_base;  // log2 of the rotary base
-  // Written only by the EXTRA instantiation (the backward pass recomputes the projection, the
-  // gate's columns included, and also needs the pre-activations):
+  // Written only by the EXTRA instantiation (the backward pass recomputes the projection and
+  // also needs its pre-activations):
   typename E::T* Hr;  // [M, e+s]: X W_v | X W_z before SiLU
-  typename E::T* Hu;  // [M, e]: X W_u before SiLU
 };
 
 template <class E, int BM, int BN, int WM, int WN, int NS, bool EXTRA = false>
 __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   using G = TileGemm<E, BM, BN, WM, WN, NS>;
   __shared__ u32x4 lds[G::kLds];
-  // Columns: EXTRA starts with the e gate columns (cu = e); then V (e columns), then the s head
-  // features. hcols is the row pitch of the pre-activations Hr.
-  const int cu = EXTRA ? p.e : 0;
+  // Columns: V (e columns), then the s head features. hcols is the row pitch of the
+  // pre-activations Hr.
   const int hcols = p.e + p.s;
-  const int ncols = cu + p.e + p.s;
+  const int ncols = p.e + p.s;
   const int ntn = (ncols + BN - 1) / BN;
   const int ntm = (p.M + BM - 1) / BM;
   const int lid = xcd_remap(blockIdx.x, ntm * ntn);
@@ -519,7 +517,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   // 8-byte stores and the rotary pairs sit inside the lane. The tiles are square, so swapping
   // the operands is all it takes.
   static_assert(BM == BN, "transposed head tiles need square tiles");
-  const bool heads_t = n0 >= cu + p.e;
+  const bool heads_t = n0 >= p.e;
 
   G g;
   g.zero();
@@ -538,7 +536,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
   const int e = p.e, s = p.s, c = p.c;
   if (heads_t) {
     g.epilogue(wm, wn, lane, [&](int r, int cl, const f32x4& v) {
-      const int j = n0 - cu - e + r;  // first of four consecutive features (s % 8 == 0)
+      const int j = n0 - e + r;  // first of four consecutive features (s % 8 == 0)
       const int row = m0 + cl;        // token
       if (j >= s || row >= p.M) return;
       if constexpr (EXTRA) store4(p.Hr + int64_t(row) * hcols + e + j, v[0], v[1], v[2], v[3]);
@@ -574,32 +572,16 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
     return;
   }
   // A wave whose columns all fall in V stages its tile through LDS and writes full 16-byte runs
-  // of the chunk-transposed V (a wave of gate columns: token-major H_u); other waves store
-  // element-wise.
+  // of the chunk-transposed V; other waves store element-wise.
   const int wc0 = n0 + wn * G::WTN, wc1 = wc0 + G::WTN;
-  if constexpr (EXTRA) {
-    if (wc1 <= cu) {
-      g.template stage_cols<T>(lds, wave, wm, wn, lane,
-                               [&](int, int, int, int, const f32x4& v, T* out) {
-#pragma unroll
-                                 for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
-                               },
-                               [&](int r, int cl, const u32x4& chunk) {
-                                 const int row = m0 + r, col = n0 + cl;
-                                 if (row < p.M)
-                                   *reinterpret_cast<u32x4*>(p.Hu + int64_t(row) * e + col) = chunk;
-                               });
-      return;
-    }
-  }
-  if (wc0 >= cu && wc1 <= cu + e) {
+  if (wc1 <= e) {
     g.template stage_rows<T>(lds, wave, wm, wn, lane,
                              [&](int, int, int, int, const f32x4& v, T* out) {
 #pragma unroll
                                for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(v[k]));
                              },
                              [&](int cl, int r, const u32x4& chunk) {
-                               const int row = m0 + r, col = n0 + cl - cu;
+                               const int row = m0 + r, col = n0 + cl;
                                if (row >= p.M) return;
                                const int64_t bg = row / c, t = row % c;  // 8 rows, one chunk
                                store16_stream(p.Vt + (bg * e + col) * c + t, chunk);
@@ -611,7 +593,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
                                  for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
                                },
                                [&](int r, int cl, const u32x4& chunk) {
-                                 const int row = m0 + r, col = n0 + cl - cu;
+                                 const int row = m0 + r, col = n0 + cl;
                                  if (row < p.M)
                                    *reinterpret_cast<u32x4*>(p.Hr + int64_t(row) * hcols + col) = chunk;
                                });
@@ -631,14 +613,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
     }
     if (row >= p.M || gcol >= ncols) return;
     const int64_t bg = row / c, t = row % c;  // c % 8 == 0: rows row..row+3 share a chunk
-    if constexpr (EXTRA) {
-      if (gcol < cu) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p.Hu[int64_t(row + k) * e + gcol] = from_f32<E>(v[k]);
-        return;
-      }
-    }
-    const int col = gcol - cu;  // V column, or e + head feature
+    const int col = gcol;  // V column, or e + head feature
     if constexpr (EXTRA) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) p.Hr[int64_t(row + k) * hcols + col] = from_f32<E>(v[k]);
