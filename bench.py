@@ -13,7 +13,7 @@ calls. `value` is tokens/s = B*n / (wall time of one step), timed over exactly -
 between two device synchronisations, with nothing else on the stream. Two separate passes follow
 outside the timed region: calls that record a HIP event before every kernel on the library's
 stream (per-kernel durations; the roofline object reports the kernel that takes the longest), and
-calls bracketed by events (`step_ms_quantiles`). The CPU baseline is the fp64 oracle timed on the
+at least 50 calls each bracketed by two events (`step_ms_quantiles`). The CPU baseline is the fp64 oracle timed on the
 host on one sequence of the same batch; its output also checks the GPU's on that sequence.
 
 `configs` holds one row per workload of inputs.WORKLOADS (the eight configurations, the headline
@@ -702,7 +702,7 @@ def main():
           file=sys.stderr, flush=True)
     head, O = measure_forward(fg, torch, dev, inp, args.steps, args.warmup, args.settle_ms,
                               kernel_steps=max(10, min(args.steps, 50)),
-                              quantile_steps=max(10, args.steps))
+                              quantile_steps=max(50, args.steps))
     print("[bench] timed region done", file=sys.stderr, flush=True)
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "compute_units": props.multi_processor_count,
