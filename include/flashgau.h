@@ -311,7 +311,9 @@ int flash_gau_decode_step(const void* x, const void* packed, size_t packed_bytes
  * call), accumulates every product in fp32 and rounds intermediates and results to dtype. */
 
 /* Bytes of device workspace flash_gau_backward needs (host-only; same validation as
- * flash_gau_forward; 0 for an empty problem). Returns FLASHGAU_OK or an error code. */
+ * flash_gau_forward; 0 for an empty problem). The size is a fixed function of the arguments: it
+ * includes one fp32 copy of the weight gradients per token range of their split-K sum, and the
+ * range count is chosen per shape. Returns FLASHGAU_OK or an error code. */
 int flashgau_backward_workspace_size(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                                      int64_t chunk, int causal, flashgau_dtype dtype,
                                      size_t* out_bytes);
@@ -340,7 +342,8 @@ int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const vo
 /* Training without the backward's recompute: flash_gau_forward_train computes O exactly as
  * flash_gau_forward_rope / flash_gau_forward do (rope_base 0: none) and also leaves in the
  * workspace (at least flashgau_backward_workspace_size() bytes) everything the backward reads of
- * the forward: the projection over W_u | W_v | W_z with its pre-activations, the heads, the scores,
+ * the forward: the projection over W_v | W_z with its pre-activations, the gate's pre-activations
+ * X W_u, the heads, the scores,
  * the prefix states and the gated mix Y = U ⊙ (V̂_quad + V̂_lin). Its mix stage reads the stored X W_u instead of running the gate's GEMM, so
  * O may differ from flash_gau_forward's in the last bf16 bit (same tolerance to the exact result).
  * flash_gau_backward_saved then returns the gradients flash_gau_backward would (bitwise the same),
