@@ -711,8 +711,9 @@ __device__ __forceinline__ void wgrad_block(const WArgs<E>& p, u32x4* lds, int l
   const int ntok = min(p.M, tbeg + p.tps) - tbeg;
   const Src a = make_src_mn(J.A, tbeg, J.Fa, E::kSize, ntok, m0, J.Fa - m0);
   const Src b = make_src_mn(J.B, tbeg, J.Fb, E::kSize, ntok, n0, J.Fb - n0);
-  gemm_to_f32<G, XShapes<E>::kPasses>(lds, a, 0, b, 0, ksteps<E>(ntok), J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0,
-                 J.Fb, J.Fa - m0, J.Fb - n0);
+  float* const out = J.out + int64_t(q) * J.Fa * J.Fb + int64_t(m0) * J.Fb + n0;
+  gemm_to_f32<G, XShapes<E>::kPasses>(lds, a, 0, b, 0, ksteps<E>(ntok), out, J.Fb, J.Fa - m0,
+                                      J.Fb - n0);
 }
 
 // One launch for the input and weight gradients, which read the same finished inputs: the
@@ -870,7 +871,7 @@ double schedule_us(const SplitModel& m, int64_t tiles_per_split, int64_t splits,
 }
 
 // Tokens per split for a shape (a multiple of the stage's ks tokens); the last few answers are
-// kept, since the search costs a few milliseconds and a training loop repeats its shapes.
+// kept, since the search takes up to about a millisecond and a training loop repeats its shapes.
 int64_t pick_tps(int64_t M, int64_t d, int64_t e, int64_t s, flashgau_dtype dtype, int64_t xbt,
                  int64_t ks) {
   struct Entry { int64_t M, d, e, s, dtype, tps; };
