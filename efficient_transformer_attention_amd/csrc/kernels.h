@@ -1150,13 +1150,16 @@ template <> struct Shapes<BF16> {
   // taken when its tile count fills the CUs' rounds better (launch_out)
   static constexpr bool kOutBig = true;
 };
+// fp32 runs the small problems (its matrix rate is a sixteenth of bf16's): 64 x 64 tiles for the
+// projections and the mix stage spread one call's work over four times the workgroups of 128 x 128
+// tiles.
 template <> struct Shapes<F32> {
-  static constexpr int kProjBM = 128, kProjBN = 128, kProjWM = 2, kProjWN = 2, kProjNS = 3;
+  static constexpr int kProjBM = 64, kProjBN = 64, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2, kScoresNS = 3;
   static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesNS = 3;
-  static constexpr int kMixBM = 128, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
-  static constexpr int kOutBM = 128, kOutBN = 128, kOutWM = 2, kOutWN = 2, kOutNS = 3;
+  static constexpr int kMixBM = 64, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
+  static constexpr int kOutBM = 64, kOutBN = 64, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
   static constexpr bool kOutBig = false;
 };
@@ -1280,6 +1283,14 @@ template <class E>
 void launch_out(const OutArgs<E>& a, hipStream_t stream) {
   using S = Shapes<E>;
   if constexpr (S::kOutBig) {
+    if (cdiv(a.d, S::kOutBM) * cdiv(a.M, S::kOutBN) < kCUs) {
+      // too few 256 x 128 tiles to give every CU one: 128 x 128 tiles, two per CU, twice the
+      // workgroups for the same work
+      const int64_t nb = cdiv(a.d, 128) * cdiv(a.M, 128);
+      hipLaunchKernelGGL((out_kernel<E, 128, 128, 2, 4, 2, false>), dim3(unsigned(nb)), dim3(512), 0,
+                         stream, a);
+      return;
+    }
     if (out_big_tiles(a.M, a.d, true)) {
       const int64_t nb = cdiv(a.d, 256) * cdiv(a.M, 256);
       hipLaunchKernelGGL((out_kernel<E, 256, 256, 2, 4, 2, false, true>), dim3(unsigned(nb)),
