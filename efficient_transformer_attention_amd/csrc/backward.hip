@@ -1011,10 +1011,7 @@ void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const voi
   {
     ProjArgs<E> a{Xp, WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt, gamma, beta, M, d, e, s, c,
                   int(pl.n), rope, log2_base, R(BR_HR)};
-    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(e + s, S::kProjBN);
-    hipLaunchKernelGGL(
-        (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, true>),
-        dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
+    launch_proj<E, true>(a, stream);
   }
   {
     // the gate's pre-activations H_u = X W_u, token-major: the output projection's GEMM (and its

@@ -99,9 +99,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     ProjArgs<E> a{reinterpret_cast<const T*>(X), WcatT + int64_t(e) * d, Vt, Qq, Kq, Ql, Klt,
                   gamma, beta, M, d, e, s, c, int(pl.n), rope_base > 0.0f ? 1 : 0,
                   rope_base > 0.0f ? log2(double(rope_base)) : 0.0};
-    const int64_t nb = cdiv(M, S::kProjBM) * cdiv(e + s, S::kProjBN);
-    hipLaunchKernelGGL((proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS>),
-                       dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
+    launch_proj<E>(a, stream);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   // Causal with a single chunk: the only chunk reads an empty prefix, so there is no global

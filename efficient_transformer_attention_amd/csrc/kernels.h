@@ -1304,6 +1304,27 @@ void launch_out(const OutArgs<E>& a, hipStream_t stream) {
                      dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
 }
 
+// The projection: 128 x 128 tiles, two workgroups per CU; a bf16 problem whose 128 x 128 tiles
+// would not fill that first round of the CUs takes 64 x 64 tiles of four waves instead (four
+// times the workgroups for the same work).
+template <class E, bool EXTRA = false>
+void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
+  using S = Shapes<E>;
+  const int64_t ncols = int64_t(a.e) + a.s;
+  if constexpr (S::kProjBM == 128) {
+    if (cdiv(a.M, 128) * cdiv(ncols, 128) < 2 * kCUs) {
+      const int64_t nb = cdiv(a.M, 64) * cdiv(ncols, 64);
+      hipLaunchKernelGGL((proj_kernel<E, 64, 64, 2, 2, 3, EXTRA>), dim3(unsigned(nb)), dim3(256), 0,
+                         stream, a);
+      return;
+    }
+  }
+  const int64_t nb = cdiv(a.M, S::kProjBM) * cdiv(ncols, S::kProjBN);
+  hipLaunchKernelGGL(
+      (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, EXTRA>),
+      dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
+}
+
 // pack: (W_u | W_v | W_z)ᵀ into WcatT [2e+s, d] and W_oᵀ into WoT [d, e], one launch.
 template <class E>
 void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* W_o, int d, int e,
