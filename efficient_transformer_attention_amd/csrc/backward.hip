@@ -1044,7 +1044,6 @@ int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const 
                          const void* W_z, const float* gamma, const float* beta, const void* W_o,
                          int causal, float rope_base, void* O, char* ws, hipStream_t stream) {
   using T = typename E::T;
-  using S = Shapes<E>;
   const Plan& pl = bp.f;
   auto W = [&](int r) { return reinterpret_cast<T*>(ws + pl.off[r]); };
   auto R = [&](int r) { return reinterpret_cast<T*>(ws + bp.off[r]); };
@@ -1055,9 +1054,7 @@ int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const 
     MixArgs<E> a{W(FLASHGAU_WS_VT), W(FLASHGAU_WS_ST), W(FLASHGAU_WS_P), W(FLASHGAU_WS_QL),
                  reinterpret_cast<const T*>(X), W(FLASHGAU_WS_WCAT_T), W(FLASHGAU_WS_Y), d,
                  int(pl.nbg), int(pl.G), c, e, s, causal, int(lin), R(BR_HU)};
-    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
-    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS, true>),
-                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+    launch_mix<E, true>(a, stream);
   }
   {
     OutArgs<E> a{W(FLASHGAU_WS_WO_T), W(FLASHGAU_WS_Y), reinterpret_cast<T*>(O), M, d, e};

@@ -128,9 +128,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
   {
     MixArgs<E> a{Vt, St, P, Ql, reinterpret_cast<const T*>(X), WcatT, Y, d, int(pl.nbg),
                  int(pl.G), c, e, s, causal, int(lin)};
-    const int64_t nb = pl.nbg * cdiv(e, S::kMixBM) * cdiv(c, S::kMixBN);
-    hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS>),
-                       dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+    launch_mix<E>(a, stream);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {

@@ -1325,6 +1325,16 @@ void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
       dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
 }
 
+// The mix stage, one workgroup per (chunk, value-column tile, token tile). (64-column tiles of
+// four waves for problems that leave CUs idle measured no faster.)
+template <class E, bool HU = false>
+void launch_mix(const MixArgs<E>& a, hipStream_t stream) {
+  using S = Shapes<E>;
+  const int64_t nb = int64_t(a.nbg) * cdiv(a.e, S::kMixBM) * cdiv(a.c, S::kMixBN);
+  hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS, HU>),
+                     dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
+}
+
 // pack: (W_u | W_v | W_z)ᵀ into WcatT [2e+s, d] and W_oᵀ into WoT [d, e], one launch.
 template <class E>
 void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* W_o, int d, int e,
