@@ -1151,12 +1151,12 @@ template <> struct Shapes<BF16> {
   static constexpr bool kOutBig = true;
 };
 // fp32 runs the small problems (its matrix rate is a sixteenth of bf16's): 64 x 64 tiles for the
-// projections and the mix stage spread one call's work over four times the workgroups of 128 x 128
-// tiles.
+// projections, the states and the mix stage spread one call's work over four times the workgroups
+// of 128 x 128 tiles.
 template <> struct Shapes<F32> {
   static constexpr int kProjBM = 64, kProjBN = 64, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2, kScoresNS = 3;
-  static constexpr int kStatesBM = 128, kStatesBN = 128, kStatesWM = 2, kStatesWN = 2;
+  static constexpr int kStatesBM = 64, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesNS = 3;
   static constexpr int kMixBM = 64, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
   static constexpr int kOutBM = 64, kOutBN = 64, kOutWM = 2, kOutWN = 2, kOutNS = 3;
@@ -1175,10 +1175,6 @@ constexpr bool scores_cover_mix() {
 static_assert(scores_cover_mix<BF16>() && scores_cover_mix<F32>(),
               "unwritten causal P tiles could be read by the mix stage");
 
-// The host plan sizes the chunk groups of the states stage with a 128 x 128 tile.
-static_assert(Shapes<BF16>::kStatesBM == 128 && Shapes<BF16>::kStatesBN == 128 &&
-                  Shapes<F32>::kStatesBM == 128 && Shapes<F32>::kStatesBN == 128,
-              "states tile differs from the host plan");
 
 // ------------------------------------------------------------------------------ host side
 struct Plan {
@@ -1193,7 +1189,13 @@ struct Plan {
 constexpr int64_t kMaxScoreElems = int64_t(1) << 33;
 
 // states tile (both element types) and the workgroup count the chunk grouping aims for
-constexpr int64_t kStatesTileM = 128, kStatesTileN = 128, kStatesTargetBlocks = 2048;
+constexpr int64_t kStatesTargetBlocks = 2048;
+
+// The states stage's tile (state rows x value columns) for an element size.
+inline void states_tile(int64_t esz, int64_t* tm, int64_t* tn) {
+  *tm = esz == 2 ? Shapes<BF16>::kStatesBM : Shapes<F32>::kStatesBM;
+  *tn = esz == 2 ? Shapes<BF16>::kStatesBN : Shapes<F32>::kStatesBN;
+}
 
 int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk, int causal,
               flashgau_dtype dtype, Plan* p) {
@@ -1213,7 +1215,9 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   if (d > kInt32Max || p->ncols > kInt32Max || chunk > kInt32Max) return FLASHGAU_ERR_BAD_SHAPE;
   // About two thousand states workgroups: enough chunk groups to fill the chip many times over.
   {
-    const int64_t base = B * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN);
+    int64_t tm, tn;
+    states_tile(p->esz, &tm, &tn);
+    const int64_t base = B * cdiv(s, tm) * cdiv(e, tn);
     int64_t ng = base > 0 ? cdiv(kStatesTargetBlocks, base) : 1;
     ng = std::max<int64_t>(1, std::min<int64_t>(ng, std::max<int64_t>(p->G, 1)));
     p->gs = p->G > 0 ? cdiv(p->G, ng) : 1;
@@ -1252,7 +1256,7 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   // Grid sizes of every launch (the largest tile counts use the smallest tiles).
   const int64_t grids[] = {
       cdiv(M, 128) * cdiv(p->ncols, 128),
-      p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64) + kXcds + B * p->ng * cdiv(s, kStatesTileM) * cdiv(e, kStatesTileN),
+      p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64) + kXcds + B * p->ng * cdiv(s, 64) * cdiv(e, 64),
       cdiv(B * e * s / 8, 256),
       p->nbg * cdiv(e, 128) * cdiv(chunk, 64),
       cdiv(d, 128) * cdiv(M, 128),
