@@ -1150,16 +1150,17 @@ template <> struct Shapes<BF16> {
   // taken when its tile count fills the CUs' rounds better (launch_out)
   static constexpr bool kOutBig = true;
 };
-// fp32 runs the small problems (its matrix rate is a sixteenth of bf16's): 64 x 64 tiles for the
-// projections, the states and the mix stage spread one call's work over four times the workgroups
-// of 128 x 128 tiles.
+// fp32's matrix rate is a sixteenth of bf16's, so its tiles can be small without the LDS becoming
+// the limit: 32 x 32 projection and output tiles, 32 (value columns) x 64 (tokens) mix tiles and
+// 64 x 64 state tiles spread a call's work over many more workgroups than 128 x 128 tiles do (the
+// fp32 configuration, B = 1, n = 512, gave its output GEMM 8 workgroups with those).
 template <> struct Shapes<F32> {
-  static constexpr int kProjBM = 64, kProjBN = 64, kProjWM = 2, kProjWN = 2, kProjNS = 3;
+  static constexpr int kProjBM = 32, kProjBN = 32, kProjWM = 2, kProjWN = 2, kProjNS = 3;
   static constexpr int kScoresBT = 64, kScoresWM = 2, kScoresWN = 2, kScoresNS = 3;
   static constexpr int kStatesBM = 64, kStatesBN = 64, kStatesWM = 2, kStatesWN = 2;
   static constexpr int kStatesNS = 3;
-  static constexpr int kMixBM = 64, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
-  static constexpr int kOutBM = 64, kOutBN = 64, kOutWM = 2, kOutWN = 2, kOutNS = 3;
+  static constexpr int kMixBM = 32, kMixBN = 64, kMixWM = 2, kMixWN = 2, kMixNS = 3;
+  static constexpr int kOutBM = 32, kOutBN = 32, kOutWM = 2, kOutWN = 2, kOutNS = 3;
   static constexpr bool kOutPrio = false;
   static constexpr bool kOutBig = false;
 };
@@ -1254,12 +1255,21 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   }
   p->total = off;
   // Grid sizes of every launch (the largest tile counts use the smallest tiles).
+  // launch grids at the smallest tiles each stage takes for this dtype (bf16's smaller projection
+  // and output tiles serve only problems of a few hundred tiles)
+  const bool f32 = p->esz == 4;
+  const int64_t pt = f32 ? Shapes<F32>::kProjBM : Shapes<BF16>::kProjBM;
+  const int64_t mt = f32 ? Shapes<F32>::kMixBM : Shapes<BF16>::kMixBM;
+  const int64_t mn = f32 ? Shapes<F32>::kMixBN : Shapes<BF16>::kMixBN;
+  const int64_t ot = f32 ? Shapes<F32>::kOutBN : 128;
+  static_assert(Shapes<F32>::kProjBM == Shapes<F32>::kProjBN && Shapes<F32>::kOutBM == Shapes<F32>::kOutBN,
+                "square fp32 projection and output tiles");
   const int64_t grids[] = {
-      cdiv(M, 128) * cdiv(p->ncols, 128),
+      cdiv(M, pt) * cdiv(p->ncols, pt),
       p->nbg * cdiv(chunk, 64) * cdiv(chunk, 64) + kXcds + B * p->ng * cdiv(s, 64) * cdiv(e, 64),
       cdiv(B * e * s / 8, 256),
-      p->nbg * cdiv(e, 128) * cdiv(chunk, 64),
-      cdiv(d, 128) * cdiv(M, 128),
+      p->nbg * cdiv(e, mt) * cdiv(chunk, mn),
+      cdiv(std::max(d, e), ot) * cdiv(M, ot),  // the output GEMM, and the backward's H_u = X W_u
   };
   for (int64_t g : grids)
     if (g > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
