@@ -21,7 +21,9 @@
  * Conventions shared by every entry point
  *   - All tensors are dense row-major; every device pointer is memory owned by the caller.
  *   - The library never allocates, frees or synchronises. Its only mutable global state is the
- *     per-device address of flash_gau_forward_noalloc's scratch array, set once per device.
+ *     per-device address of flash_gau_forward_noalloc's scratch array, set once per device, and
+ *     a small host-side cache of the backward's split plans per shape (mutex-guarded; it changes
+ *     no result, only how soon a plan is found).
  *   - flash_gau_forward enqueues its kernels on `hip_stream` (NULL = the null stream) and returns
  *     at once. Faults inside a kernel surface at the caller's next synchronisation.
  *   - Every argument is validated on the host before the first launch; on any error nothing has
