@@ -140,6 +140,30 @@ def test_backward_full_size_through_sequence_zero(name):
         assert errs[k] <= TOL[dtype], (k, errs[k])
 
 
+@pytest.mark.parametrize("name,t0", [("c3_causal_bf16_n4096", 1000), ("c3_causal_bf16_n4096", 3584)])
+def test_backward_causality_full_size(name, t0):
+    # Causal: O[t] depends on X[t'] for t' <= t only, so with dO zero from token t0 on, dX from t0
+    # on is exactly zero: every contribution to it is a product with a zero of dO (through the
+    # chunk's own attention, its state and the gate). t0 = 1000 falls inside a chunk (c = 256),
+    # 3584 on a chunk boundary; the run is the benchmark's launch configuration at full size.
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
+    assert causal
+    print(f"[gpu case] backward causality {name} t0={t0}", flush=True)
+    inp = gen.workload_inputs(name, seed=1)
+    dO = gen.make_output_grad(B, n, d, dtype, seed=1)
+    dO[:, t0:] = 0.0
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    grads = fg.flash_gau_backward(*args, _dev(dO, dtype), c, causal)
+    torch.cuda.synchronize()
+    dX = grads["dX"].float()
+    assert float(dX[:, t0:].abs().max()) == 0.0
+    assert float(dX[:, t0 - 1].abs().max()) > 0.0  # the token before t0 still has a gradient
+    for k in fg.GRAD_NAMES:
+        assert bool(torch.isfinite(grads[k].float()).all()), k
+
+
 def test_forward_and_backward_replayed_from_a_hip_graph_match_eager():
     # One forward and one backward captured into a HIP graph (torch.cuda.CUDAGraph) on a side
     # stream; every replay must reproduce the eager outputs bitwise. Neither path records a memset.

@@ -158,9 +158,11 @@ def test_stage_parity(name):
 
 
 @pytest.mark.parametrize("name,t", [("c2_causal_bf16", 300), ("ragged_causal_fp32", 100),
-                                    ("many_chunks_causal_bf16", 517)])
+                                    ("many_chunks_causal_bf16", 517),
+                                    ("c3_causal_bf16_n4096", 2900)])
 def test_causal_output_ignores_future_tokens(name, t):
-    B, n, d, e, s, c, causal, dtype = SMALL[name]
+    # (the last case runs the headline configuration at full size)
+    B, n, d, e, s, c, causal, dtype = SMALL[name] if name in SMALL else gen.WORKLOADS[name]
     _announce(f"{name} causality t={t}")
     inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=4)
     O1 = run_gpu(inp)
