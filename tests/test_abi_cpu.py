@@ -332,6 +332,35 @@ def test_backward_workspace_holds_the_forward_layout_first():
     assert fg.backward_workspace_size(0, 128, 64, 128, 128, 64, True, fg.BF16) == 0
 
 
+def test_backward_split_plan_is_quick_and_stable():
+    # The backward splits its weight-gradient sums into token ranges chosen on the host (a replay
+    # of the launch's tile schedule per candidate count). For any shape the choice must come back
+    # quickly, hold at least one fp32 copy of the weight gradients, and be the same when asked
+    # again (the second answer comes from the library's per-shape cache).
+    import random
+    import time
+    rng = random.Random(0)
+    seen = 0
+    for _ in range(80):
+        c = 8 * rng.randint(1, 64)
+        n = c * rng.randint(1, 64)
+        B = rng.randint(1, 16)
+        d, e, s = (8 * rng.randint(1, 256) for _ in range(3))
+        dt = rng.choice([fg.BF16, fg.F32])
+        causal = rng.random() < 0.5
+        t0 = time.perf_counter()
+        try:
+            bwd = fg.backward_workspace_size(B, n, d, e, s, c, causal, dt)
+        except fg.FlashGauError:
+            continue
+        assert time.perf_counter() - t0 < 0.25
+        seen += 1
+        fwd = fg.workspace_size(B, n, d, e, s, c, causal, dt)
+        assert bwd >= fwd + 4 * (3 * d * e + d * s)
+        assert fg.backward_workspace_size(B, n, d, e, s, c, causal, dt) == bwd
+    assert seen >= 60
+
+
 @pytest.mark.parametrize("shape,code", [
     ((1, 100, 64, 128, 128, 64), fg.ERR_BAD_SHAPE),   # chunk does not divide n
     ((1, 128, 60, 128, 128, 64), fg.ERR_UNSUPPORTED),  # d not a multiple of 8
