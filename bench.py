@@ -411,7 +411,54 @@ def decode_measure(inp, dtype, torch, fg, dev, cpu_seconds):
         rec["cpu_baseline"] = {"value": round(B / med, 1), "unit": "tokens/s", "kind": "oracle",
                                "sample": f"fp64 oracle decode_step for the same {B} sequences, "
                                          f"median of {len(times)} steps ({med * 1e3:.1f} ms each)"}
+    rec["batch_sweep"] = [decode_batch_point(Bx, n, d, e, s, c, dtype, torch, fg, dev)
+                          for Bx in (32, 128)]
     return rec
+
+
+def decode_batch_point(B, n, d, e, s, c, dtype, torch, fg, dev):
+    """The same decoding step at a larger batch (the widths and sequence length of the workload,
+    seeded synthetic tokens and weights for 2c positions): one chunk untimed, one chunk timed between
+    HIP events. The weights are read once per step whatever the batch, so the HBM fraction grows
+    with B until the state and cache reads dominate."""
+    from efficient_transformer_attention_amd import inputs as gen
+    inp = gen.make_inputs(B, 2 * c, d, e, s, c, True, dtype, seed=11)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    esz = 2 if dtype == "bf16" else 4
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    packed = fg.pack_weights(*[up(a) for a in (inp.W_u, inp.W_v, inp.W_z, inp.W_o)])
+    gamma, beta = up(inp.gamma, torch.float32), up(inp.beta, torch.float32)
+    state = fg.DecodeState(B, d, e, s, c, tdt, dev)
+    xs = up(inp.X).transpose(0, 1).contiguous()
+    o = torch.empty((B, d), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+
+    def step(t):
+        rc = fg.decode_step_raw(xs[t].data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
+                                beta.data_ptr(), c, t, n, 0.0, B, d, e, s, dt, o.data_ptr(),
+                                state.buf.data_ptr(), state.buf.numel(), stream)
+        if rc != fg.OK:
+            raise fg.FlashGauError(rc, "flash_gau_decode_step")
+
+    for t in range(c):
+        step(t)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[0]), ctypes.c_void_p(stream))
+    for t in range(c, 2 * c):
+        step(t)
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.handles[1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    us_step = ev.ms(ev.handles[0], ev.handles[1]) * 1e3 / c
+    ev.close()
+    nbytes = sum(decode_bytes(B, d, e, s, c, esz, i) for i in range(c)) / c
+    achieved = nbytes / (us_step * 1e-6) / 1e9
+    return {"batch": B, "us_per_step": round(us_step, 2), "tokens_per_s": round(B / (us_step * 1e-6), 1),
+            "bytes_per_step": int(nbytes), "hbm_frac": round(achieved / HBM_PEAK, 4)}
 
 
 def time_forward(fg, torch, dev, B, n, d, e, s, c, causal, dtype, rope_base=None, steps=20,
