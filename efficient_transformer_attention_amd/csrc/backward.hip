@@ -744,48 +744,52 @@ struct RArgs {
   int njobs, splits;
 };
 
+// The last launch of the backward: blocks [0, nw) sum the split-K partials of the weight
+// gradients (four values per thread, the splits in order); blocks from nw on sum dγ, dβ [4, s]
+// each from the dz partials [nzb, 8, s] (16 outputs per block, 16 lanes per output each summing
+// every 16th partial, then a fixed-order sum of the 16). One launch instead of two: both read
+// only finished partials.
 template <class E>
-__global__ __launch_bounds__(256) void wreduce_kernel(RArgs<E> p, int64_t total4) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= total4) return;
-  RJob<E> J = p.job[0];
+__global__ __launch_bounds__(256) void reduce_kernel(RArgs<E> p, int64_t total4, int nw,
+                                                     const float* gbpart, int nzb, int s,
+                                                     float* dgamma, float* dbeta) {
+  __shared__ float red[16][16 + 1];
+  if (int(blockIdx.x) < nw) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= total4) return;
+    RJob<E> J = p.job[0];
 #pragma unroll
-  for (int i = 1; i < 4; ++i)
-    if (i < p.njobs && idx >= p.job[i].first4) J = p.job[i];
-  const int64_t i4 = idx - J.first4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < p.splits; ++q) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(J.part)[int64_t(q) * J.count4 + i4];
-    s[0] += v[0];
-    s[1] += v[1];
-    s[2] += v[2];
-    s[3] += v[3];
+    for (int i = 1; i < 4; ++i)
+      if (i < p.njobs && idx >= p.job[i].first4) J = p.job[i];
+    const int64_t i4 = idx - J.first4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < p.splits; ++q) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(J.part)[int64_t(q) * J.count4 + i4];
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    store4(J.out + i4 * 4, acc[0], acc[1], acc[2], acc[3]);
+    return;
   }
-  store4(J.out + i4 * 4, s[0], s[1], s[2], s[3]);
-}
-
-// dγ, dβ [4, s] each from the dz partials [nzb, 8, s]: 16 outputs per workgroup, 64 lanes per
-// output each summing every 64th partial (four loads in flight), then a fixed-order sum of the 64.
-__global__ __launch_bounds__(1024) void gbreduce_kernel(const float* gbpart, int nzb, int s,
-                                                       float* dgamma, float* dbeta) {
-  __shared__ float red[64][16 + 1];
   const int o = threadIdx.x & 15, l = threadIdx.x >> 4;
-  const int j = blockIdx.x * 16 + o;  // output index in [0, 8 s)
+  const int j = (int(blockIdx.x) - nw) * 16 + o;  // output index in [0, 8 s)
   const int64_t stride = int64_t(8) * s;
   float v = 0.0f;
   if (j < 8 * s) {
     int b = l;
-    for (; b + 192 < nzb; b += 256) {
-      const float x0 = gbpart[int64_t(b) * stride + j], x1 = gbpart[int64_t(b + 64) * stride + j];
-      const float x2 = gbpart[int64_t(b + 128) * stride + j], x3 = gbpart[int64_t(b + 192) * stride + j];
+    for (; b + 48 < nzb; b += 64) {
+      const float x0 = gbpart[int64_t(b) * stride + j], x1 = gbpart[int64_t(b + 16) * stride + j];
+      const float x2 = gbpart[int64_t(b + 32) * stride + j], x3 = gbpart[int64_t(b + 48) * stride + j];
       v += (x0 + x1) + (x2 + x3);
     }
-    for (; b < nzb; b += 64) v += gbpart[int64_t(b) * stride + j];
+    for (; b < nzb; b += 16) v += gbpart[int64_t(b) * stride + j];
   }
   red[l][o] = v;
   __syncthreads();
   if (l == 0 && j < 8 * s) {
-    for (int k = 1; k < 64; ++k) v += red[k][o];
+    for (int k = 1; k < 16; ++k) v += red[k][o];
     if (j < 4 * s)
       dgamma[j] = v;
     else
@@ -971,7 +975,7 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
       nbg * ntc * ntc + nbg * ntc * nts + B * f.ng * cdiv(s, bt) * cdiv(e, bt),  // dscores_states
       3 * nbg * ntc * nts + nbg * nte * ntc,                                  // dheads + dv
       cdiv(d, xbt) * cdiv(M, xbt) + bp->splits * tiles_per_split,             // dx + wgrad
-      cdiv(wtot / 4, 256),                                                    // reduce
+      cdiv(wtot / 4, 256) + cdiv(8 * s, 16),                                  // reduce
       bp->nzb * cdiv(s / 2, 256),                                             // dz
   };
   for (int64_t g : grids)
@@ -1179,10 +1183,9 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
     }
     a.njobs = 4;
     a.splits = int(bp.splits);
-    hipLaunchKernelGGL(wreduce_kernel<E>, dim3(unsigned(cdiv(first, 256))), dim3(256), 0, stream, a,
-                       first);
-    hipLaunchKernelGGL(gbreduce_kernel, dim3(unsigned(cdiv(8 * s, 16))), dim3(1024), 0, stream,
-                       Rf(BR_GBPART), int(bp.nzb), s, dgamma, dbeta);
+    const int64_t nw = cdiv(first, 256);
+    hipLaunchKernelGGL(reduce_kernel<E>, dim3(unsigned(nw + cdiv(8 * s, 16))), dim3(256), 0, stream,
+                       a, first, int(nw), Rf(BR_GBPART), int(bp.nzb), s, dgamma, dbeta);
   }
   return hipGetLastError() == hipSuccess ? FLASHGAU_OK : FLASHGAU_ERR_HIP;
 }
