@@ -1318,9 +1318,9 @@ void launch_out(const OutArgs<E>& a, hipStream_t stream) {
                      dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
 }
 
-// The projection: 128 x 128 tiles, two workgroups per CU; a bf16 problem whose 128 x 128 tiles
-// would not fill that first round of the CUs takes 64 x 64 tiles of four waves instead (four
-// times the workgroups for the same work).
+// The projection: bf16 on 128 x 128 tiles, two workgroups per CU, or, for a problem whose
+// 128 x 128 tiles would not fill that first round of the CUs, on 64 x 64 tiles of four waves (four
+// times the workgroups for the same work); fp32 on its own (small) tile.
 template <class E, bool EXTRA = false>
 void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
   using S = Shapes<E>;
