@@ -1,5 +1,5 @@
-// common.h — device and host helpers shared by the library's translation units (forward and
-// decode): vector types, element types and conversions, SiLU, the matrix-core step, buffer
+// common.h — device and host helpers shared by the library's translation units (forward,
+// backward and decode): vector types, element types and conversions, SiLU, the matrix-core step, buffer
 // descriptors, global-to-LDS copies, explicit memory waits, the XCD-aware tile order, and host-side
 // size and pointer checks. Everything has internal linkage: each translation unit gets its own
 // copy.

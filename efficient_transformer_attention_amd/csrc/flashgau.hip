@@ -7,8 +7,8 @@
 //   global Q_lin S_g / n with S_g = Σ K_lin_hᵀ V_h over all chunks (non-causal) or h < g (causal);
 //   O = [U ⊙ (V̂_quad + V̂_lin)] W_o.
 //
-// Every step is a dense contraction, so every kernel here is one tiled matrix-core GEMM with its
-// own operand sources and epilogue:
+// Every contraction runs as one tiled matrix-core GEMM with its own operand sources and epilogue;
+// pack and carry only move memory:
 //   pack    W_u|W_v|W_z and W_o transposed so that every GEMM reads K-contiguous rows
 //   proj    X [W_v|W_z]; epilogue SiLU, the four heads, V and K_lin written chunk-transposed
 //   scores_states  one launch of two roles: per chunk P = relu(Q_quad K_quadᵀ / c)² (zero above
@@ -24,7 +24,7 @@
 // Matrix-core mapping (CDNA4): bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses four
 // v_mfma_f32_16x16x4_f32. Operand tiles are staged in LDS as rows of 128 bytes (8 chunks of 16 B);
 // the 16-byte chunk index is XOR-swizzled with the row index so that both the row-wise fills and
-// the fragment reads of 16 consecutive rows are free of bank conflicts. Tiles travel from global
+// the fragment reads of 16 consecutive rows spread over the LDS banks. Tiles travel from global
 // memory straight into a ring of two or three LDS stages (buffer loads with an LDS destination),
 // so the copies of later K-tiles are in flight while one is multiplied.
 

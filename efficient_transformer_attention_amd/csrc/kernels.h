@@ -1,6 +1,7 @@
 // kernels.h — the GEMM core, the forward kernels and their host-side plan, shared by the
-// forward (flashgau.hip) and the backward pass (backward.hip). Everything here lives in an
-// anonymous namespace: each translation unit instantiates what it launches.
+// forward (flashgau.hip), the backward pass (backward.hip) and the decoder's state fold
+// (decode.hip). Everything here lives in an anonymous namespace: each translation unit
+// instantiates what it launches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,15 +17,16 @@
 namespace {
 
 
-// Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ, both operands K-contiguous.
+// Block-level tiled GEMM C[BM x BN] += A[BM x K] · B[BN x K]ᵀ (operand layouts below).
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of 16x16 accumulator fragments.
 // Operand tiles travel from global memory straight into a ring of NS LDS stages (no staging
 // registers): with NS = 3 the loads of tile t+2 fly while tile t is multiplied, one barrier per
 // tile; with NS = 2 (tiles too large for three stages) the loads of tile t+2 are issued after
 // tile t has been consumed, two barriers per tile, or, with SB (single barrier), the loads of
 // tile t+1 are issued right after the barrier that opens tile t (the stage they fill held tile
-// t-1, which every wave finished before that barrier), one barrier per tile. PRIO raises the wave priority while it issues
-// matrix instructions; iglp_opt(1) asks the scheduler to interleave the LDS reads with them.
+// t-1, which every wave finished before that barrier), one barrier per tile. PRIO raises the
+// wave priority while it issues matrix instructions; iglp_opt(1) asks the scheduler to
+// interleave the LDS reads with them.
 //
 // Operand layouts (AL for A, BL for B): kLayoutK (the default) stores each of the tile's rows with
 // its K elements contiguous; kLayoutMN stores the operand as K rows of M-contiguous elements (a
