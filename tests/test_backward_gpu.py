@@ -140,12 +140,14 @@ def test_backward_full_size_through_sequence_zero(name):
         assert errs[k] <= TOL[dtype], (k, errs[k])
 
 
-@pytest.mark.parametrize("name,t0", [("c3_causal_bf16_n4096", 1000), ("c3_causal_bf16_n4096", 3584)])
+@pytest.mark.parametrize("name,t0", [("c3_causal_bf16_n4096", 1000), ("c3_causal_bf16_n4096", 3584),
+                                     ("c5_causal_bf16_n32768", 20000)])
 def test_backward_causality_full_size(name, t0):
     # Causal: O[t] depends on X[t'] for t' <= t only, so with dO zero from token t0 on, dX from t0
     # on is exactly zero: every contribution to it is a product with a zero of dO (through the
     # chunk's own attention, its state and the gate). t0 = 1000 falls inside a chunk (c = 256),
-    # 3584 on a chunk boundary; the run is the benchmark's launch configuration at full size.
+    # 3584 on a chunk boundary; the run is the benchmark's launch configuration at full size. The
+    # n = 32768, d = 1024, e = 2048, c = 512 case runs other widths through the same kernels.
     torch = _torch()
     B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
     assert causal
