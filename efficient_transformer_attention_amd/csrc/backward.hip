@@ -991,10 +991,12 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
 // (also storing the pre-activations H_v | H_z), the gate's pre-activations H_u, scores and prefix
 // states. `flash_gau_backward` runs this first; `flash_gau_forward_train` runs it as part of a
 // forward and leaves it in the workspace.
+// gate: also compute the gate's pre-activations H_u (the training forward's mix stage writes them
+// itself).
 template <class E>
 void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
                       const void* W_z, const float* gamma, const float* beta, const void* W_o,
-                      int causal, float rope_base, char* ws, hipStream_t stream) {
+                      int causal, float rope_base, char* ws, hipStream_t stream, bool gate) {
   using T = typename E::T;
   using S = Shapes<E>;
   const Plan& pl = bp.f;
@@ -1017,7 +1019,7 @@ void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const voi
                   int(pl.n), rope, log2_base, R(BR_HR)};
     launch_proj<E, true>(a, stream);
   }
-  {
+  if (gate) {
     // the gate's pre-activations H_u = X W_u, token-major: the output projection's GEMM (and its
     // large tiles) with W_uᵀ, the first e rows of the packed weights, in W_oᵀ's place and X in Y's
     OutArgs<E> g{WcatT, Xp, R(BR_HU), M, e, d};
@@ -1042,7 +1044,7 @@ void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const voi
 }
 
 // A forward that keeps what the backward needs: the recompute stages, then the forward's mix
-// (its gate read from the stored H_u instead of its own GEMM) and output projection.
+// (which also writes the gate's pre-activations H_u) and output projection.
 template <class E>
 int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
                          const void* W_z, const float* gamma, const float* beta, const void* W_o,
@@ -1053,7 +1055,8 @@ int launch_train_forward(const BPlan& bp, const void* X, const void* W_u, const 
   auto R = [&](int r) { return reinterpret_cast<T*>(ws + bp.off[r]); };
   const int M = int(pl.M), d = int(pl.d), e = int(pl.e), s = int(pl.s), c = int(pl.c);
   const bool lin = !(causal && pl.G == 1);
-  launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream);
+  launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream,
+                      false);
   {
     MixArgs<E> a{W(FLASHGAU_WS_VT), W(FLASHGAU_WS_ST), W(FLASHGAU_WS_P), W(FLASHGAU_WS_QL),
                  reinterpret_cast<const T*>(X), W(FLASHGAU_WS_WCAT_T), W(FLASHGAU_WS_Y), d,
@@ -1092,7 +1095,8 @@ int launch_backward(const BPlan& bp, const void* X, const void* W_u, const void*
   const float inv_n = float(1.0 / double(pl.n));
 
   if (recompute)
-    launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream);
+    launch_recompute<E>(bp, X, W_u, W_v, W_z, gamma, beta, W_o, causal, rope_base, ws, stream,
+                        true);
 
   // ---- gate, output projection and V̂
   {

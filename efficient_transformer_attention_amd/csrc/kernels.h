@@ -986,8 +986,8 @@ struct MixArgs {
   int d;
   int nbg, G, c, e, s, causal;
   int lin;  // 0: no global term (causal with a single chunk: its prefix state is empty)
-  const typename E::T* Hu;   // HU instantiation: X W_u before SiLU, [B*G*c, e], stored by the
-                             // projection (the gate's GEMM is then not run here)
+  typename E::T* Hu;  // HU instantiation (the training forward): X W_u before SiLU, [B*G*c, e],
+                      // written here for the backward
 };
 
 template <class E, int BM, int BN, int WM, int WN, int NS, bool HU = false>
@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
   // share a CU (one pipeline over all three K-ranges needs more and halves the occupancy).
   G gu;
   gu.zero();
-  if constexpr (!HU) {
+  {
     const Src au = make_src(p.WuT, m0, p.d, E::kSize, p.e - m0, BM, p.d);
     const Src bu = make_src(p.X, tok0 + n0, p.d, E::kSize, p.c - n0, BN, p.d);
     const int nku = (p.d * E::kSize + kStageBytes - 1) / kStageBytes;
@@ -1058,28 +1058,34 @@ __global__ __launch_bounds__(64 * WM * WN) void mix_kernel(MixArgs<E> p) {
         wave, wm, wn, lane);
 
   // Y = SiLU(X W_u) ⊙ (P V + Q_lin S / n), formed in fp32 from both accumulators, rounded once,
-  // and staged through LDS so that every token row of Y is written as full 16-byte runs. A stored
-  // H_u tile first goes whole into the LDS half the staging leaves free.
+  // and staged through LDS so that every token row of Y is written as full 16-byte runs. The
+  // training forward (HU) first writes the gate's pre-activations H_u the same way, rounded to the
+  // storage type, and forms Y from the rounded values: the backward's recompute reads that same
+  // H_u, so both arrive at the same Y.
   using T = typename E::T;
-  char* const hub = reinterpret_cast<char*>(lds) + BM * BN * E::kSize;
   if constexpr (HU) {
-    static_assert(2 * BM * BN * E::kSize <= G::kLds * 16, "H_u tile and staging exceed the LDS");
-    lds_tile_load<T, BN, BM, G::kThreads>(hub, p.Hu + (tok0 + n0) * p.e + m0, p.e, p.c - n0,
-                                          p.e - m0);
-    __syncthreads();
+    gu.template stage_rows<T>(
+        lds, wave, wm, wn, lane,
+        [&](int, int, int, int, const f32x4& v, T* out) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(v[k]);
+        },
+        [&](int cl, int r, const u32x4& chunk) {
+          const int j = m0 + r, i = n0 + cl;
+          if (j < p.e && i < p.c) store16_stream(p.Hu + (tok0 + i) * p.e + j, chunk);
+        });
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gu.acc[i][j][k] = to_f32(from_f32<E>(gu.acc[i][j][k]));
   }
   g.template stage_rows<T>(
       lds, wave, wm, wn, lane,
-      [&](int fi, int fj, int r, int cl, const f32x4& v, T* out) {
-        float hu[4];
-        if constexpr (HU) {
-          lds_tile_read4f<T, BM>(hub, cl, r, hu);
-        } else {
+      [&](int fi, int fj, int, int, const f32x4& v, T* out) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) hu[k] = gu.acc[fi][fj][k];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(hu[k]) * v[k]);
+        for (int k = 0; k < 4; ++k) out[k] = from_f32<E>(silu(gu.acc[fi][fj][k]) * v[k]);
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, i = n0 + cl;

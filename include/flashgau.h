@@ -346,8 +346,9 @@ int flash_gau_backward(const void* X, const void* W_u, const void* W_v, const vo
  * workspace (at least flashgau_backward_workspace_size() bytes) everything the backward reads of
  * the forward: the projection over W_v | W_z with its pre-activations, the gate's pre-activations
  * X W_u, the heads, the scores,
- * the prefix states and the gated mix Y = U ⊙ (V̂_quad + V̂_lin). Its mix stage reads the stored X W_u instead of running the gate's GEMM, so
- * O may differ from flash_gau_forward's in the last bf16 bit (same tolerance to the exact result).
+ * the prefix states and the gated mix Y = U ⊙ (V̂_quad + V̂_lin). Its mix stage writes X W_u
+ * rounded to the storage type and forms the gate from those rounded values, so O may differ from
+ * flash_gau_forward's in the last bf16 bit (same tolerance to the exact result).
  * flash_gau_backward_saved then returns the gradients flash_gau_backward would (bitwise the same),
  * reading that workspace instead of recomputing it: it must follow a flash_gau_forward_train of
  * the same inputs, shapes and rope_base on the same stream, with the workspace untouched between.
