@@ -238,3 +238,31 @@ def test_train_forward_then_saved_backward(name):
     assert err <= TOL[dtype]
     for k in fg.GRAD_NAMES:
         assert torch.equal(saved[k], full[k]), k
+
+
+def test_train_pair_full_size():
+    # The training pair at the benchmark's size and launch configuration: the training forward's
+    # mix stage writes the gate's pre-activations itself, which the recomputing backward gets from a
+    # separate GEMM; both must hold the same values, so the saved backward returns the recomputing
+    # one's gradients bitwise. O is checked against the oracle on sequence 0.
+    torch = _torch()
+    name = "c3_causal_bf16_n4096"
+    B, n, d, e, s, c, causal, dtype = gen.WORKLOADS[name]
+    print(f"[gpu case] train pair full size {name}", flush=True)
+    inp = gen.workload_inputs(name, seed=2)
+    dO = _dev(gen.make_output_grad(B, n, d, dtype, seed=2), dtype)
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, fg.BF16),),
+                     dtype=torch.uint8, device="cuda")
+    O = fg.flash_gau_forward_train(*args, c, causal, ws)
+    saved = fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, saved=True)
+    full = fg.flash_gau_backward(*args, dO, c, causal)
+    torch.cuda.synchronize()
+    for k in fg.GRAD_NAMES:
+        assert torch.equal(saved[k], full[k]), k
+    ref = oracle.flash_forward(inp.X[:1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o, c,
+                               causal)
+    err = _rel(O[:1].float().cpu().numpy(), ref)
+    print(f"  O sequence 0 max rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
