@@ -988,11 +988,9 @@ int make_bplan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t ch
 
 // ------------------------------------------------------------------------------ launches
 // The forward's intermediates as the backward reads them: pack, the projection over W_v | W_z
-// (also storing the pre-activations H_v | H_z), the gate's pre-activations H_u, scores and prefix
-// states. `flash_gau_backward` runs this first; `flash_gau_forward_train` runs it as part of a
-// forward and leaves it in the workspace.
-// gate: also compute the gate's pre-activations H_u (the training forward's mix stage writes them
-// itself).
+// (also storing the pre-activations H_v | H_z), with `gate` the gate's pre-activations H_u, scores
+// and prefix states. `flash_gau_backward` runs this first; `flash_gau_forward_train` runs it
+// without `gate` as part of a forward (its mix stage writes H_u) and leaves it in the workspace.
 template <class E>
 void launch_recompute(const BPlan& bp, const void* X, const void* W_u, const void* W_v,
                       const void* W_z, const float* gamma, const float* beta, const void* W_o,
