@@ -107,7 +107,7 @@ __device__ __forceinline__ void gemm_to_f32(u32x4* lds, const Src& a, int ka0, c
         for (int k = 0; k < 4; ++k) o[k] = v[k];
       },
       [&](int r, int cl, const u32x4& chunk) {
-        if (r < rows && cl < cols) *reinterpret_cast<u32x4*>(out + r * ldo + cl) = chunk;
+        if (r < rows && cl < cols) store16_stream(out + r * ldo + cl, chunk);
       });
 }
 
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(BGemm<E>::kThreads) void mixb_kernel(MixBArgs<E> p)
         },
         [&](int cl, int r, const u32x4& chunk) {
           const int j = m0 + r, i = n0 + cl;
-          if (j < p.e && i < p.c) *reinterpret_cast<u32x4*>(dst[w] + (tok0 + i) * p.e + j) = chunk;
+          if (j < p.e && i < p.c) store16_stream(dst[w] + (tok0 + i) * p.e + j, chunk);
         });
   }
 }
@@ -306,7 +306,7 @@ __device__ __forceinline__ void dp_block(const DScoresArgs<E>& p, u32x4* lds, in
       },
       [&](int r, int cl, const u32x4& chunk) {
         const int i = i0 + r, j = j0 + cl;
-        if (i < p.c && j < p.c) *reinterpret_cast<u32x4*>(p.dAr + (tok0 + i) * p.c + j) = chunk;
+        if (i < p.c && j < p.c) store16_stream(p.dAr + (tok0 + i) * p.c + j, chunk);
       });
 }
 
@@ -483,7 +483,7 @@ __device__ __forceinline__ void dv_block(const DVArgs<E>& p, u32x4* lds, int lid
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int j = m0 + r, key = n0 + cl;
-        if (j < p.e && key < p.c) *reinterpret_cast<u32x4*>(p.dHvr + (tok0 + key) * p.e + j) = chunk;
+        if (j < p.e && key < p.c) store16_stream(p.dHvr + (tok0 + key) * p.e + j, chunk);
       });
 }
 
@@ -673,7 +673,7 @@ __device__ __forceinline__ void dx_block(const DXArgs<E>& p, u32x4* lds, int lid
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int k = m0 + r, i = n0 + cl;
-        if (k < p.d && i < p.M) *reinterpret_cast<u32x4*>(p.dX + int64_t(i) * p.d + k) = chunk;
+        if (k < p.d && i < p.M) store16_stream(p.dX + int64_t(i) * p.d + k, chunk);
       });
 }
 

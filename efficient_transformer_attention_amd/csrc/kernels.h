@@ -597,7 +597,7 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjArgs<E> p) {
                                [&](int r, int cl, const u32x4& chunk) {
                                  const int row = m0 + r, col = n0 + cl;
                                  if (row < p.M)
-                                   *reinterpret_cast<u32x4*>(p.Hr + int64_t(row) * hcols + col) = chunk;
+                                   store16_stream(p.Hr + int64_t(row) * hcols + col, chunk);
                                });
     }
     return;
