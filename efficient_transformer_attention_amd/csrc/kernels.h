@@ -722,7 +722,7 @@ __device__ __forceinline__ void scores_block(const ScoresArgs<E>& p, u32x4* lds,
       },
       [&](int cl, int r, const u32x4& chunk) {
         const int key = k0 + r, tok = t0 + cl;
-        if (key < p.c && tok < p.c) *reinterpret_cast<u32x4*>(P + int64_t(tok) * p.c + key) = chunk;
+        if (key < p.c && tok < p.c) store16_stream(P + int64_t(tok) * p.c + key, chunk);
       });
 }
 
@@ -892,7 +892,7 @@ __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     w[k] = uint32_t(f32_to_bf16(v[2 * k])) | (uint32_t(f32_to_bf16(v[2 * k + 1])) << 16);
-  *reinterpret_cast<u32x4*>(p) = w;
+  store16_stream(p, w);
 }
 __device__ __forceinline__ void store8(float* p, const float* v) {
   reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
