@@ -256,7 +256,9 @@ __device__ __forceinline__ void grouped_tile(int lid, int ntm, int ntn, int gm, 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
 constexpr int64_t kInt32Max = 2147483647;
-constexpr int64_t kMaxBlocks = 1 << 24;  // keeps blocks x threads within a 32-bit grid
+// Launch limit: with at most 512 threads per workgroup, a grid of at most 2^22 workgroups keeps
+// its work-item count within 32 bits.
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -1281,8 +1281,10 @@ int make_plan(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chu
   };
   for (int64_t g : grids)
     if (g > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
-  const int64_t pack_tiles = cdiv(d, 64) * (2 * cdiv(e, 64) + cdiv(s, 64)) + cdiv(e, 64) * cdiv(d, 64);
-  if (pack_tiles > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
+  // the weight transposes: 64 x 64 wave tiles at bf16, 32 x 32 at fp32, four per workgroup
+  const int64_t te = f32 ? 32 : 64;
+  const int64_t pack_tiles = cdiv(d, te) * (2 * cdiv(e, te) + cdiv(s, te)) + cdiv(e, te) * cdiv(d, te);
+  if (cdiv(pack_tiles, 4) > kMaxBlocks) return FLASHGAU_ERR_BAD_SHAPE;
   return FLASHGAU_OK;
 }
 
