@@ -1,0 +1,89 @@
+"""GPU parity over seeded random shapes: the forward and the backward through the C ABI against
+the fp64 oracle, on shapes drawn from the accepted range (every width a multiple of 8, n a
+multiple of the chunk), mixing element types, masks, chunk counts and the rotary embedding. The
+draws are fixed by their seeds, and each case prints its shape before it runs. Bars as in the
+other parity tests: max |got - ref| / max |ref| per tensor, 2e-2 for bf16, 1e-4 for fp32.
+"""
+
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+from efficient_transformer_attention_amd import flashgau as fg
+from efficient_transformer_attention_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _draw(count, seed):
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(count):
+        c = 8 * rng.randint(1, 24)
+        G = rng.randint(1, 4)
+        B = rng.randint(1, 3)
+        d, e, s = 8 * rng.randint(1, 34), 8 * rng.randint(1, 49), 8 * rng.randint(1, 25)
+        dtype = rng.choice(["bf16", "f32"])
+        causal = rng.random() < 0.5
+        rope = rng.choice([None, 10000.0])
+        cases.append((B, c * G, d, e, s, c, causal, dtype, rope))
+    return cases
+
+
+FORWARD = _draw(24, 11)
+BACKWARD = _draw(10, 12)
+
+
+def _dev(a, dtype):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(tdt).contiguous()
+
+
+def _rel(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _args(inp, dtype):
+    return [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+
+
+@pytest.mark.parametrize("i", range(len(FORWARD)))
+def test_forward_random_shape(i):
+    import torch
+    B, n, d, e, s, c, causal, dtype, rope = FORWARD[i]
+    print(f"[gpu case] forward random shape {i}: B={B} n={n} d={d} e={e} s={s} c={c} "
+          f"causal={causal} {dtype} rope={rope}", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=100 + i, gamma_std=0.3, beta_std=0.1)
+    O = fg.flash_gau_forward(*_args(inp, dtype), c, causal, rope_base=rope)
+    torch.cuda.synchronize()
+    ref = oracle.flash_forward(inp.X, inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o, c,
+                               causal, rope_base=rope)
+    err = _rel(O.float().cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("i", range(len(BACKWARD)))
+def test_backward_random_shape(i):
+    import torch
+    B, n, d, e, s, c, causal, dtype, rope = BACKWARD[i]
+    print(f"[gpu case] backward random shape {i}: B={B} n={n} d={d} e={e} s={s} c={c} "
+          f"causal={causal} {dtype} rope={rope}", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=200 + i, gamma_std=0.3, beta_std=0.1)
+    dO = gen.make_output_grad(B, n, d, dtype, seed=200 + i)
+    grads = fg.flash_gau_backward(*_args(inp, dtype), _dev(dO, dtype), c, causal,
+                                  rope_base=rope or 0.0)
+    torch.cuda.synchronize()
+    ref = oracle.flash_backward(inp.X, inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o, dO,
+                                c, causal, rope_base=rope)
+    errs = {k: _rel(grads[k].float().cpu().numpy(), ref[k]) for k in fg.GRAD_NAMES}
+    print("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k in fg.GRAD_NAMES:
+        assert errs[k] <= TOL[dtype], (k, errs[k])
