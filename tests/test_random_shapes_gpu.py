@@ -1,8 +1,9 @@
-"""GPU parity over seeded random shapes: the forward and the backward through the C ABI against
-the fp64 oracle, on shapes drawn from the accepted range (every width a multiple of 8, n a
-multiple of the chunk), mixing element types, masks, chunk counts and the rotary embedding. The
-draws are fixed by their seeds, and each case prints its shape before it runs. Bars as in the
-other parity tests: max |got - ref| / max |ref| per tensor, 2e-2 for bf16, 1e-4 for fp32.
+"""GPU parity over seeded random shapes: the forward, the backward and the decoding step through
+the C ABI against the fp64 oracle, on shapes drawn from the accepted range (every width a multiple
+of 8; for the forward and backward n a multiple of the chunk), mixing element types, masks, chunk
+counts and the rotary embedding. The draws are fixed by their seeds, and each case prints its
+shape before it runs. Bars as in the other parity tests: max |got - ref| / max |ref| per tensor
+(per step for decoding), 2e-2 for bf16, 1e-4 for fp32.
 """
 
 import random
@@ -87,3 +88,46 @@ def test_backward_random_shape(i):
     print("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k in fg.GRAD_NAMES:
         assert errs[k] <= TOL[dtype], (k, errs[k])
+
+
+def _draw_decode(count, seed):
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(count):
+        B = rng.randint(1, 20)
+        d, e, s = 8 * rng.randint(1, 34), 8 * rng.randint(1, 49), 8 * rng.randint(1, 25)
+        c = rng.randint(1, 48)
+        T = rng.randint(1, min(120, 5 * c // 2 + 1))
+        n = T + rng.randint(0, 64)
+        cases.append((B, d, e, s, c, T, n, rng.choice(["bf16", "f32"]), rng.choice([None, 10000.0])))
+    return cases
+
+
+DECODE = _draw_decode(8, 13)
+
+
+@pytest.mark.parametrize("i", range(len(DECODE)))
+def test_decode_random_shape(i):
+    # step by step from an empty state (its buffer filled with 0xFF bytes), across chunk ends
+    import torch
+    B, d, e, s, c, T, n, dtype, rope = DECODE[i]
+    print(f"[gpu case] decode random shape {i}: B={B} d={d} e={e} s={s} c={c} T={T} n={n} {dtype} "
+          f"rope={rope}", flush=True)
+    inp = gen.make_inputs(B, -(-T // c) * c, d, e, s, c, True, dtype, seed=300 + i, gamma_std=0.3,
+                          beta_std=0.1)
+    W = [_dev(w, dtype) for w in (inp.W_u, inp.W_v, inp.W_z, inp.W_o)]
+    gamma, beta = _dev(inp.gamma, "f32"), _dev(inp.beta, "f32")
+    packed = fg.pack_weights(*W)
+    state = fg.DecodeState(B, d, e, s, c, W[0].dtype, "cuda")
+    state.buf.fill_(255)
+    X = _dev(inp.X, dtype)
+    outs = [fg.flash_gau_decode_step(X[:, t].contiguous(), packed, gamma, beta, c, t, n, state,
+                                     rope_base=rope or 0.0).float() for t in range(T)]
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 1).cpu().numpy().astype(np.float64)
+    ref, _ = oracle.decode_sequence(inp.X[:, :T], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta,
+                                    inp.W_o, c, n=n, rope_base=rope)
+    errs = [_rel(got[:, t], ref[:, t]) for t in range(T)]
+    worst = int(np.argmax(errs))
+    print(f"  worst step {worst} rel err {errs[worst]:.3e}", flush=True)
+    assert errs[worst] <= TOL[dtype], (worst, errs[worst])
