@@ -11,8 +11,9 @@ host has just spent seconds generating inputs with the GPU idle, and the first c
 run on clocks that are still ramping; `settle_ms` in the line records it), then --warmup untimed
 calls. `value` is tokens/s = B*n / (wall time of one step), timed over exactly --steps calls
 between two device synchronisations, with nothing else on the stream. Two separate passes follow
-outside the timed region: calls that record a HIP event before every kernel on the library's
-stream (per-kernel durations; the roofline object reports the kernel that takes the longest), and
+outside the timed region: calls that launch every kernel with its own start and stop HIP events
+on the library's stream (per-kernel durations; the roofline object reports the kernel that takes
+the longest), and
 at least 50 calls each bracketed by two events (`step_ms_quantiles`). The CPU baseline is the fp64 oracle timed on the
 host on one sequence of the same batch; its output also checks the GPU's on that sequence.
 
@@ -525,8 +526,8 @@ def measure_forward(fg, torch, dev, inp, steps, warmup, settle_ms, kernel_steps,
     settle_ms (after host-side input generation the GPU has idled for seconds and its clocks have
     dropped), `warmup` untimed calls, then exactly `steps` calls between two device
     synchronisations (the timed region: no events, nothing else on the stream). Then two separate
-    passes, outside the timed region: `kernel_steps` calls of flash_gau_forward_timed (a HIP event
-    before every kernel, on the library's stream) for per-kernel durations, and `quantile_steps`
+    passes, outside the timed region: `kernel_steps` calls of flash_gau_forward_timed (each kernel
+    launched with its own start and stop HIP events) for per-kernel durations, and `quantile_steps`
     calls each bracketed by two events for the step-time distribution. Returns the record and O."""
     B, n, d, e, s = inp.shape
     c, causal = inp.chunk, inp.causal
@@ -564,10 +565,10 @@ def measure_forward(fg, torch, dev, inp, steps, warmup, settle_ms, kernel_steps,
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / steps
 
-    # per-kernel durations, a pass of its own
-    events = HipEvents(kernel_steps * (nst + 1))
+    # per-kernel durations, a pass of its own: each kernel's own start and stop events
+    events = HipEvents(kernel_steps * 2 * nst)
     for k in range(kernel_steps):
-        evs = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+        evs = events.handles[k * 2 * nst:(k + 1) * 2 * nst]
         rc = fg.forward_timed_raw(*ptrs, c, causal, B, n, d, e, s, dt, O.data_ptr(), ws.data_ptr(),
                                   nbytes, stream, evs)
         if rc != fg.OK:
@@ -575,9 +576,9 @@ def measure_forward(fg, torch, dev, inp, steps, warmup, settle_ms, kernel_steps,
     torch.cuda.synchronize(dev)
     stage_ms = {st: [] for st in fg.STAGES}
     for k in range(kernel_steps):
-        h = events.handles[k * (nst + 1):(k + 1) * (nst + 1)]
+        h = events.handles[k * 2 * nst:(k + 1) * 2 * nst]
         for i, st in enumerate(fg.STAGES):
-            stage_ms[st].append(events.ms(h[i], h[i + 1]))
+            stage_ms[st].append(events.ms(h[2 * i], h[2 * i + 1]))
     events.close()
 
     # step-time distribution, a pass of its own (events between steps only)

@@ -5,6 +5,7 @@
 // copy.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -261,6 +262,27 @@ constexpr int64_t kInt32Max = 2147483647;
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-kernel timing (the timed forward): while `g_kernel_timing` holds two events, the next launch
+// made through launch_kernel records them when its kernel starts and when it ends
+// (hipExtLaunchKernel) and clears them; otherwise launch_kernel is a plain launch.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local KernelTiming g_kernel_timing;
+
+template <class... KArgs, class... Args>
+void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
+                   hipStream_t stream, Args... args) {
+  if (g_kernel_timing.start) {
+    const KernelTiming t = g_kernel_timing;
+    g_kernel_timing = KernelTiming{};
+    hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds_bytes), stream, t.start, t.stop, 0u,
+                          args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+  }
+}
 
 // Layout of the packed weights: (W_u | W_v | W_z)ᵀ [2e+s, d], then W_oᵀ [d, e] at the next
 // 256-byte boundary (the same two buffers open the forward's workspace).

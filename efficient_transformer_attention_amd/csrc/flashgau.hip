@@ -67,15 +67,29 @@ template <class E>
 int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, const void* W_z,
                const float* gamma, const float* beta, const void* W_o, int causal, float rope_base,
                void* O, char* ws, hipStream_t stream, hipEvent_t const* events,
-               const void* packed = nullptr, size_t wo_off = 0) {
+               const void* packed = nullptr, size_t wo_off = 0, bool per_kernel = false) {
   using T = typename E::T;
   using S = Shapes<E>;
-  // events (optional): events[i] is recorded right before stage i is launched, and
-  // events[FLASHGAU_NUM_STAGES] after the last one.
+  // events (optional). Boundaries (per_kernel false): events[i] is recorded right before stage i
+  // is launched, and events[FLASHGAU_NUM_STAGES] after the last one. Per kernel: events[2i] and
+  // events[2i + 1] record when stage i's kernel starts and ends; a stage that launches nothing
+  // records both at once.
   int stage = 0;
+  struct ClearTiming {  // no timing request outlives this call, whichever way it returns
+    ~ClearTiming() { g_kernel_timing = KernelTiming{}; }
+  } clear_timing;
   auto mark = [&]() -> bool {
     if (!events) return true;
-    return hipEventRecord(events[stage++], stream) == hipSuccess;
+    if (!per_kernel) return hipEventRecord(events[stage++], stream) == hipSuccess;
+    if (stage > 0 && g_kernel_timing.start) {  // the stage before launched nothing
+      const KernelTiming t = g_kernel_timing;
+      g_kernel_timing = KernelTiming{};
+      if (hipEventRecord(t.start, stream) != hipSuccess || hipEventRecord(t.stop, stream) != hipSuccess)
+        return false;
+    }
+    if (stage < FLASHGAU_NUM_STAGES) g_kernel_timing = {events[2 * stage], events[2 * stage + 1]};
+    ++stage;
+    return true;
   };
   T* WcatT = packed ? reinterpret_cast<T*>(const_cast<void*>(packed))
                     : reinterpret_cast<T*>(ws + pl.off[FLASHGAU_WS_WCAT_T]);
@@ -113,7 +127,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     StatesArgs<E> ta{Klt, Vt, St, Carry, int(pl.B), int(pl.G), s, e, c, causal,
                      int(pl.ng), int(pl.gs), float(1.0 / double(pl.n)), 0};
     const int64_t ntb = lin ? pl.B * pl.ng * cdiv(s, S::kStatesBM) * cdiv(e, S::kStatesBN) : 0;
-    hipLaunchKernelGGL((scores_states_kernel<E, S>), dim3(unsigned(nsb8 + ntb)),
+    launch_kernel((scores_states_kernel<E, S>), dim3(unsigned(nsb8 + ntb)),
                        dim3(64 * S::kScoresWM * S::kScoresWN), 0, stream, sa, int(nsb8), int(nsb), ta,
                        int(lin));
   }
@@ -122,7 +136,7 @@ int launch_all(const Plan& pl, const void* X, const void* W_u, const void* W_v, 
     CarryArgs<E> a{St, Carry, int(pl.B), int(pl.G), int(pl.ng), int(pl.gs), causal,
                    int64_t(e) * s, 0};
     const int64_t nb = cdiv(pl.B * e * s / 8, 256);
-    hipLaunchKernelGGL(carry_kernel<E>, dim3(unsigned(nb)), dim3(256), 0, stream, a);
+    launch_kernel(carry_kernel<E>, dim3(unsigned(nb)), dim3(256), 0, stream, a);
   }
   if (!mark()) return FLASHGAU_ERR_HIP;
   {
@@ -178,7 +192,8 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
                         int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,
                         flashgau_dtype dtype, void* O, void* workspace, size_t workspace_bytes,
                         void* hip_stream, hipEvent_t const* events, float rope_base,
-                        const void* packed = nullptr, size_t packed_bytes = 0) {
+                        const void* packed = nullptr, size_t packed_bytes = 0,
+                        bool per_kernel = false) {
   Plan pl;
   const int rc = make_plan(B, n, d, e, s, chunk, causal, dtype, &pl);
   if (rc != FLASHGAU_OK) return rc;
@@ -214,9 +229,9 @@ static int forward_impl(const void* X, const void* W_u, const void* W_v, const v
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == FLASHGAU_BF16)
     return launch_all<BF16>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
-                            ws, stream, events, packed, wo_off);
+                            ws, stream, events, packed, wo_off, per_kernel);
   return launch_all<F32>(pl, X, W_u, W_v, W_z, gamma, beta, W_o, causal ? 1 : 0, rope_base, O,
-                         ws, stream, events, packed, wo_off);
+                         ws, stream, events, packed, wo_off, per_kernel);
 }
 
 int flashgau_state_groups(int64_t B, int64_t n, int64_t d, int64_t e, int64_t s, int64_t chunk,
@@ -284,12 +299,14 @@ int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, con
                             size_t workspace_bytes, void* hip_stream, void* const* stage_events,
                             int num_events) {
   if (!stage_events) return FLASHGAU_ERR_NULL_PTR;
-  if (num_events != FLASHGAU_NUM_STAGES + 1) return FLASHGAU_ERR_BAD_SHAPE;
+  const bool per_kernel = num_events == 2 * FLASHGAU_NUM_STAGES;
+  if (num_events != FLASHGAU_NUM_STAGES + 1 && !per_kernel) return FLASHGAU_ERR_BAD_SHAPE;
   for (int i = 0; i < num_events; ++i)
     if (!stage_events[i]) return FLASHGAU_ERR_NULL_PTR;
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, hip_stream,
-                      reinterpret_cast<hipEvent_t const*>(stage_events), 0.0f);
+                      reinterpret_cast<hipEvent_t const*>(stage_events), 0.0f, nullptr, 0,
+                      per_kernel);
 }
 
 int flashgau_packed_weights_size(int64_t d, int64_t e, int64_t s, flashgau_dtype dtype,

@@ -1311,19 +1311,19 @@ void launch_out(const OutArgs<E>& a, hipStream_t stream) {
       // too few 256 x 128 tiles to give every CU one: 128 x 128 tiles, two per CU, twice the
       // workgroups for the same work
       const int64_t nb = cdiv(a.d, 128) * cdiv(a.M, 128);
-      hipLaunchKernelGGL((out_kernel<E, 128, 128, 2, 4, 2, false>), dim3(unsigned(nb)), dim3(512), 0,
+      launch_kernel((out_kernel<E, 128, 128, 2, 4, 2, false>), dim3(unsigned(nb)), dim3(512), 0,
                          stream, a);
       return;
     }
     if (out_big_tiles(a.M, a.d, true)) {
       const int64_t nb = cdiv(a.d, 256) * cdiv(a.M, 256);
-      hipLaunchKernelGGL((out_kernel<E, 256, 256, 2, 4, 2, false, true>), dim3(unsigned(nb)),
+      launch_kernel((out_kernel<E, 256, 256, 2, 4, 2, false, true>), dim3(unsigned(nb)),
                          dim3(512), 0, stream, a);
       return;
     }
   }
   const int64_t nb = cdiv(a.d, S::kOutBM) * cdiv(a.M, S::kOutBN);
-  hipLaunchKernelGGL((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
+  launch_kernel((out_kernel<E, S::kOutBM, S::kOutBN, S::kOutWM, S::kOutWN, S::kOutNS,
                                   S::kOutPrio>),
                      dim3(unsigned(nb)), dim3(64 * S::kOutWM * S::kOutWN), 0, stream, a);
 }
@@ -1338,13 +1338,13 @@ void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
   if constexpr (S::kProjBM == 128) {
     if (cdiv(a.M, 128) * cdiv(ncols, 128) < 2 * kCUs) {
       const int64_t nb = cdiv(a.M, 64) * cdiv(ncols, 64);
-      hipLaunchKernelGGL((proj_kernel<E, 64, 64, 2, 2, 3, EXTRA>), dim3(unsigned(nb)), dim3(256), 0,
+      launch_kernel((proj_kernel<E, 64, 64, 2, 2, 3, EXTRA>), dim3(unsigned(nb)), dim3(256), 0,
                          stream, a);
       return;
     }
   }
   const int64_t nb = cdiv(a.M, S::kProjBM) * cdiv(ncols, S::kProjBN);
-  hipLaunchKernelGGL(
+  launch_kernel(
       (proj_kernel<E, S::kProjBM, S::kProjBN, S::kProjWM, S::kProjWN, S::kProjNS, EXTRA>),
       dim3(unsigned(nb)), dim3(64 * S::kProjWM * S::kProjWN), 0, stream, a);
 }
@@ -1355,7 +1355,7 @@ template <class E, bool HU = false>
 void launch_mix(const MixArgs<E>& a, hipStream_t stream) {
   using S = Shapes<E>;
   const int64_t nb = int64_t(a.nbg) * cdiv(a.e, S::kMixBM) * cdiv(a.c, S::kMixBN);
-  hipLaunchKernelGGL((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS, HU>),
+  launch_kernel((mix_kernel<E, S::kMixBM, S::kMixBN, S::kMixWM, S::kMixWN, S::kMixNS, HU>),
                      dim3(unsigned(nb)), dim3(64 * S::kMixWM * S::kMixWN), 0, stream, a);
 }
 
@@ -1379,7 +1379,7 @@ void launch_pack(const void* W_u, const void* W_v, const void* W_z, const void* 
   }
   a.njobs = 4;
   a.ntiles = tiles;
-  hipLaunchKernelGGL(pack_kernel<E>, dim3(unsigned(cdiv(tiles, 4))), dim3(256), 0, stream, a);
+  launch_kernel(pack_kernel<E>, dim3(unsigned(cdiv(tiles, 4))), dim3(256), 0, stream, a);
 }
 
 }  // namespace

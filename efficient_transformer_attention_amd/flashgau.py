@@ -183,8 +183,9 @@ def forward_rope_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, rope_bas
 
 def forward_timed_raw(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       workspace, workspace_bytes, stream, events) -> int:
-    """flash_gau_forward_timed with integer addresses; ``events`` is a sequence of
-    len(STAGES) + 1 hipEvent_t handles (integers)."""
+    """flash_gau_forward_timed with integer addresses; ``events`` is a sequence of hipEvent_t
+    handles (integers): len(STAGES) + 1 stage boundaries, or 2 * len(STAGES) start/stop pairs,
+    one pair per kernel."""
     arr = (ctypes.c_void_p * len(events))(*events)
     return lib().flash_gau_forward_timed(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, int(bool(causal)),
                                          B, n, d, e, s, dtype, O, workspace, workspace_bytes, stream,

@@ -207,13 +207,17 @@ int flash_gau_forward_rope(const void* X, const void* W_u, const void* W_v, cons
  *                   workgroup ("Mixed Chunk", both terms and the gate)
  * 5 out           : Y W_o                                                                    */
 
-/* flash_gau_forward with per-stage timing: the same validation and the same launches, plus
- * hipEventRecord(stage_events[i], hip_stream) right before stage i is launched and
- * hipEventRecord(stage_events[FLASHGAU_NUM_STAGES], hip_stream) after the last stage.
- * stage_events points to num_events == FLASHGAU_NUM_STAGES + 1 hipEvent_t handles created by the
- * caller (NULL pointer or entry -> FLASHGAU_ERR_NULL_PTR, wrong count -> FLASHGAU_ERR_BAD_SHAPE).
- * For an empty problem no event is recorded. Used by benchmarks to time each kernel on the stream
- * it runs on. */
+/* flash_gau_forward with per-stage timing: the same validation and the same launches, and
+ * stage_events points to num_events hipEvent_t handles created by the caller, in one of two forms:
+ *   num_events == FLASHGAU_NUM_STAGES + 1: hipEventRecord(stage_events[i], hip_stream) right before
+ *     stage i is launched and hipEventRecord(stage_events[FLASHGAU_NUM_STAGES], hip_stream) after
+ *     the last stage (each interval then also holds the launch of its kernel);
+ *   num_events == 2 * FLASHGAU_NUM_STAGES: stage_events[2i] and stage_events[2i + 1] record when
+ *     stage i's kernel starts and ends (hipExtLaunchKernel's start and stop events); a stage that
+ *     launches nothing records both at once.
+ * NULL pointer or entry -> FLASHGAU_ERR_NULL_PTR, another count -> FLASHGAU_ERR_BAD_SHAPE. For an
+ * empty problem no event is recorded. Used by benchmarks to time each kernel on the stream it runs
+ * on. */
 int flash_gau_forward_timed(const void* X, const void* W_u, const void* W_v, const void* W_z,
                             const float* gamma, const float* beta, const void* W_o, int64_t chunk,
                             int causal, int64_t B, int64_t n, int64_t d, int64_t e, int64_t s,

@@ -231,6 +231,34 @@ def test_timed_entry_point_matches_and_orders_events():
         assert ms.value >= 0.0
     for h in evs:
         hip.hipEventDestroy(ctypes.c_void_p(h))
+    # the per-kernel form: a start and a stop event for each kernel, the kernels in launch order
+    pairs = []
+    for _ in range(2 * len(fg.STAGES)):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        pairs.append(h.value)
+    O.zero_()
+    rc = fg.forward_timed_raw(args[0].data_ptr(), args[1].data_ptr(), args[2].data_ptr(),
+                              args[3].data_ptr(), gamma.data_ptr(), beta.data_ptr(), Wo.data_ptr(),
+                              c, causal, B, n, d, e, s, fg.BF16, O.data_ptr(), ws.data_ptr(), nbytes,
+                              stream, pairs)
+    assert rc == fg.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), ref)
+    for i in range(len(fg.STAGES)):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), pairs[2 * i], pairs[2 * i + 1]) == 0
+        assert ms.value > 0.0  # every stage of this case launches a kernel
+        if i > 0:
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), pairs[2 * i - 1], pairs[2 * i]) == 0
+            assert ms.value >= 0.0
+    bad = fg.forward_timed_raw(args[0].data_ptr(), args[1].data_ptr(), args[2].data_ptr(),
+                               args[3].data_ptr(), gamma.data_ptr(), beta.data_ptr(), Wo.data_ptr(),
+                               c, causal, B, n, d, e, s, fg.BF16, O.data_ptr(), ws.data_ptr(), nbytes,
+                               stream, pairs[:-1])
+    assert bad == fg.ERR_BAD_SHAPE
+    for h in pairs:
+        hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
 def test_native_library_is_the_in_tree_build():
