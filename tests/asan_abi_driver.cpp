@@ -96,11 +96,21 @@ int main() {
   EXPECT(flash_gau_forward_rope(fake(0), fake(1), fake(2), fake(3), (const float*)fake(4),
                                 (const float*)fake(5), fake(6), c, 1, -1.0f, B, n, d, e, s,
                                 FLASHGAU_BF16, fake(7), fake(8), ws, nullptr) == FLASHGAU_ERR_BAD_SHAPE);
-  void* events[FLASHGAU_NUM_STAGES + 1] = {};
+  void* events[2 * FLASHGAU_NUM_STAGES] = {};
   EXPECT(flash_gau_forward_timed(fake(0), fake(1), fake(2), fake(3), (const float*)fake(4),
                                  (const float*)fake(5), fake(6), c, 1, B, n, d, e, s, FLASHGAU_BF16,
                                  fake(7), fake(8), ws, nullptr, events,
                                  FLASHGAU_NUM_STAGES + 1) == FLASHGAU_ERR_NULL_PTR);
+  // the per-kernel form (a start and a stop event per stage) is checked the same way; any other
+  // count is rejected before an event is looked at
+  EXPECT(flash_gau_forward_timed(fake(0), fake(1), fake(2), fake(3), (const float*)fake(4),
+                                 (const float*)fake(5), fake(6), c, 1, B, n, d, e, s, FLASHGAU_BF16,
+                                 fake(7), fake(8), ws, nullptr, events,
+                                 2 * FLASHGAU_NUM_STAGES) == FLASHGAU_ERR_NULL_PTR);
+  EXPECT(flash_gau_forward_timed(fake(0), fake(1), fake(2), fake(3), (const float*)fake(4),
+                                 (const float*)fake(5), fake(6), c, 1, B, n, d, e, s, FLASHGAU_BF16,
+                                 fake(7), fake(8), ws, nullptr, events,
+                                 FLASHGAU_NUM_STAGES) == FLASHGAU_ERR_BAD_SHAPE);
   size_t pk = 0;
   flashgau_packed_weights_size(d, e, s, FLASHGAU_BF16, &pk);
   EXPECT(flash_gau_forward_packed(fake(0), fake(1), pk - 1, (const float*)fake(4),
