@@ -1,8 +1,8 @@
 """GPU parity over seeded random shapes: the forward, the backward and the decoding step through
 the C ABI against the fp64 oracle, on shapes drawn from the accepted range (every width a multiple
 of 8; for the forward and backward n a multiple of the chunk), mixing element types, masks, chunk
-counts and the rotary embedding. The draws are fixed by their seeds, and each case prints its
-shape before it runs. Bars as in the other parity tests: max |got - ref| / max |ref| per tensor
+counts and the rotary embedding, plus a few larger shapes with ragged widths. The draws are fixed by their
+seeds, and each case prints its shape before it runs. Bars as in the other parity tests: max |got - ref| / max |ref| per tensor
 (per step for decoding), 2e-2 for bf16, 1e-4 for fp32.
 """
 
@@ -131,3 +131,57 @@ def test_decode_random_shape(i):
     worst = int(np.argmax(errs))
     print(f"  worst step {worst} rel err {errs[worst]:.3e}", flush=True)
     assert errs[worst] <= TOL[dtype], (worst, errs[worst])
+
+
+# Larger shapes with ragged widths, chosen so that the large-tile paths run with partial edge
+# tiles: 128 x 128 projection tiles that straddle the V | heads boundary (e not a multiple of 128),
+# 256 x 256 output tiles over a d that is not a multiple of 256, chunks that are not a multiple of
+# the 128-token tile, fp32's small tiles. The batch runs whole; the oracle checks its first and last
+# sequence. name: (B, n, d, e, s, chunk, causal, dtype)
+LARGE = {
+    "straddle_c200_causal": (4, 4000, 1000, 1000, 200, 200, True, "bf16"),
+    "c384_noncausal": (2, 6144, 768, 1536, 128, 384, False, "bf16"),
+    "ragged8_causal": (8, 2048, 520, 1544, 136, 256, True, "bf16"),
+    "long_ragged_causal": (1, 16384, 1032, 2056, 136, 512, True, "bf16"),
+    "ragged_noncausal_c192": (3, 3072, 776, 1288, 200, 192, False, "bf16"),
+    "fp32_ragged_causal": (2, 2048, 264, 520, 72, 128, True, "f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LARGE))
+def test_forward_large_ragged(name):
+    import torch
+    B, n, d, e, s, c, causal, dtype = LARGE[name]
+    print(f"[gpu case] forward large ragged {name}: B={B} n={n} d={d} e={e} s={s} c={c} "
+          f"causal={causal} {dtype}", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=400, gamma_std=0.3, beta_std=0.1)
+    O = fg.flash_gau_forward(*_args(inp, dtype), c, causal)
+    torch.cuda.synchronize()
+    sample = sorted({0, B - 1})
+    got = O.float().cpu().numpy()[sample]
+    ref = oracle.flash_forward(inp.X[sample], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o,
+                               c, causal)
+    err = _rel(got, ref)
+    print(f"  sequences {sample}: max rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+def test_backward_large_ragged():
+    # the input and weight gradients on 256 x 256 tiles with partial edge tiles in d, e and s and
+    # several token ranges; dO is zero on every sequence but the first, so the oracle needs only it
+    import torch
+    B, n, d, e, s, c, causal, dtype = LARGE["ragged8_causal"]
+    print(f"[gpu case] backward large ragged: B={B} n={n} d={d} e={e} s={s} c={c}", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=401, gamma_std=0.3, beta_std=0.1)
+    dO = gen.make_output_grad(B, n, d, dtype, seed=401)
+    dO[1:] = 0.0
+    grads = fg.flash_gau_backward(*_args(inp, dtype), _dev(dO, dtype), c, causal)
+    torch.cuda.synchronize()
+    ref = oracle.flash_backward(inp.X[:1], inp.W_u, inp.W_v, inp.W_z, inp.gamma, inp.beta, inp.W_o,
+                                dO[:1], c, causal)
+    got = {k: v.float().cpu().numpy() for k, v in grads.items()}
+    assert np.abs(got["dX"][1:]).max() == 0.0
+    errs = {k: _rel(got[k][:1] if k == "dX" else got[k], ref[k]) for k in fg.GRAD_NAMES}
+    print("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k in fg.GRAD_NAMES:
+        assert errs[k] <= TOL[dtype], (k, errs[k])
