@@ -257,6 +257,20 @@ def _check_workspace(ws, nbytes, dev):
         raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
 
 
+def _hold_for_stream(tensors, stream, dev):
+    """Tensors that a call allocated from torch's caching allocator (which ties them to the
+    current stream) but whose memory the library uses on ``stream``: when that is another stream,
+    each is recorded on it, so that the allocator hands the memory out again only after the work
+    queued there has finished (a workspace freed on return could otherwise be reused while the
+    kernels still read it)."""
+    import torch
+    if not tensors or stream == torch.cuda.current_stream(dev).cuda_stream:
+        return
+    ext = torch.cuda.ExternalStream(stream, device=dev)
+    for t in tensors:
+        t.record_stream(ext)
+
+
 def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=None, workspace=None,
                       stream=None, rope_base=None):
     """One FLASH layer forward on the GPU. X [B, n, d]; W_u, W_v [d, e]; W_z [d, s]; gamma, beta
@@ -267,16 +281,20 @@ def flash_gau_forward(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, out=Non
     import torch
     B, n, d, e, s, dt, dev = _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o)
     nbytes = workspace_size(B, n, d, e, s, chunk, causal, dt)
+    made = []
     if out is None:
         out = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+        made.append(out)
     else:
         _check_output(out, "out", (B, n, d), X.dtype, dev)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     else:
         _check_workspace(workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for_stream(made, stream, dev)
     ptrs = (X.data_ptr(), W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), gamma.data_ptr(),
             beta.data_ptr(), W_o.data_ptr())
     if rope_base is None:
@@ -369,6 +387,7 @@ def pack_weights(W_u, W_v, W_z, W_o, stream=None):
     packed = torch.empty((nbytes,), dtype=torch.uint8, device=W_u.device)
     if stream is None:
         stream = torch.cuda.current_stream(W_u.device).cuda_stream
+    _hold_for_stream([packed], stream, W_u.device)
     rc = pack_weights_raw(W_u.data_ptr(), W_v.data_ptr(), W_z.data_ptr(), W_o.data_ptr(), d, e, s, dt,
                           packed.data_ptr(), nbytes, stream)
     if rc != OK:
@@ -425,12 +444,15 @@ def flash_gau_decode_step(x, packed, gamma, beta, chunk, t, n, state, out=None, 
         raise ValueError(f"gamma and beta must be float32 [4, {state.s}]")
     if packed.dtype != torch.uint8 or not packed.is_contiguous():
         raise ValueError("packed must be the contiguous uint8 tensor pack_weights returned")
+    made = []
     if out is None:
         out = torch.empty((B, d), dtype=x.dtype, device=x.device)
+        made.append(out)
     else:
         _check_output(out, "out", (B, d), x.dtype, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
+    _hold_for_stream(made, stream, x.device)
     rc = decode_step_raw(x.data_ptr(), packed.data_ptr(), packed.numel(), gamma.data_ptr(),
                          beta.data_ptr(), chunk, t, n, rope_base, B, d, state.e, state.s, state.dt,
                          out.data_ptr(), state.buf.data_ptr(), state.buf.numel(), stream)
@@ -488,12 +510,15 @@ def flash_gau_forward_train(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, w
     B, n, d, e, s, dt, dev = _check_inputs(X, W_u, W_v, W_z, gamma, beta, W_o)
     nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
     _check_workspace(workspace, nbytes, dev)
+    made = []
     if out is None:
         out = torch.empty((B, n, d), dtype=X.dtype, device=dev)
+        made.append(out)
     else:
         _check_output(out, "out", (B, n, d), X.dtype, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for_stream(made, stream, dev)
     tensors = (X, W_u, W_v, W_z, gamma, beta, W_o)
     rc = forward_train_raw(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n,
                            d, e, s, dt, out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
@@ -523,9 +548,11 @@ def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, ro
     unknown = set(grads) - set(shapes)
     if unknown:
         raise ValueError(f"unknown gradient names {sorted(unknown)}")
+    made = []
     for k, (shape, tdt) in shapes.items():
         if k not in grads:
             grads[k] = torch.empty(shape, dtype=tdt, device=dev)
+            made.append(grads[k])
         else:
             _check_output(grads[k], k, shape, tdt, dev)
     nbytes = backward_workspace_size(B, n, d, e, s, chunk, causal, dt)
@@ -533,10 +560,12 @@ def flash_gau_backward(X, W_u, W_v, W_z, gamma, beta, W_o, dO, chunk, causal, ro
         raise ValueError("saved=True needs the workspace of a flash_gau_forward_train call")
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     else:
         _check_workspace(workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    _hold_for_stream(made, stream, dev)
     call = backward_saved_raw if saved else backward_raw
     rc = call(*(t.data_ptr() for t in tensors), chunk, causal, rope_base or 0.0, B, n, d, e,
               s, dt, *(grads[k].data_ptr() for k in GRAD_NAMES), workspace.data_ptr(),

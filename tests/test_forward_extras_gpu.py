@@ -1,6 +1,7 @@
 """GPU checks around the forward's boundary: the weight transpose is exact, the packed-weights
 entry point returns bitwise what flash_gau_forward does, and the forward writes nothing outside O
-and its workspace (guard bands of 0xFF bytes around both stay untouched).
+and its workspace (guard bands of 0xFF bytes around both stay untouched), and calls on another
+stream keep the memory they allocate until their kernels are done.
 """
 
 import numpy as np
@@ -111,3 +112,52 @@ def test_forward_writes_only_its_output_and_workspace(name):
         assert bool((buf[:GUARD] == 0xFF).all())
         assert bool((buf[GUARD + size:] == 0xFF).all())
     assert torch.equal(_bits(O), _bits(ref))
+
+
+def _delay(stream, torch):
+    # queue a few milliseconds of matrix products on `stream` (operands made and finished first)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    buf = torch.empty_like(a)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(4):
+            torch.mm(a, a, out=buf)
+    return a, buf
+
+
+def _scribble(nbytes, torch):
+    # allocations on the current stream of about the size just freed, overwritten at once
+    return [torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(2)]
+
+
+def test_calls_on_another_stream_keep_their_allocations():
+    # A call given `stream=` but no workspace allocates the workspace on torch's current stream
+    # and drops it on return, while its kernels run later on the given stream (here held back by
+    # queued products). New allocations on the current stream, filled at once, must not receive
+    # that memory before those kernels finish, or the kernels' late writes would land in them:
+    # the fills stay intact, and the results equal a plain call's bit for bit.
+    torch = _torch()
+    (B, n, d, e, s, c, causal, dt, tdt), args = _setup("c2_causal_bf16")
+    O_ref = fg.flash_gau_forward(*args, c, causal)
+    dO = torch.randn(B, n, d, device="cuda").to(tdt)
+    g_ref = fg.flash_gau_backward(*args, dO, c, causal)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    keep = _delay(side, torch)
+    O = fg.flash_gau_forward(*args, c, causal, stream=side.cuda_stream)
+    junk = _scribble(fg.workspace_size(B, n, d, e, s, c, causal, dt), torch)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert all(bool((j == 0x7F).all()) for j in junk)
+    assert torch.equal(_bits(O), _bits(O_ref))
+
+    keep = _delay(side, torch)
+    g = fg.flash_gau_backward(*args, dO, c, causal, stream=side.cuda_stream)
+    junk = _scribble(fg.backward_workspace_size(B, n, d, e, s, c, causal, dt), torch)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert all(bool((j == 0x7F).all()) for j in junk)
+    del keep, junk
+    for k in fg.GRAD_NAMES:
+        assert torch.equal(_bits(g[k]), _bits(g_ref[k])), k
