@@ -46,15 +46,26 @@ constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxScratchDevices] = {};
 
-// The device address of the current device's scratch copy, looked up on the first call per device.
-int scratch_for_current_device(void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLASHGAU_ERR_HIP;
+// The device address of the scratch copy on the device that `stream` belongs to (the null stream:
+// the current device), looked up on the first call per device with that device made current for
+// the lookup and the previous current device restored after it.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur < 0) return FLASHGAU_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess || sd < 0) return FLASHGAU_ERR_HIP;
+    dev = sd;
+  }
   if (dev >= kMaxScratchDevices) return FLASHGAU_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FLASHGAU_ERR_HIP;
     void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FLASHGAU_ERR_HIP;
+    const hipError_t rc = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FLASHGAU_ERR_HIP;
+    if (rc != hipSuccess || !ptr) return FLASHGAU_ERR_HIP;
     g_scratch_ptr[dev] = ptr;
   }
   *out = g_scratch_ptr[dev];
@@ -274,7 +285,7 @@ int flash_gau_forward_noalloc(const void* X, const void* W_u, const void* W_v, c
   if (pl.M == 0) return FLASHGAU_OK;
   if (pl.total > kScratchBytes) return FLASHGAU_ERR_TOO_LARGE;
   void* ws = nullptr;
-  const int rs = scratch_for_current_device(&ws);
+  const int rs = scratch_for_stream(static_cast<hipStream_t>(hip_stream), &ws);
   if (rs != FLASHGAU_OK) return rs;
   return forward_impl(X, W_u, W_v, W_z, gamma, beta, W_o, chunk, causal, B, n, d, e, s, dtype, O,
                       ws, kScratchBytes, hip_stream, nullptr, 0.0f);

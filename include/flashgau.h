@@ -164,9 +164,10 @@ int flash_gau_forward_packed(const void* X, const void* packed, size_t packed_by
  * device array inside the library, flashgau_noalloc_scratch_bytes() bytes (64 MiB) on every GPU
  * the library is loaded on, held until the process ends. A problem whose workspace
  * (flashgau_workspace_size) is larger returns FLASHGAU_ERR_TOO_LARGE before anything is launched.
- * The call makes no allocation of any kind. On its first call on a device it looks up that
- * device's copy of the array (hipGetSymbolAddress) with the current device, which must be the
- * stream's device. Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * The call makes no allocation of any kind. It uses the copy of the array on the device that
+ * hip_stream belongs to (the null stream: the current device), looked up on the first call on
+ * that device (hipGetSymbolAddress, with that device made current for the lookup and the current
+ * device restored after it). Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (concurrent streams, or host threads) race and must be serialised by the caller. The array
  * keeps the last call's intermediates; nothing in it needs to start at zero. Arguments as for
  * flash_gau_forward, without the workspace. Returns FLASHGAU_OK or an error code. */

@@ -21,7 +21,7 @@ def _upload(inp, tdt):
             up(inp.beta, torch.float32), up(inp.W_o)]
 
 
-def _both(shape, dtype, seed):
+def _both(shape, dtype, seed, side=None):
     B, n, d, e, s, c, causal = shape
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     dt = fg.BF16 if dtype == "bf16" else fg.F32
@@ -29,12 +29,15 @@ def _both(shape, dtype, seed):
     args = _upload(inp, tdt)
     ptrs = [t.data_ptr() for t in args]
     stream = torch.cuda.current_stream().cuda_stream
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        stream = side.cuda_stream
     nbytes = fg.workspace_size(B, n, d, e, s, c, causal, dt)
     assert nbytes <= fg.noalloc_scratch_bytes()
     ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
     ref = torch.empty((B, n, d), dtype=tdt, device="cuda")
     got = torch.full((B, n, d), float("nan"), dtype=tdt, device="cuda")
-    print(f"noalloc: shape {shape} {dtype} seed {seed}", flush=True)
+    print(f"noalloc: shape {shape} {dtype} seed {seed} stream {stream:#x}", flush=True)
     assert fg.forward_raw(*ptrs, c, causal, B, n, d, e, s, dt, ref.data_ptr(), ws.data_ptr(),
                           nbytes, stream) == fg.OK
     assert fg.forward_noalloc_raw(*ptrs, c, causal, B, n, d, e, s, dt, got.data_ptr(),
@@ -70,3 +73,11 @@ def test_noalloc_rejects_a_problem_beyond_its_scratch():
                                 g.data_ptr(), Wo.data_ptr(), c, 1, B, n, d, e, s, fg.BF16, O.data_ptr(),
                                 torch.cuda.current_stream().cuda_stream)
     assert rc == fg.ERR_TOO_LARGE
+
+
+@pytest.mark.gpu
+def test_noalloc_on_a_created_stream():
+    # the call takes the scratch copy of the device its stream belongs to (asked of the stream)
+    side = torch.cuda.Stream()
+    ref, got = _both((2, 512, 256, 512, 64, 128, True), "bf16", 4, side=side)
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
