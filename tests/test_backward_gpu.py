@@ -208,6 +208,10 @@ TRAIN_CASES = {
     "noncausal_ragged_bf16": (3, 216, 200, 136, 24, 72, False, "bf16", None),
     "rope_causal_f32": (1, 256, 64, 128, 32, 64, True, "f32", 100.0),
     "single_chunk_causal_f32": (2, 128, 32, 64, 24, 128, True, "f32", None),
+    "rope_causal_bf16": (2, 256, 128, 256, 64, 128, True, "bf16", 10000.0),
+    # chunk groups: the state scans run in two levels (in-group prefix, then carry)
+    "groups_noncausal_bf16": (8, 256, 64, 1536, 16, 8, False, "bf16", None),
+    "groups_causal_bf16": (8, 256, 64, 1536, 16, 8, True, "bf16", None),
 }
 
 
