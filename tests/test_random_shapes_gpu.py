@@ -145,6 +145,9 @@ LARGE = {
     "long_ragged_causal": (1, 16384, 1032, 2056, 136, 512, True, "bf16"),
     "ragged_noncausal_c192": (3, 3072, 776, 1288, 200, 192, False, "bf16"),
     "fp32_ragged_causal": (2, 2048, 264, 520, 72, 128, True, "f32"),
+    # wide heads: four head tiles per projection row block, a 512-deep score contraction
+    "wide_heads_s512_causal": (2, 2048, 512, 1024, 512, 256, True, "bf16"),
+    "wide_heads_s264_noncausal_f32": (2, 1024, 136, 264, 264, 128, False, "f32"),
 }
 
 
@@ -166,12 +169,13 @@ def test_forward_large_ragged(name):
     assert err <= TOL[dtype]
 
 
-def test_backward_large_ragged():
+@pytest.mark.parametrize("name", ["ragged8_causal", "wide_heads_s512_causal"])
+def test_backward_large_ragged(name):
     # the input and weight gradients on 256 x 256 tiles with partial edge tiles in d, e and s and
     # several token ranges; dO is zero on every sequence but the first, so the oracle needs only it
     import torch
-    B, n, d, e, s, c, causal, dtype = LARGE["ragged8_causal"]
-    print(f"[gpu case] backward large ragged: B={B} n={n} d={d} e={e} s={s} c={c}", flush=True)
+    B, n, d, e, s, c, causal, dtype = LARGE[name]
+    print(f"[gpu case] backward large ragged {name}: B={B} n={n} d={d} e={e} s={s} c={c}", flush=True)
     inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=401, gamma_std=0.3, beta_std=0.1)
     dO = gen.make_output_grad(B, n, d, dtype, seed=401)
     dO[1:] = 0.0
