@@ -261,6 +261,45 @@ def test_timed_entry_point_matches_and_orders_events():
         hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
+def test_timed_per_kernel_form_with_stages_that_launch_nothing():
+    # chunk = n, causal: the cross-chunk stage launches nothing (the one chunk's prefix is empty);
+    # its start and stop events are still recorded, back to back, and every other pair spans a kernel
+    import ctypes
+    torch = _torch()
+    _announce("timed entry point, per kernel, single chunk")
+    B, n, d, e, s, c, causal, dtype = 2, 256, 64, 128, 32, 256, True, "bf16"
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=8)
+    ref = run_gpu(inp)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    pairs = []
+    for _ in range(2 * len(fg.STAGES)):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        pairs.append(h.value)
+    args = [_dev(a, dtype) for a in (inp.X, inp.W_u, inp.W_v, inp.W_z)]
+    gamma, beta = _dev(inp.gamma, "f32"), _dev(inp.beta, "f32")
+    Wo = _dev(inp.W_o, dtype)
+    nbytes = fg.workspace_size(B, n, d, e, s, c, causal, fg.BF16)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, n, d), dtype=torch.bfloat16, device="cuda")
+    rc = fg.forward_timed_raw(args[0].data_ptr(), args[1].data_ptr(), args[2].data_ptr(),
+                              args[3].data_ptr(), gamma.data_ptr(), beta.data_ptr(), Wo.data_ptr(),
+                              c, causal, B, n, d, e, s, fg.BF16, O.data_ptr(), ws.data_ptr(), nbytes,
+                              torch.cuda.current_stream().cuda_stream, pairs)
+    assert rc == fg.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), ref)
+    for i, stage in enumerate(fg.STAGES):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), pairs[2 * i], pairs[2 * i + 1]) == 0, stage
+        assert ms.value >= 0.0, stage
+        if stage != "carry":
+            assert ms.value > 0.0, stage
+    for h in pairs:
+        hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
 def test_native_library_is_the_in_tree_build():
     import os
     _announce("library path")
