@@ -1307,6 +1307,14 @@ template <class E>
 void launch_out(const OutArgs<E>& a, hipStream_t stream) {
   using S = Shapes<E>;
   if constexpr (S::kOutBig) {
+    if (cdiv(a.d, 128) * cdiv(a.M, 128) < kCUs) {
+      // too few even of those to give every CU one: 64 x 64 tiles of four waves (the projection's
+      // small tile), four times as many workgroups again
+      const int64_t nb = cdiv(a.d, 64) * cdiv(a.M, 64);
+      launch_kernel((out_kernel<E, 64, 64, 2, 2, 3, false>), dim3(unsigned(nb)), dim3(256), 0,
+                    stream, a);
+      return;
+    }
     if (cdiv(a.d, S::kOutBM) * cdiv(a.M, S::kOutBN) < kCUs) {
       // too few 256 x 128 tiles to give every CU one: 128 x 128 tiles, two per CU, twice the
       // workgroups for the same work
