@@ -220,6 +220,68 @@ def cpu_baseline(inp, seconds):
     return rec, ref
 
 
+def _train_pair(fg, torch, dev, args, dO, c, causal, ws, grads, steps, dtype):
+    """A training step without the backward's recompute, timed with events around each half:
+    flash_gau_forward_train, then flash_gau_backward_saved on its workspace (10 untimed pairs
+    first). grads: the gradient tensors to write (flash_gau_backward's dict)."""
+    B, n, d = args[0].shape
+    e, s = args[1].shape[1], args[3].shape[1]
+    O = torch.empty_like(args[0])
+    for _ in range(10):
+        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=grads, saved=True)
+    torch.cuda.synchronize(dev)
+    t_f = t_b = 0.0
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(steps):
+        e0.record()
+        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+        e1.record()
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=grads, saved=True)
+        e2.record()
+        torch.cuda.synchronize(dev)
+        t_f += e0.elapsed_time(e1)
+        t_b += e1.elapsed_time(e2)
+    t_f, t_b = t_f / steps, t_b / steps
+    step_flops = 3.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
+    return {"forward_train_ms": round(t_f, 4), "backward_saved_ms": round(t_b, 4),
+            "train_step_tokens_per_s": round(B * n / ((t_f + t_b) * 1e-3), 1),
+            "frac_bf16_peak": round(step_flops / ((t_f + t_b) * 1e-3) / 1e12 / PEAK["bf16"], 4)
+            if dtype == "bf16" else None}
+
+
+def train_measure(inp, dtype, torch, fg, dev, steps=10, settle_s=0.5):
+    """Only the training pair (no recomputing backward is called), for a kernel trace of the pair
+    alone: untimed pairs for settle_s seconds (the clocks ramp up after the host has generated
+    the inputs), then _train_pair's 10 untimed and `steps` timed pairs."""
+    from efficient_transformer_attention_amd import inputs as gen
+    B, n, d = inp.X.shape
+    e, s, c, causal = inp.W_u.shape[1], inp.W_z.shape[1], inp.chunk, inp.causal
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def up(a, t=tdt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(t).contiguous()
+
+    args = [up(inp.X), up(inp.W_u), up(inp.W_v), up(inp.W_z), up(inp.gamma, torch.float32),
+            up(inp.beta, torch.float32), up(inp.W_o)]
+    dO = up(gen.make_output_grad(B, n, d, dtype))
+    dt = fg.BF16 if dtype == "bf16" else fg.F32
+    ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, dt),), dtype=torch.uint8,
+                     device=dev)
+    O = fg.flash_gau_forward_train(*args, c, causal, ws)
+    grads = fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, saved=True)
+    settle_pairs = 1
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
+        fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=grads, saved=True)
+        torch.cuda.synchronize(dev)
+        settle_pairs += 1
+    rec = _train_pair(fg, torch, dev, args, dO, c, causal, ws, grads, steps, dtype)
+    rec.update(steps=steps, settle_pairs=settle_pairs)
+    return rec
+
+
 def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10, with_saved=True):
     """Times flash_gau_backward on the whole batch (dO drawn by inputs.make_output_grad) and the
     fp64 oracle's backward on sequence 0; checks the GPU gradients of a call whose dO is zero on
@@ -257,28 +319,7 @@ def backward_measure(inp, dtype, torch, fg, dev, cpu_seconds, steps=10, with_sav
     # a training step without the backward's recompute: forward_train, then backward_saved
     training = None
     if with_saved:
-        O = torch.empty_like(args[0])
-        for _ in range(10):
-            fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
-            fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
-        torch.cuda.synchronize(dev)
-        t_f = t_b = 0.0
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        for _ in range(steps):
-            e0.record()
-            fg.flash_gau_forward_train(*args, c, causal, ws, out=O)
-            e1.record()
-            fg.flash_gau_backward(*args, dO, c, causal, workspace=ws, out=out, saved=True)
-            e2.record()
-            torch.cuda.synchronize(dev)
-            t_f += e0.elapsed_time(e1)
-            t_b += e1.elapsed_time(e2)
-        t_f, t_b = t_f / steps, t_b / steps
-        step_flops = 3.0 * sum(alg_flops(B, n, d, e, s, c, causal).values())
-        training = {"forward_train_ms": round(t_f, 4), "backward_saved_ms": round(t_b, 4),
-                    "train_step_tokens_per_s": round(B * n / ((t_f + t_b) * 1e-3), 1),
-                    "frac_bf16_peak": round(step_flops / ((t_f + t_b) * 1e-3) / 1e12 / PEAK["bf16"], 4)
-                    if dtype == "bf16" else None}
+        training = _train_pair(fg, torch, dev, args, dO, c, causal, ws, out, steps, dtype)
     rec = {"workload": f"backward of the same layer and batch", "steps": steps,
            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
            "alg_gflop": round(flops / 1e9, 2),
@@ -701,6 +742,9 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="only flash_gau_backward's timing (no CPU baseline, no training pair), "
                          "one JSON line")
+    ap.add_argument("--train-only", action="store_true",
+                    help="only the training pair (flash_gau_forward_train, then "
+                         "flash_gau_backward_saved), one JSON line")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rotary-embedding and FLASH-Quad (chunk = n) timings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -736,6 +780,10 @@ def main():
     if args.backward_only:
         print(json.dumps({"workload": name, "backward": backward_measure(
             inp, dtype, torch, fg, dev, 0.0, steps=args.steps, with_saved=False)}), flush=True)
+        return
+    if args.train_only:
+        print(json.dumps({"workload": name, "training_pair": train_measure(
+            inp, dtype, torch, fg, dev, steps=args.steps)}), flush=True)
         return
     if args.decode_only:
         if not causal:
