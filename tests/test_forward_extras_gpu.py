@@ -161,3 +161,36 @@ def test_calls_on_another_stream_keep_their_allocations():
     del keep, junk
     for k in fg.GRAD_NAMES:
         assert torch.equal(_bits(g[k]), _bits(g_ref[k])), k
+
+
+def test_calls_on_two_streams_at_once_match_sequential_calls():
+    # the library keeps no state between calls besides the allocation-free entry point's scratch:
+    # two problems run concurrently on two streams, each with its own workspace, give bit for bit
+    # what they give one after the other
+    torch = _torch()
+    (B, n, d, e, s, c, causal, dt, tdt), a1 = _setup("c2_causal_bf16", seed=1)
+    _, a2 = _setup("c2_causal_bf16", seed=2)
+    dO1 = torch.randn(B, n, d, device="cuda").to(tdt)
+    dO2 = torch.randn(B, n, d, device="cuda").to(tdt)
+    O1 = fg.flash_gau_forward(*a1, c, causal)
+    O2 = fg.flash_gau_forward(*a2, c, not causal)
+    g1 = fg.flash_gau_backward(*a1, dO1, c, causal)
+    g2 = fg.flash_gau_backward(*a2, dO2, c, not causal)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = {}
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            outs["O1"] = fg.flash_gau_forward(*a1, c, causal)
+            outs["g1"] = fg.flash_gau_backward(*a1, dO1, c, causal)
+        with torch.cuda.stream(s2):
+            outs["O2"] = fg.flash_gau_forward(*a2, c, not causal)
+            outs["g2"] = fg.flash_gau_backward(*a2, dO2, c, not causal)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(outs["O1"]), _bits(O1)), rep
+        assert torch.equal(_bits(outs["O2"]), _bits(O2)), rep
+        for k in fg.GRAD_NAMES:
+            assert torch.equal(_bits(outs["g1"][k]), _bits(g1[k])), (rep, k)
+            assert torch.equal(_bits(outs["g2"][k]), _bits(g2[k])), (rep, k)
