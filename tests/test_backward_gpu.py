@@ -202,6 +202,46 @@ def test_forward_and_backward_replayed_from_a_hip_graph_match_eager():
             assert torch.equal(grads[k], g_eager[k]), (rep, k)
 
 
+def test_training_pair_replayed_from_a_hip_graph_matches_eager():
+    # flash_gau_forward_train then flash_gau_backward_saved, with the rotary embedding, captured
+    # into one HIP graph; before every replay the workspace is filled with 0xFF bytes (NaN in
+    # bf16) by eager work, so a replay that read anything its own forward did not write would
+    # show it. Every replay must reproduce the eager outputs bitwise.
+    torch = _torch()
+    B, n, d, e, s, c, causal, dtype, base = 2, 256, 64, 128, 32, 64, True, "bf16", 10000.0
+    print("[gpu case] training pair graph replay", flush=True)
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, dtype, seed=9, gamma_std=0.3, beta_std=0.1)
+    args = [_dev(inp.X, dtype), _dev(inp.W_u, dtype), _dev(inp.W_v, dtype), _dev(inp.W_z, dtype),
+            _dev(inp.gamma, "f32"), _dev(inp.beta, "f32"), _dev(inp.W_o, dtype)]
+    dO = _dev(gen.make_output_grad(B, n, d, dtype, seed=9), dtype)
+    ws = torch.empty((fg.backward_workspace_size(B, n, d, e, s, c, causal, fg.BF16),),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(255)
+    O_eager = fg.flash_gau_forward_train(*args, c, causal, ws, rope_base=base).clone()
+    g_eager = {k: v.clone() for k, v in fg.flash_gau_backward(*args, dO, c, causal, rope_base=base,
+                                                              workspace=ws, saved=True).items()}
+    torch.cuda.synchronize()
+    O = torch.empty_like(O_eager)
+    grads = {k: torch.empty_like(v) for k, v in g_eager.items()}
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=stream):
+        fg.flash_gau_forward_train(*args, c, causal, ws, rope_base=base, out=O, stream=stream.cuda_stream)
+        fg.flash_gau_backward(*args, dO, c, causal, rope_base=base, workspace=ws,
+                              stream=stream.cuda_stream, out=grads, saved=True)
+    for rep in range(3):
+        ws.fill_(255)
+        O.zero_()
+        for v in grads.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O, O_eager), rep
+        for k in fg.GRAD_NAMES:
+            assert torch.equal(grads[k], g_eager[k]), (rep, k)
+
+
 # name: (B, n, d, e, s, chunk, causal, dtype, rope_base)
 TRAIN_CASES = {
     "causal_bf16": (2, 512, 128, 256, 128, 256, True, "bf16", None),
