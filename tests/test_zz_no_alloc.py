@@ -81,3 +81,35 @@ def test_noalloc_on_a_created_stream():
     side = torch.cuda.Stream()
     ref, got = _both((2, 512, 256, 512, 64, 128, True), "bf16", 4, side=side)
     assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_noalloc_replayed_from_a_hip_graph():
+    # the callers it is for: a forward captured into a HIP graph with no allocation during
+    # capture. One eager call first (the per-device scratch address is looked up then, outside
+    # the capture); every replay, with eager work and synchronisations between, must equal
+    # flash_gau_forward bit for bit.
+    B, n, d, e, s, c, causal = 2, 512, 256, 512, 64, 128, True
+    inp = gen.make_inputs(B, n, d, e, s, c, causal, "bf16", seed=5, beta_std=0.1)
+    args = _upload(inp, torch.bfloat16)
+    ptrs = [t.data_ptr() for t in args]
+    ref = fg.flash_gau_forward(*args, c, causal)
+    O = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    assert fg.forward_noalloc_raw(*ptrs, c, causal, B, n, d, e, s, fg.BF16, O.data_ptr(),
+                                  side.cuda_stream) == fg.OK
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), ref.view(torch.int16))
+    print("noalloc: graph capture", flush=True)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        rc = fg.forward_noalloc_raw(*ptrs, c, causal, B, n, d, e, s, fg.BF16, O.data_ptr(),
+                                    side.cuda_stream)
+    assert rc == fg.OK
+    for rep in range(3):
+        O.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O.view(torch.int16), ref.view(torch.int16)), rep
