@@ -1338,7 +1338,8 @@ void launch_out(const OutArgs<E>& a, hipStream_t stream) {
 
 // The projection: bf16 on 128 x 128 tiles, two workgroups per CU, or, for a problem whose
 // 128 x 128 tiles would not fill that first round of the CUs, on 64 x 64 tiles of four waves (four
-// times the workgroups for the same work); fp32 on its own (small) tile.
+// times the workgroups for the same work) with a two-stage ring (32 KB of LDS, five workgroups per
+// CU, so that they all run in one round); fp32 on its own (small) tile.
 template <class E, bool EXTRA = false>
 void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
   using S = Shapes<E>;
@@ -1346,7 +1347,7 @@ void launch_proj(const ProjArgs<E>& a, hipStream_t stream) {
   if constexpr (S::kProjBM == 128) {
     if (cdiv(a.M, 128) * cdiv(ncols, 128) < 2 * kCUs) {
       const int64_t nb = cdiv(a.M, 64) * cdiv(ncols, 64);
-      launch_kernel((proj_kernel<E, 64, 64, 2, 2, 3, EXTRA>), dim3(unsigned(nb)), dim3(256), 0,
+      launch_kernel((proj_kernel<E, 64, 64, 2, 2, 2, EXTRA>), dim3(unsigned(nb)), dim3(256), 0,
                          stream, a);
       return;
     }
